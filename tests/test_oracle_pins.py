@@ -1,0 +1,494 @@
+"""Pins of the oracle against what the pages and mathematics fix (CPU only).
+
+Every check here compares the oracle with something other than itself:
+worked examples printed on the pages (tests/golden/page_examples.json),
+brute-force enumeration of tiny languages, Python's strict UTF-8 codec,
+exhaustive integer ranges, and library routines (torch argmax/log_softmax,
+torch's Philox4x32-10 engine).
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from logit_masking_amd import workloads as W
+from oracle import oracle as O
+from tests import langref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def grammars():
+    return {c: O.load_spec(W.spec_json(c)) for c in W.SPECS}
+
+
+# ---------------------------------------------------------------------------
+# Worked examples from the pages
+# ---------------------------------------------------------------------------
+def _page_cases():
+    with open(os.path.join(GOLDEN, "page_examples.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _page_cases()["cases"], ids=lambda c: c["input"][:40])
+def test_page_examples(grammars, case):
+    g = grammars[case["cfg"]]
+    data = case["input"].encode()
+    k, complete = g.try_input(data)
+    want = len(data) if case["refused_at"] is None else case["refused_at"]
+    assert k == want, case["cite"]
+    assert complete == case["complete"], case["cite"]
+    # the independent full-string validator agrees on membership
+    assert langref.member(W.SPECS[case["cfg"]], data) == case["complete"]
+
+
+@pytest.mark.parametrize("case", _page_cases()["next_bytes"], ids=lambda c: c["prefix"][:40])
+def test_page_boundary_trace(grammars, case):
+    g = grammars[case["cfg"]]
+    c = g.start()
+    pre = case["prefix"].encode()
+    assert g.feed(c, pre) == len(pre)
+    assert g.next_bytes(c) == set(case["allowed"].encode()), case["cite"]
+
+
+def test_calc_evaluator_example():
+    # "Evaluator aware decoding", "The core idea": 17 * 23 + 91 = 482
+    assert O.eval_calc(b"<calc>17 * 23 + 91</calc>") == 482
+    assert O.eval_calc(b"<calc>(1+2)*3</calc>") == 9
+    assert O.eval_calc(b"<calc>7/2 - 9/4</calc>") == 1
+    assert O.eval_calc(b"<calc>0-7/2</calc>") == -3
+    with pytest.raises(O.CalcError):
+        O.eval_calc(b"<calc>1/0</calc>")
+
+
+def test_unarmed_shapes_refused_at_byte0(grammars):
+    # no tool name starts with '<' or "tool "
+    g = grammars[3]
+    for s in (b"<tool_call>", b"tool read_document", b"```", b" calculate("):
+        assert g.try_input(s)[0] == 0
+
+
+# ---------------------------------------------------------------------------
+# Whitespace bound k: a run of k is accepted, byte k+1 of the run refused
+# ("Constrained decoding", "A valid call also has to end").
+# ---------------------------------------------------------------------------
+WS_POSITIONS = {
+    1: [b"<calc>", b"<calc>1", b"<calc>1+", b"<calc>(", b"<calc>(2", b"<calc>(2)"],
+    2: [b"{", b'{"eligibility"', b'{"eligibility":', b'{"eligibility":{"criteria_met":true',
+        b'{"eligibility":{"criteria_met":true,'],
+    3: [b"calculate({", b'calculate({"expression"', b'calculate({"expression":', b'calculate({"expression":"a"',
+        b'store_record({"key":"k","value":[', b'store_record({"key":"k","value":{"a":1'],
+    5: [b"[", b"[1", b"[1,", b'{"a"', b'{"a":', b'{"a":[{}'],
+}
+
+
+@pytest.mark.parametrize("cfg", sorted(WS_POSITIONS))
+@pytest.mark.parametrize("wsb", [b" ", b"\t", b"\n", b"\r"])
+def test_ws_bound(grammars, cfg, wsb):
+    g = grammars[cfg]
+    k = W.SPECS[cfg]["ws_max"]
+    for pre in WS_POSITIONS[cfg]:
+        assert g.viable(pre), pre
+        assert g.viable(pre + wsb * k), pre
+        assert g.try_input(pre + wsb * (k + 1))[0] == len(pre) + k, pre
+
+
+def test_ws_not_outside_root(grammars):
+    assert grammars[2].try_input(b" {")[0] == 0
+    assert grammars[5].try_input(b"[] ")[0] == 2
+    assert grammars[3].try_input(b"calculate( {")[0] == 10
+    assert grammars[3].try_input(b'calculate({"expression":"x"} )')[0] == len(b'calculate({"expression":"x"}')
+
+
+def test_compact_has_no_ws(grammars):
+    g = grammars[4]
+    for pre in (b"{", b'{"reasoning"', b'{"reasoning":', b'{"reasoning":"x"', b'{"reasoning":"x",'):
+        assert g.try_input(pre + b" ")[0] == len(pre)
+
+
+# ---------------------------------------------------------------------------
+# Strings: UTF-8 against Python's strict codec, escapes, caps.
+# ---------------------------------------------------------------------------
+def _utf8_truth():
+    enc = set()
+    for cp in range(0x80, 0x110000):
+        if 0xD800 <= cp <= 0xDFFF:
+            continue
+        enc.add(chr(cp).encode("utf-8"))
+    pre = set()
+    for e in enc:
+        for i in range(1, len(e)):
+            pre.add(e[:i])
+    return enc, pre
+
+
+def test_utf8_exhaustive_boundary(grammars):
+    """Inside an uncapped string: for the empty pending sequence and every
+    proper prefix of a well-formed encoding, byte b is accepted iff the
+    extended sequence is a prefix of (or is) a well-formed encoding."""
+    g = grammars[5]
+    enc, pre = _utf8_truth()
+    base = g.start()
+    assert g.feed(base, b'["') == 2
+    allowed_ascii = {b for b in range(0x20, 0x80)}  # '"' ends the string, '\\' escapes
+    got0 = g.next_bytes(base)
+    want0 = allowed_ascii | {e[0] for e in enc}
+    assert got0 == want0
+    for p in sorted(pre):
+        c = g.clone(base)
+        assert g.feed(c, p) == len(p)
+        got = g.next_bytes(c)
+        want = {b for b in range(256) if (p + bytes([b])) in pre or (p + bytes([b])) in enc}
+        assert got == want, p
+
+
+def test_escapes(grammars):
+    g = grammars[5]
+    base = g.start()
+    g.feed(base, b'["\\')
+    assert g.next_bytes(base) == set(b'"\\/bfnrtu')
+    hexd = b"0123456789abcdefABCDEF"
+    # every 4-hex escape: accepted iff not a surrogate code unit
+    for h in itertools.product(b"0d89aF", repeat=4):
+        s = b'["\\u' + bytes(h)
+        want = not (0xD800 <= int(bytes(h), 16) <= 0xDFFF)
+        assert g.viable(s) == want, s
+    # refusal at the first hex digit that leaves only surrogates
+    assert g.try_input(b'["\\uD8')[0] == len(b'["\\uD')
+    assert g.try_input(b'["\\udfff')[0] == len(b'["\\ud')
+    assert g.viable(b'["\\uD7FF"]')
+    for b in range(256):
+        s = b'["\\u' + bytes([b])
+        assert g.viable(s) == (b in hexd)
+
+
+def test_string_caps_count_code_points(grammars):
+    g = grammars[3]  # calendar.time <= 10, open strings <= 256
+    pre = b'calendar({"action":"list","date":"d","time":"'
+    for unit in (b"a", b"\xc3\xa9", b"\xe2\x82\xac", b"\xf0\x9f\x98\x80", b"\\n", b"\\u00e9"):
+        assert g.viable(pre + unit * 10 + b'"')
+        k = g.try_input(pre + unit * 11)[0]
+        assert k == len(pre) + 10 * len(unit), unit
+    pre = b'calculate({"expression":"'
+    assert g.viable(pre + b"x" * 256 + b'"')
+    assert g.try_input(pre + b"x" * 257)[0] == len(pre) + 256
+
+
+def test_controls_refused_in_strings(grammars):
+    g = grammars[5]
+    for b in range(0x20):
+        assert g.try_input(b'["' + bytes([b]))[0] == 2
+    assert g.viable(b'["\x7f"]')
+
+
+# ---------------------------------------------------------------------------
+# Integers: canonical spelling and inclusive ranges, by exhaustive enumeration.
+# ---------------------------------------------------------------------------
+RANGES = [(1, 500), (5, 480), (1, 86400), (1, 20), (-1, 1000000), (-3, 5), (-120, -7), (0, 0), (10, 99)]
+
+
+def _int_prefix_truth(lo, hi):
+    full = {str(v).encode() for v in range(lo, hi + 1)}
+    pre = set()
+    for s in full:
+        for i in range(1, len(s) + 1):
+            pre.add(s[:i])
+    return full, pre
+
+
+@pytest.mark.parametrize("lo,hi", RANGES)
+def test_int_range_exhaustive(lo, hi):
+    spec = {"kind": "json_schema", "ws_max": 0,
+            "schema": {"type": "object", "properties": {"n": {"type": "integer", "minimum": lo, "maximum": hi}},
+                       "required": ["n"], "additionalProperties": False}}
+    g = O.load_spec(spec)
+    full, pre = _int_prefix_truth(lo, hi)
+    base = g.start()
+    g.feed(base, b'{"n":')
+    # boundary check: from every viable spelling prefix, each next byte
+    # (large ranges: all prefixes of up to 4 bytes, the bounds, and a sample)
+    todo = sorted(pre | {b""})
+    if len(todo) > 50000:
+        rng = W.SplitMix(lo * 31 + hi)
+        edge = {str(v).encode() for v in (lo, hi, lo + 1, hi - 1)}
+        todo = [p for p in todo if len(p) <= 4 or p in edge] + [todo[rng.below(len(todo))] for _ in range(20000)]
+    for p in todo:
+        c = g.clone(base)
+        assert g.feed(c, p) == len(p)
+        got = g.next_bytes(c)
+        want = {b for b in b"-0123456789" if p + bytes([b]) in pre}
+        if p in full:
+            want.add(ord("}"))
+        assert got == want, p
+
+
+def test_open_int_twenty_digits(grammars):
+    g = grammars[4]
+    pre = b'{"reasoning":"","answer":'
+    assert g.viable(pre + b"9" * 20 + b"}")
+    assert g.try_input(pre + b"9" * 21)[0] == len(pre) + 20
+    assert g.viable(pre + b"-" + b"1" * 20 + b"}")
+    assert g.try_input(pre + b"-" + b"1" * 21)[0] == len(pre) + 21
+
+
+# ---------------------------------------------------------------------------
+# Brute force: tiny languages enumerated generatively; the oracle's viable
+# set must be exactly their prefix set on the test alphabet.
+# ---------------------------------------------------------------------------
+TINY = [
+    ("enum-int-str", {"kind": "json_schema", "ws_max": 0, "schema": {
+        "type": "object", "properties": {
+            "a": {"enum": ["x", "yz"]},
+            "b": {"type": "integer", "minimum": 0, "maximum": 12},
+            "c": {"type": "string", "maxLength": 2}},
+        "required": ["a", "c"], "additionalProperties": False}},
+     b'{}":,xyzabc0129\\n\xc3\xa9\xff-', 60),
+    ("ws-one-key", {"kind": "json_schema", "ws_max": 2, "schema": {
+        "type": "object", "properties": {"a": {"enum": ["x"]}}, "required": ["a"],
+        "additionalProperties": False}},
+     b'{}":,ax \n', 40),
+    ("nested-anyof", {"kind": "json_schema", "ws_max": 0, "schema": {
+        "type": "object", "properties": {
+            "o": {"type": "object", "properties": {"p": {"type": "boolean"}}, "required": [],
+                  "additionalProperties": False},
+            "n": {"anyOf": [{"type": "null"}, {"type": "integer", "minimum": -3, "maximum": 5}]}},
+        "required": ["n"], "additionalProperties": False}},
+     b'{}":,opntruefalsl-0123456x', 60),
+    ("array-enum", {"kind": "json_schema", "ws_max": 1, "schema": {
+        "type": "array", "items": {"enum": ["a", "b"]}, "maxItems": 3}},
+     b'[]",ab ', 40),
+    ("tools-shared-prefix", {"kind": "tool_call", "ws_max": 0, "tools": [
+        {"name": "f", "parameters": {"type": "object", "properties": {"x": {"type": "integer", "minimum": 0,
+                                                                               "maximum": 3}},
+                                     "required": ["x"], "additionalProperties": False}},
+        {"name": "fg", "parameters": {"type": "object", "properties": {"y": {"type": "boolean"}},
+                                      "required": [], "additionalProperties": False}}]},
+     b'fg(){}":,xy0123truefals4', 40),
+    ("utf8-str", {"kind": "json_schema", "ws_max": 0, "schema": {
+        "type": "object", "properties": {"s": {"type": "string", "maxLength": 2}}, "required": ["s"],
+        "additionalProperties": False}},
+     b'{}":s\\/n\xc3\xa9\xe2\x82\xac\xf0\x9f\x98\x80\xed\x9f\xbf', 40),
+    ("depth-cap", {"kind": "json_schema", "ws_max": 0, "depth_cap": 2, "schema": {
+        "type": "object", "properties": {"a": {"type": "object", "properties": {
+            "b": {"type": "object", "properties": {}, "additionalProperties": False}},
+            "required": [], "additionalProperties": False}}, "required": [], "additionalProperties": False}},
+     b'{}":ab', 40),
+]
+
+
+def _check_tiny(spec, sigma, budget, min_room=0):
+    g = O.load_spec(spec)
+    M = langref.Enumerator(spec, sigma, budget).members()
+    assert M
+    for m in M:
+        assert langref.member(spec, m), m
+        assert g.try_input(m) == (len(m), True), m
+        if spec["kind"] == "json_schema":
+            json.loads(m.decode("utf-8"))
+    P = langref.prefixes(M)
+    sig = set(sigma)
+    checked = 0
+    for p in P:
+        if len(p) + 1 + min_room > budget:
+            continue
+        c = g.start()
+        assert g.feed(c, p) == len(p), p
+        assert g.complete(c) == (p in M), p
+        got = g.next_bytes(c) & sig
+        want = {b for b in sig if p + bytes([b]) in P}
+        assert got == want, (p, sorted(got ^ want))
+        checked += 1
+    return checked
+
+
+@pytest.mark.parametrize("name,spec,sigma,budget", TINY, ids=[t[0] for t in TINY])
+def test_tiny_languages_bruteforce(name, spec, sigma, budget):
+    assert _check_tiny(spec, sigma, budget) > 5
+
+
+def test_tiny_calc_bruteforce():
+    # the shortest completion of any non-empty viable prefix is at most 13
+    # bytes ("<" + "calc>0</calc>"), 14 with one whitespace slot
+    spec = {"kind": "calc", "int_min": 0, "int_max": 12, "ws_max": 1, "depth_cap": 1}
+    assert _check_tiny(spec, b"<calc>/01 +()", 24, min_room=14) > 50
+    spec = {"kind": "calc", "int_min": 0, "int_max": 12, "ws_max": 0, "depth_cap": 2}
+    assert _check_tiny(spec, b"<calc>/01+()", 26, min_room=13) > 1000
+
+
+# ---------------------------------------------------------------------------
+# Rows: the engine cap and the invariants of masks on real vocabularies.
+# ---------------------------------------------------------------------------
+def test_gen_cap_and_done(grammars):
+    g = grammars[5]
+    r = O.Row(g, gen_cap=3)
+    assert r.advance(b"[") == O.ROW_OK
+    assert r.advance(b"1") == O.ROW_OK
+    assert r.advance(b",") == O.ROW_CAPPED
+    assert r.done and r.step == 3
+    assert r.advance(b"2") == O.ROW_REJECTED
+    r = O.Row(g, gen_cap=W.GEN_CAP)
+    assert W.GEN_CAP >= 1523  # largest legitimate call on the page
+    assert r.advance(b"x") == O.ROW_REJECTED and r.step == 0
+    assert r.advance(None) == O.ROW_NOOP
+    assert r.advance(b"[") == O.ROW_OK and r.advance(b"]") == O.ROW_DONE
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_mask_invariants_random_walk(grammars, cfg):
+    """(i) a live row has an allowed token; (ii) bit(t) <=> advancing by t
+    succeeds; (iii) if token u's bytes are a prefix of allowed token t's,
+    u is allowed; (iv) finished outputs are full members (validator)."""
+    g = grammars[cfg]
+    V = 4096
+    blob, off = W.make_vocab(cfg, V) if cfg != 1 else W.make_vocab(1)
+    V = len(off) - 1
+    toks = [blob[off[i]:off[i + 1]] for i in range(V)]
+    rng = W.SplitMix(cfg * 77)
+    row = O.Row(g, gen_cap=300)
+    by_bytes = {t: i for i, t in enumerate(toks)}
+    for step in range(120):
+        if row.done:
+            break
+        words = g.mask(row.conf, blob, off)
+        bits = O.unpack_mask(words, V)
+        allowed = np.nonzero(bits)[0]
+        assert len(allowed) > 0
+        for t in range(0, V, 97):
+            c = g.clone(row.conf)
+            assert (g.feed(c, toks[t]) == len(toks[t])) == bits[t]
+        for t in allowed[:200]:
+            tb = toks[t]
+            for k in range(1, len(tb)):
+                u = by_bytes.get(tb[:k])
+                if u is not None:
+                    assert bits[u]
+        # prefer structural progress half of the time so rows finish
+        pick = int(allowed[rng.below(len(allowed))])
+        assert row.advance(toks[pick]) in (O.ROW_OK, O.ROW_DONE, O.ROW_CAPPED)
+    if row.complete:
+        assert langref.member(W.SPECS[cfg], bytes(row.text))
+
+
+def test_finished_outputs_are_members(grammars):
+    """Drive rows to completion with a bias toward short structural tokens;
+    every completed output is a member, parses as JSON, and keeps the
+    decision fields before response_text ("What we measured": field order)."""
+    blob, off = W.make_vocab(2, 4096)
+    toks = [blob[off[i]:off[i + 1]] for i in range(len(off) - 1)]
+    g = grammars[2]
+    rng = W.SplitMix(5)
+    done = 0
+    for trial in range(6):
+        row = O.Row(g, gen_cap=2048)
+        while not row.done:
+            bits = O.unpack_mask(g.mask(row.conf, blob, off), len(toks))
+            allowed = np.nonzero(bits)[0]
+            short = [t for t in allowed if len(toks[t]) > 1 and b'"' in toks[t]] or list(allowed)
+            pick = short[rng.below(len(short))] if rng.uniform() < 0.7 else allowed[rng.below(len(allowed))]
+            row.advance(toks[int(pick)])
+        if row.complete:
+            done += 1
+            text = bytes(row.text)
+            assert langref.member(W.SPECS[2], text)
+            obj = json.loads(text.decode())
+            assert list(obj) == ["eligibility", "action", "appointment", "response_text"]
+            assert text.index(b'"response_text"') > text.index(b'"action"')
+    assert done >= 1
+
+
+# ---------------------------------------------------------------------------
+# Spec refusals (fail closed), each with its JSON path.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("schema,path", [
+    ({"$ref": "#/x"}, "$.schema"),
+    ({"type": "string", "pattern": "a+"}, "$.schema"),
+    ({"type": "string", "format": "date"}, "$.schema"),
+    ({"oneOf": [{"type": "null"}]}, "$.schema"),
+    ({"allOf": [{"type": "null"}]}, "$.schema"),
+    ({"type": "object", "properties": {"a": {"type": "null"}}}, "$.schema"),
+    ({"type": "object", "patternProperties": {}}, "$.schema"),
+    ({"type": "array", "minItems": 1}, "$.schema"),
+    ({"type": "integer", "multipleOf": 2}, "$.schema"),
+    ({"anyOf": [{"type": "integer"}, {"type": "number"}]}, "$.schema"),
+    ({"anyOf": [{"type": "string"}, {"enum": ["a"]}]}, "$.schema"),
+    ({"type": "object", "properties": {"a": {"type": "string", "minLength": 1}}, "required": [],
+      "additionalProperties": False}, "$.schema/properties/a"),
+    ({"type": "integer", "minimum": 5, "maximum": 4}, "$.schema"),
+])
+def test_unsupported_fail_closed(schema, path):
+    with pytest.raises(O.Unsupported) as e:
+        O.load_spec({"kind": "json_schema", "schema": schema})
+    assert e.value.path == path
+
+
+# ---------------------------------------------------------------------------
+# Sampling
+# ---------------------------------------------------------------------------
+def test_greedy_matches_torch():
+    import torch
+    rng = np.random.default_rng(0)
+    for V in (7, 300, 5000):
+        for _ in range(20):
+            x = torch.from_numpy(rng.standard_normal(V).astype(np.float32)).to(torch.bfloat16)
+            allowed = rng.random(V) < 0.3
+            allowed[rng.integers(V)] = True
+            xf = x.to(torch.float64)
+            masked = torch.where(torch.from_numpy(allowed), xf, torch.tensor(-float("inf"), dtype=torch.float64))
+            want = int(torch.argmax(masked))  # first maximal index
+            lp = float(torch.log_softmax(masked, 0)[want])
+            i, got_lp, _ = O.sample_row(xf.numpy(), allowed, 0.0, 1, 0)
+            assert i == want
+            assert abs(got_lp - lp) < 1e-12
+
+
+def test_greedy_ties_lowest_id():
+    x = np.array([1.0, 3.0, 3.0, 2.0, 3.0])
+    assert O.sample_row(x, np.array([1, 0, 1, 1, 1], bool), 0.0, 0, 0)[0] == 2
+
+
+def test_no_allowed_token():
+    assert O.sample_row(np.zeros(10), np.zeros(10, bool), 0.7, 1, 1) == (-1, 0.0,
+                                                                          {"margin_chunk": float("inf"),
+                                                                           "margin_token": float("inf")})
+
+
+def test_two_level_sampler_distribution():
+    """Empirical pick frequencies over many seeds follow softmax(x/T) on the
+    mask (chi-square), with tokens spread over several 4-id chunks."""
+    rng = np.random.default_rng(1)
+    V, T, chunk = 24, 0.7, 4
+    x = rng.standard_normal(V) * 1.5
+    allowed = rng.random(V) < 0.7
+    allowed[0] = allowed[5] = True
+    p = np.where(allowed, np.exp(x / T), 0)
+    p /= p.sum()
+    n = 20000
+    counts = np.zeros(V)
+    for s in range(n):
+        i, _, _ = O.sample_row(x, allowed, T, W.splitmix64(s), 3, chunk=chunk)
+        counts[i] += 1
+    e = p * n
+    m = e > 0
+    chi2 = float(((counts[m] - e[m]) ** 2 / e[m]).sum())
+    dof = int(m.sum()) - 1
+    assert chi2 < dof + 6 * np.sqrt(2 * dof), (chi2, dof)
+    assert counts[~allowed].sum() == 0
+
+
+def test_sampled_logprob():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(5000)
+    allowed = rng.random(5000) < 0.5
+    i, lp, _ = O.sample_row(x, allowed, 0.7, 123, 4)
+    z = x / float(np.float32(0.7))
+    m = z[allowed].max()
+    want = z[i] - (m + np.log(np.exp(z[allowed] - m).sum()))
+    assert allowed[i] and abs(lp - want) < 1e-12
+
+
+def test_gumbel_uniform_open_interval():
+    g = O.gumbel(np.array([0, 0xFFFFFFFF], dtype=np.uint64))
+    assert np.all(np.isfinite(g))
