@@ -1,0 +1,219 @@
+/*
+ * cg.h -- C ABI of the constrained-decoding hot path on MI355X (gfx950).
+ *
+ * At every decode step a byte-level pushdown automaton masks the logits so
+ * that only continuations legal under the grammar can be generated, and
+ * sampling runs after masking ("Constrained decoding", section "The
+ * guarantee").  The contract is a handful of calls over plain pointers and
+ * sizes that name no model, tokenizer, device type or file ("Constrained
+ * decoding", section "The guarantee is not tied to this engine").
+ *
+ *   cg_compile_grammar   spec + vocabulary -> automaton tables (host, once)
+ *   cg_init_state        every row at the start of the grammar (device)
+ *   cg_fill_bitmask      packed token bitmask per row (device)
+ *   cg_apply_mask_sample masked softmax + greedy / Gumbel-max pick (device)
+ *   cg_advance           walk the chosen tokens, update rows (device)
+ *   cg_try_input         where a candidate string is refused (host)
+ *
+ * Conventions
+ *   - Device pointers ("d_") are HIP device memory owned by the caller.
+ *     `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *   - Per-step calls are asynchronous on `stream`: they never synchronise,
+ *     never allocate, never print.  Their return code reports argument and
+ *     launch errors only; outcomes that depend on data (a refused forced
+ *     token, a finished row) come back in device arrays.
+ *   - Errors: a negative CG_E_* code; cg_last_error() then holds a message
+ *     (thread-local), for compile errors with the JSON path of the offending
+ *     part of the spec.
+ *   - A compiled grammar is immutable and may be used from several streams
+ *     at once; free it only after every stream using it has drained.
+ */
+#ifndef CG_H
+#define CG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ---------------------------------------------------------- */
+#define CG_OK 0
+#define CG_E_ARG (-1)         /* bad argument (null pointer, size, dtype, handle) */
+#define CG_E_PARSE (-2)       /* spec is not valid JSON / not a grammar spec */
+#define CG_E_UNSUPPORTED (-3) /* construct outside the supported subset (fail closed) */
+#define CG_E_LIMIT (-4)       /* automaton or vocabulary beyond a size limit */
+#define CG_E_VOCAB (-5)       /* malformed vocabulary (offsets) */
+#define CG_E_DEVICE (-6)      /* HIP runtime error (allocation, copy, launch) */
+
+/* ---- per-row status written by cg_advance --------------------------------- */
+#define CG_ROW_OK 0       /* token accepted, row continues */
+#define CG_ROW_DONE 1     /* token accepted, the row's bytes are now a complete member */
+#define CG_ROW_CAPPED 2   /* token accepted, row reached the generation cap */
+#define CG_ROW_REJECTED 3 /* token refused (illegal, out of range, or row finished); row unchanged */
+#define CG_ROW_NOOP 4     /* token id -1: nothing to do */
+
+/* ---- row state flags (cg_state.flags) ------------------------------------- */
+#define CG_FLAG_DONE 1u
+#define CG_FLAG_CAPPED 2u
+
+/* options of cg_compile_grammar */
+#define CG_HOST_ONLY 1u /* compile for cg_try_input only: nothing is uploaded */
+
+typedef struct cg_grammar cg_grammar; /* opaque, library-owned */
+
+typedef struct {
+    uint32_t gen_cap; /* tokens per constrained generation; 0 means 2048
+                         ("A valid call also has to end": the engine caps a
+                         constrained generation at 2048 tokens) */
+    uint32_t flags;   /* CG_HOST_ONLY or 0 */
+} cg_options;
+
+/*
+ * One row's automaton configuration (24 bytes, plain data: a snapshot is a
+ * copy).  Caller-allocated device memory, written only by cg_init_state and
+ * cg_advance; the fields are the library's business.
+ */
+typedef struct {
+    uint16_t q;     /* control state */
+    uint16_t ret;   /* state to resume after the open string */
+    uint32_t cnt;   /* code points still allowed in the open string */
+    uint64_t stk;   /* container kinds of open any-JSON containers, bit 0 innermost */
+    uint8_t depth;  /* containers on that stack */
+    uint8_t ws;     /* length of the current whitespace run */
+    uint8_t flags;  /* CG_FLAG_DONE | CG_FLAG_CAPPED */
+    uint8_t pad0;
+    uint32_t pad1;
+} cg_state;
+
+typedef struct {
+    int32_t vocab_size;
+    int32_t words_per_row;  /* ceil(vocab_size / 64) */
+    int32_t max_token_len;  /* longest token, bytes (<= 32) */
+    int32_t n_states;       /* control states after trimming */
+    int32_t table_entries;  /* packed transition slots (8 bytes each) */
+    int32_t table_bytes;    /* bytes of the transition table staged per workgroup */
+    double compile_ms;      /* host time of parse + build + pack */
+} cg_info;
+
+/*
+ * Compile a grammar spec against a vocabulary and upload the tables to the
+ * current HIP device.
+ *
+ * spec_json/spec_len: UTF-8 JSON, one of
+ *   {"kind":"calc", "int_min":0, "int_max":999, "ws_max":2, "depth_cap":16}
+ *       the span "<calc>" W E W "</calc>", E := T (W op W T)*,
+ *       T := INT | "(" W E W ")", op one of + - * /, INT canonical decimal in
+ *       [int_min, int_max] ("Evaluator aware decoding", "This is a grammar
+ *       problem");
+ *   {"kind":"json_schema", "schema":{...}, settings...}
+ *       a JSON value of the schema ("Guided Decoding & Structured-Output
+ *       Reliability", "Design 1 -- base schema, validators-first ordering");
+ *   {"kind":"tool_call", "tools":[{"name":N, "parameters":{object schema}}...]}
+ *       N "(" args-object ")" -- the grammar arms at "name(" ("Constrained
+ *       decoding", "Where it arms, and therefore where it stops").
+ *   Settings (defaults in brackets): ws_max [4] longest whitespace run;
+ *   open_string_cap [256] code points of a string without maxLength (null:
+ *   uncapped); open_int_digits [20] digits of an integer without both
+ *   bounds; depth_cap [16] open containers ({, [, or calc parentheses).
+ *   ("A valid call also has to end": bounded whitespace and open fields.)
+ *   Supported schema subset: type object/array/string/integer/number/
+ *   boolean/null; properties (declared order is emitted order), required,
+ *   additionalProperties:false (required whenever properties is given);
+ *   string enum; maxLength; integer minimum/maximum; items; maxItems;
+ *   anyOf whose alternatives start with different bytes; {} = any JSON
+ *   value.  Anything else -- $ref, pattern, format, oneOf, allOf, minItems,
+ *   minLength, multipleOf, ... -- is refused with CG_E_UNSUPPORTED and its
+ *   JSON path ("Constrained Decoding Under Matched Conditions", "What exists
+ *   beyond the experiment": typed fail-closed refusals).
+ * tok_bytes/tok_offsets/vocab_size: token t is tok_bytes[tok_offsets[t] ..
+ *   tok_offsets[t+1]); offsets has vocab_size+1 non-decreasing entries
+ *   starting at 0 (host memory, copied).  Empty tokens are never allowed.
+ *   At most 32 bytes per token.
+ * opts: may be NULL (gen_cap 2048, upload).
+ * out: receives the handle.  Returns CG_OK or a CG_E_* code.
+ */
+int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *tok_bytes,
+                       const uint32_t *tok_offsets, int32_t vocab_size, const cg_options *opts, cg_grammar **out);
+
+/* Release host and device memory of a grammar.  NULL is ignored. */
+void cg_free_grammar(cg_grammar *g);
+
+/* Sizes of a compiled grammar. */
+int cg_grammar_info(const cg_grammar *g, cg_info *info);
+
+/* Set d_states[0..batch) to the start of the grammar (flags cleared). */
+int cg_init_state(const cg_grammar *g, cg_state *d_states, int32_t batch, void *stream);
+
+/*
+ * Packed token bitmask: bit (t & 63) of d_mask[r * words_per_row + (t >> 6)]
+ * is 1 iff row r is not finished and the bytes of token t are a legal
+ * continuation of the row's bytes (the row's bytes followed by token t can
+ * still be completed to a member).  Pad bits past vocab_size are 0.
+ * words_per_row must be >= ceil(vocab_size / 64); words beyond that are
+ * left untouched.  Depends only on the states, so it may run before the
+ * logits exist ("Evaluator aware decoding", "Why isn't this in production
+ * APIs yet?": masks come from pure automaton state ahead of the step).
+ */
+int cg_fill_bitmask(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
+                    int32_t words_per_row, void *stream);
+
+/* Bytes of the workspace cg_apply_mask_sample needs for (batch, vocab). */
+size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab);
+
+/*
+ * Masked softmax and pick, per row r:
+ *   logits x = d_logits[r * row_stride + t], t < vocab (dtype 0: float32,
+ *   1: bfloat16); allowed = mask bit; T = d_temperature[r].
+ *   T == 0: greedy, the allowed token of largest x (lowest id on ties),
+ *     logprob = x_id - logsumexp_allowed(x).
+ *   T > 0: a draw from softmax(x / T) restricted to the allowed tokens, by
+ *     two-level Gumbel-max over chunks of 2048 ids: chunk c has log-mass
+ *     L_c = logsumexp_{i in c, allowed}(x_i / T); the chunk is
+ *     argmax_c L_c + G(1, c), then the token argmax_{i in chunk} x_i/T +
+ *     G(0, i) (lowest index on ties), where G(l, i) = -ln(-ln u),
+ *     u = (w + 1/2) 2^-32, and w is word (i & 3) of Philox4x32-10 (Salmon et
+ *     al., SC'11) at counter (i >> 2, d_step[r], l, 0) with key d_seed[r]
+ *     (low word first).  logprob = x_id / T - logsumexp_allowed(x / T).
+ *   No allowed token: id = -1, logprob = 0.
+ * ("Constrained decoding", "The guarantee": sampling runs after masking.)
+ * row_stride >= vocab elements.  d_workspace holds at least
+ * cg_sample_workspace_bytes(batch, vocab) bytes, 16-byte aligned.
+ * Outputs: d_out_ids[batch] int32, d_out_logprob[batch] float32.
+ */
+int cg_apply_mask_sample(const void *d_logits, int32_t dtype, int32_t batch, int32_t vocab, int64_t row_stride,
+                         const uint64_t *d_mask, int32_t words_per_row, const float *d_temperature,
+                         const uint64_t *d_seed, const int32_t *d_step, void *d_workspace, int32_t *d_out_ids,
+                         float *d_out_logprob, void *stream);
+
+/*
+ * Walk d_token_ids[r] for every row: -1 is a no-op (CG_ROW_NOOP).  A token
+ * whose bytes continue the row legally is committed: d_step[r] += 1, then
+ * the row is DONE if its bytes form a complete member, CAPPED if
+ * d_step[r] >= gen_cap.  Otherwise (illegal, id out of range, or the row is
+ * already finished) the row is left unchanged and d_status[r] is
+ * CG_ROW_REJECTED.  Ids may come from cg_apply_mask_sample or be forced by
+ * the caller: a forced token is a transition the model did not choose
+ * ("Evaluator aware decoding", "A concrete prototype on llama.cpp").
+ * d_step: in/out, tokens accepted so far (the caller zeroes it at start).
+ */
+int cg_advance(const cg_grammar *g, cg_state *d_states, int32_t batch, const int32_t *d_token_ids, int32_t *d_step,
+               int32_t *d_status, void *stream);
+
+/*
+ * Host-side diagnostic: run `bytes` against the automaton from its start.
+ * *refused_at = index of the first refused byte (len if none); *complete =
+ * 1 iff all bytes were accepted and form a complete member ("Constrained
+ * decoding", "Reading the grammar for a tool": try-input says where a
+ * candidate would have been refused).
+ */
+int cg_try_input(const cg_grammar *g, const uint8_t *bytes, size_t len, size_t *refused_at, int *complete);
+
+/* Message of the last error on this thread ("" if none). */
+const char *cg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CG_H */

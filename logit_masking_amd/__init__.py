@@ -1,0 +1,212 @@
+"""logit_masking_amd -- Python binding of libcg.so, the MI355X constrained-decoding
+hot path (grammar -> pushdown automaton tables, token bitmask, masked
+sampling, state advance).  Argument marshalling only: every step runs in the
+library's HIP kernels.  Device buffers are torch tensors; torch supplies
+memory and the current HIP stream, nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcg.so")
+
+CG_OK, CG_E_ARG, CG_E_PARSE, CG_E_UNSUPPORTED, CG_E_LIMIT, CG_E_VOCAB, CG_E_DEVICE = 0, -1, -2, -3, -4, -5, -6
+ROW_OK, ROW_DONE, ROW_CAPPED, ROW_REJECTED, ROW_NOOP = 0, 1, 2, 3, 4
+FLAG_DONE, FLAG_CAPPED = 1, 2
+HOST_ONLY = 1
+STATE_BYTES = 24
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+# Symbols the C ABI (include/cg.h) exports.
+EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask",
+           "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
+
+
+class CgError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("gen_cap", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("vocab_size", ctypes.c_int32), ("words_per_row", ctypes.c_int32),
+                ("max_token_len", ctypes.c_int32), ("n_states", ctypes.c_int32),
+                ("table_entries", ctypes.c_int32), ("table_bytes", ctypes.c_int32),
+                ("compile_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcg.so; fails loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with logit_masking_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.cg_compile_grammar.argtypes = [ctypes.c_char_p, sz, vp, vp, i32, ctypes.POINTER(Options),
+                                         ctypes.POINTER(vp)]
+        L.cg_free_grammar.argtypes = [vp]
+        L.cg_free_grammar.restype = None
+        L.cg_grammar_info.argtypes = [vp, ctypes.POINTER(Info)]
+        L.cg_init_state.argtypes = [vp, vp, i32, vp]
+        L.cg_fill_bitmask.argtypes = [vp, vp, i32, vp, i32, vp]
+        L.cg_sample_workspace_bytes.argtypes = [i32, i32]
+        L.cg_sample_workspace_bytes.restype = sz
+        L.cg_apply_mask_sample.argtypes = [vp, i32, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.cg_advance.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
+        L.cg_last_error.restype = ctypes.c_char_p
+        for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask",
+                     "cg_apply_mask_sample", "cg_advance", "cg_try_input"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != CG_OK:
+        raise CgError(rc, lib().cg_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream) or 0)
+
+
+def _dev(t, dtype, name, ndim=None):
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return t
+
+
+class Grammar:
+    """A compiled grammar (cg_compile_grammar) bound to a vocabulary."""
+
+    def __init__(self, spec_json: bytes, blob: bytes, offsets, gen_cap: int = 2048, host_only: bool = False):
+        import numpy as np
+        L = lib()
+        if isinstance(spec_json, str):
+            spec_json = spec_json.encode()
+        off = np.ascontiguousarray(np.asarray(offsets, dtype=np.uint32))
+        bl = np.frombuffer(blob if blob else b"\0", dtype=np.uint8)
+        self._keep = (off, bl)
+        h = ctypes.c_void_p()
+        opts = Options(gen_cap, HOST_ONLY if host_only else 0)
+        _check(L.cg_compile_grammar(spec_json, len(spec_json), bl.ctypes.data, off.ctypes.data, len(off) - 1,
+                                    ctypes.byref(opts), ctypes.byref(h)))
+        self._h = h
+        self.V = len(off) - 1
+        self.W = (self.V + 63) // 64
+        self.gen_cap = gen_cap
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.cg_free_grammar(h)
+            self._h = None
+
+    def info(self) -> dict:
+        i = Info()
+        _check(lib().cg_grammar_info(self._h, ctypes.byref(i)))
+        return {k: getattr(i, k) for k, _ in Info._fields_}
+
+    def try_input(self, data: bytes):
+        """(refused_at, complete) of the host walker over the packed table."""
+        buf = ctypes.create_string_buffer(data, len(data)) if data else None
+        ra, cp = ctypes.c_size_t(), ctypes.c_int()
+        _check(lib().cg_try_input(self._h, buf, len(data), ctypes.byref(ra), ctypes.byref(cp)))
+        return ra.value, bool(cp.value)
+
+    # ---- device calls (async on the current stream) --------------------
+    def new_states(self, B: int, device="cuda"):
+        import torch
+        return torch.empty((B, STATE_BYTES), dtype=torch.uint8, device=device)
+
+    def init_state(self, states, stream=None):
+        import torch
+        _dev(states, torch.uint8, "states", 2)
+        _check(lib().cg_init_state(self._h, _ptr(states), states.shape[0], _stream(stream)))
+
+    def fill_bitmask(self, states, mask, stream=None):
+        import torch
+        _dev(states, torch.uint8, "states", 2)
+        _dev(mask, torch.int64, "mask", 2)
+        if mask.shape[0] < states.shape[0]:
+            raise ValueError("mask has fewer rows than states")
+        _check(lib().cg_fill_bitmask(self._h, _ptr(states), states.shape[0], _ptr(mask), mask.shape[1],
+                                     _stream(stream)))
+
+    def advance(self, states, ids, steps, status, stream=None):
+        import torch
+        _dev(states, torch.uint8, "states", 2)
+        for t, n in ((ids, "ids"), (steps, "steps"), (status, "status")):
+            _dev(t, torch.int32, n, 1)
+            if t.shape[0] < states.shape[0]:
+                raise ValueError(f"{n} has fewer rows than states")
+        _check(lib().cg_advance(self._h, _ptr(states), states.shape[0], _ptr(ids), _ptr(steps), _ptr(status),
+                                _stream(stream)))
+
+
+def sample_workspace_bytes(B: int, V: int) -> int:
+    return int(lib().cg_sample_workspace_bytes(B, V))
+
+
+def new_workspace(B: int, V: int, device="cuda"):
+    import torch
+    n = max(16, sample_workspace_bytes(B, V))
+    return torch.empty((n + 15) // 16 * 2, dtype=torch.float64, device=device)
+
+
+def apply_mask_sample(logits, mask, temperature, seed, step, workspace, out_ids, out_logprob, vocab=None,
+                      stream=None):
+    """cg_apply_mask_sample on torch tensors: logits [B, stride] float32 or
+    bfloat16, mask [B, W] int64, temperature [B] float32, seed [B] int64
+    (the u64 bits), step [B] int32, outputs ids [B] int32, logprob [B] float32."""
+    import torch
+    if logits.dtype == torch.float32:
+        dt = DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    else:
+        raise ValueError("logits must be float32 or bfloat16")
+    if not logits.is_cuda or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D device tensor with unit column stride")
+    B = logits.shape[0]
+    V = logits.shape[1] if vocab is None else vocab
+    _dev(mask, torch.int64, "mask", 2)
+    _dev(temperature, torch.float32, "temperature", 1)
+    _dev(seed, torch.int64, "seed", 1)
+    _dev(step, torch.int32, "step", 1)
+    _dev(out_ids, torch.int32, "out_ids", 1)
+    _dev(out_logprob, torch.float32, "out_logprob", 1)
+    if workspace.numel() * workspace.element_size() < sample_workspace_bytes(B, V):
+        raise ValueError("workspace too small")
+    for t, n in ((mask, "mask"), (temperature, "temperature"), (seed, "seed"), (step, "step"),
+                 (out_ids, "out_ids"), (out_logprob, "out_logprob")):
+        if t.shape[0] < B:
+            raise ValueError(f"{n} has fewer rows than logits")
+    _check(lib().cg_apply_mask_sample(_ptr(logits), dt, B, V, logits.stride(0), _ptr(mask), mask.shape[1],
+                                      _ptr(temperature), _ptr(seed), _ptr(step), _ptr(workspace), _ptr(out_ids),
+                                      _ptr(out_logprob), _stream(stream)))

@@ -1,0 +1,144 @@
+// cg_internal.hpp -- automaton table format shared by the host compiler, the
+// host walker behind cg_try_input, and the gfx950 kernels.
+//
+// The control of the pushdown automaton is a byte-level transition table
+// packed by row displacement ("comb"): a state's id is its base offset, and
+// the transition of state q on byte b is the 64-bit slot comb[q + b], valid
+// iff the slot's owner field equals q.  One table lookup per byte, no byte
+// classes, no per-state descriptor.
+//
+// Slot layout (little-endian u64):
+//   bits  0..15  owner   state id whose row this slot belongs to (0xFFFF: empty)
+//   bits 16..31  next    next state (see ops)
+//   bits 32..35  op      what the byte does to the registers besides moving
+//   bits 36..63  arg     operand (28 bits)
+//
+// Registers of a configuration besides the state: the open string's
+// remaining code points (cnt) and resume state (ret), the whitespace run
+// (ws), and a bit stack of open any-JSON containers (stk, depth) -- the
+// automaton's stack alphabet is {object, array}; everything a schema fixes
+// statically lives in the control states.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/cg.h"
+
+namespace cg {
+
+enum Op : uint32_t {
+    OP_NONE = 0,      // q = next
+    OP_WS = 1,        // whitespace byte: ws += 1, refused past ws_max
+    OP_CHAR = 2,      // first byte of a string code point: refused when cnt == 0, cnt -= 1
+    OP_STR_OPEN = 3,  // opening quote: ret = next, q = string body, cnt = arg
+    OP_STR_CLOSE = 4, // closing quote: q = ret
+    OP_PUSH = 5,      // open container: bit = arg & 1 (0 object, 1 array); refused if depth >= arg >> 1
+    OP_POP = 6,       // close container: pop; depth == 0 ? next : (top bit ? arg >> 14 : arg & 0x3FFF)
+};
+
+constexpr uint32_t kEmptyOwner = 0xFFFF;
+constexpr uint32_t kMaxStateId = 0x3FFF;   // POP packs two state ids in 28 bits
+constexpr uint32_t kUncapped = 0x0FFFFFFF; // cnt of an uncapped string
+constexpr int kMaxTokenLen = 32;
+
+// Per-grammar constants needed by every walker.
+struct WalkConsts {
+    uint32_t s_body;   // state of a string body at a code-point boundary
+    uint32_t accept;   // the single accepting state (no outgoing bytes)
+    uint32_t start;    // start state
+    uint32_t ws_max;   // longest whitespace run
+    uint32_t q_limit;  // every valid state id is < q_limit (comb has q_limit + 256 slots)
+};
+
+// A configuration in registers.
+struct Walker {
+    uint32_t q, ret, cnt, ws, depth;
+    uint64_t stk;
+};
+
+__host__ __device__ inline Walker load_walker(const cg_state &s) {
+    Walker w;
+    w.q = s.q;
+    w.ret = s.ret;
+    w.cnt = s.cnt;
+    w.ws = s.ws;
+    w.depth = s.depth;
+    w.stk = s.stk;
+    return w;
+}
+
+__host__ __device__ inline void store_walker(cg_state &s, const Walker &w) {
+    s.q = (uint16_t)w.q;
+    s.ret = (uint16_t)w.ret;
+    s.cnt = w.cnt;
+    s.ws = (uint8_t)w.ws;
+    s.depth = (uint8_t)w.depth;
+    s.stk = w.stk;
+}
+
+// One byte.  Returns false if the byte is refused (the walker is then
+// unspecified but every state id in it stays < q_limit, so a dead lane may
+// keep indexing the table safely).
+__host__ __device__ inline bool step_byte(Walker &w, uint32_t b, const uint64_t *comb, const WalkConsts &k) {
+    const uint64_t e = comb[w.q + b];
+    const uint32_t lo = (uint32_t)e, hi = (uint32_t)(e >> 32);
+    bool ok = (lo & 0xFFFFu) == w.q;
+    uint32_t nq = lo >> 16;
+    const uint32_t op = hi & 0xFu, arg = hi >> 4;
+    const uint32_t ws1 = (op == OP_WS) ? w.ws + 1 : 0;
+    ok = ok && ws1 <= k.ws_max;
+    w.ws = ws1;
+    if (op == OP_CHAR) {
+        ok = ok && w.cnt != 0;
+        w.cnt -= 1;
+    } else if (op == OP_STR_OPEN) {
+        w.ret = nq;
+        nq = k.s_body;
+        w.cnt = arg;
+    } else if (op == OP_STR_CLOSE) {
+        nq = w.ret;
+    } else if (op == OP_PUSH) {
+        ok = ok && w.depth < (arg >> 1);
+        w.stk = (w.stk << 1) | (arg & 1u);
+        w.depth += 1;
+    } else if (op == OP_POP) {
+        w.stk >>= 1;
+        w.depth -= 1;
+        nq = (w.depth == 0) ? nq : ((w.stk & 1u) ? (arg >> 14) : (arg & 0x3FFFu));
+    }
+    w.q = nq;
+    return ok;
+}
+
+// Device copy of a compiled grammar.
+struct DeviceTables {
+    uint64_t *comb = nullptr;     // [comb_len]
+    uint32_t *tokw = nullptr;     // [nw][V] token bytes, 4 per word, little-endian, zero padded
+    uint8_t *toklen = nullptr;    // [V]
+    uint8_t *blob = nullptr;      // token bytes, concatenated
+    uint32_t *offsets = nullptr;  // [V+1]
+};
+
+}  // namespace cg
+
+struct cg_grammar {
+    cg::WalkConsts k;
+    uint32_t comb_len = 0;
+    int32_t V = 0;
+    int32_t max_len = 0;
+    int32_t nw = 0;          // words per token in tokw (ceil(max_len / 4), at least 1)
+    int32_t n_states = 0;
+    uint32_t gen_cap = 2048;
+    int device = -1;         // HIP device the tables live on (-1: host only)
+    int n_cu = 256;          // compute units of that device
+    double compile_ms = 0;
+    uint64_t *host_comb = nullptr;
+    cg::DeviceTables dev;
+};
+
+namespace cg {
+// compiler.cpp: parse + build + pack; fills host_comb/comb_len/k/n_states.
+// Returns CG_OK or an error code (message via set_error).
+int compile_spec(const char *spec, size_t len, cg_grammar *g);
+void set_error(const char *fmt, ...);
+}  // namespace cg

@@ -97,6 +97,8 @@ def lib():
             L.oc_mask_rows.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, i32]
             L.oc_mask_rows.restype = i64
             L.oc_next_bytes.argtypes = [vp, vp, vp]
+            L.og_sat.argtypes = [vp, i32, i32]
+            L.og_sat.restype = ctypes.c_int
             _lib = L
     return _lib
 
@@ -331,6 +333,9 @@ class Grammar:
         elif kind == "json_schema":
             og.gkind = G_JSON
             og.root = b.schema(spec.get("schema"), "$.schema", 0)
+            # prefix-free languages only: a number at the root has no end
+            if "num" in _first_classes(og.root, b.nodes, b.props):
+                raise Unsupported("$.schema", "the root value must end by itself (object, array, string, literal)")
         elif kind == "tool_call":
             og.gkind = G_TOOL
             tools = spec.get("tools")
@@ -369,6 +374,12 @@ class Grammar:
         self._og = og
         self._L = lib()
         self.conf_size = self._L.oc_size()
+        # the language must not be empty
+        if og.gkind == G_JSON and not self._L.og_sat(ctypes.byref(og), og.root, 0):
+            raise Unsupported("$", "grammar accepts no string")
+        if og.gkind == G_TOOL and not any(self._L.og_sat(ctypes.byref(og), b.props[og.tools_first + i]["node"], 0)
+                                          for i in range(og.tools_count)):
+            raise Unsupported("$", "grammar accepts no string")
 
     # -- configurations --------------------------------------------------
     def start(self):

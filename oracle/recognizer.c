@@ -786,6 +786,8 @@ static int step_frame(const og *g, oconf *c, ofr *f, int ch) {
 }
 
 /* ---- public API --------------------------------------------------------- */
+int og_sat(const og *g, int node, int depth) { return sat(g, node, depth); }
+
 int oc_size(void) { return (int)sizeof(oconf); }
 
 void oc_start(const og *g, oconf *c) {
@@ -796,8 +798,11 @@ void oc_start(const og *g, oconf *c) {
     }
     ofr *r = push(c, F_ROOT, -1);
     if (g->gkind == G_TOOL) {
+        /* tools whose arguments can be completed */
         r->phase = RT_NAME;
-        r->cand = (g->tools_count >= 64) ? ~0ull : ((1ull << g->tools_count) - 1);
+        r->cand = 0;
+        for (int i = 0; i < g->tools_count; i++)
+            if (sat(g, g->props[g->tools_first + i].node, 0)) r->cand |= 1ull << i;
     } else {
         r->phase = RT_VALUE;
     }
