@@ -159,7 +159,7 @@ int cg_init_state(const cg_grammar *g, cg_state *d_states, int32_t batch, void *
 int cg_fill_bitmask(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
                     int32_t words_per_row, void *stream);
 
-/* Bytes of the workspace cg_apply_mask_sample needs for (batch, vocab). */
+/* Bytes of the workspace cg_apply_mask_sample needs for (batch, vocab) (0 if batch or vocab < 1). */
 size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab);
 
 /*
@@ -178,8 +178,10 @@ size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab);
  *     (low word first).  logprob = x_id / T - logsumexp_allowed(x / T).
  *   No allowed token: id = -1, logprob = 0.
  * ("Constrained decoding", "The guarantee": sampling runs after masking.)
- * row_stride >= vocab elements.  d_workspace holds at least
- * cg_sample_workspace_bytes(batch, vocab) bytes, 16-byte aligned.
+ * row_stride >= vocab elements; vocab <= 6,291,456.
+ * d_workspace: cg_sample_workspace_bytes(batch, vocab) bytes, 16-byte
+ *   aligned; may be NULL when that size is 0 (this build keeps every
+ *   intermediate on chip, so it always is).
  * Outputs: d_out_ids[batch] int32, d_out_logprob[batch] float32.
  */
 int cg_apply_mask_sample(const void *d_logits, int32_t dtype, int32_t batch, int32_t vocab, int64_t row_stride,

@@ -174,9 +174,10 @@ def sample_workspace_bytes(B: int, V: int) -> int:
 
 
 def new_workspace(B: int, V: int, device="cuda"):
+    """A workspace for apply_mask_sample (possibly empty)."""
     import torch
-    n = max(16, sample_workspace_bytes(B, V))
-    return torch.empty((n + 15) // 16 * 2, dtype=torch.float64, device=device)
+    n = sample_workspace_bytes(B, V)
+    return torch.zeros(max(1, (n + 15) // 16 * 2), dtype=torch.float64, device=device)
 
 
 def apply_mask_sample(logits, mask, temperature, seed, step, workspace, out_ids, out_logprob, vocab=None,

@@ -43,9 +43,7 @@ void release(cg_grammar *g) {
         (void)hipSetDevice(g->device);
         (void)hipFree(g->dev.comb);
         (void)hipFree(g->dev.tokw);
-        (void)hipFree(g->dev.toklen);
-        (void)hipFree(g->dev.blob);
-        (void)hipFree(g->dev.offsets);
+        (void)hipFree(g->dev.tokinfo);
         (void)hipSetDevice(cur);
     }
     free(g->host_comb);
@@ -53,6 +51,22 @@ void release(cg_grammar *g) {
 }
 
 bool on_device(const cg_grammar *g) { return g && g->device >= 0; }
+
+// Walk a token through the string body from a code-point boundary with the
+// same table the kernels use; see tokinfo in cg_internal.hpp.
+uint32_t string_summary(const cg_grammar *g, const uint8_t *s, uint32_t n) {
+    if (g->k.s_body >= g->k.q_limit) return STR_DEAD << 8;
+    uint32_t q = g->k.s_body, chars = 0;
+    for (uint32_t i = 0; i < n; i++) {
+        const uint64_t e = g->host_comb[q + s[i]];
+        const uint32_t lo = (uint32_t)e, op = (uint32_t)(e >> 32) & 0xFu;
+        if ((lo & 0xFFFFu) != q) return STR_DEAD << 8;
+        if (op == OP_STR_CLOSE) return (STR_QUOTE << 8) | (chars << 10) | (i << 16);
+        if (op == OP_CHAR) chars++;
+        q = lo >> 16;
+    }
+    return (STR_IN << 8) | (chars << 10);
+}
 
 }  // namespace
 
@@ -101,17 +115,16 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
         g->device = dev;
         if (hipDeviceGetAttribute(&g->n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || g->n_cu < 1)
             g->n_cu = 256;
-        const size_t V = (size_t)vocab_size, nbytes = tok_offsets[vocab_size];
+        const size_t V = (size_t)vocab_size;
         std::vector<uint32_t> tokw((size_t)g->nw * V, 0u);
-        std::vector<uint8_t> toklen(V);
+        std::vector<uint32_t> tokinfo(V);
         for (size_t t = 0; t < V; t++) {
             const uint32_t a = tok_offsets[t], n = tok_offsets[t + 1] - a;
-            toklen[t] = (uint8_t)n;
+            tokinfo[t] = n | string_summary(g, tok_bytes + a, n);
             for (uint32_t i = 0; i < n; i++) tokw[(size_t)(i >> 2) * V + t] |= (uint32_t)tok_bytes[a + i] << (8 * (i & 3));
         }
         if (upload(&g->dev.comb, g->host_comb, g->comb_len) || upload(&g->dev.tokw, tokw.data(), tokw.size()) ||
-            upload(&g->dev.toklen, toklen.data(), V) || upload(&g->dev.blob, tok_bytes, nbytes) ||
-            upload(&g->dev.offsets, tok_offsets, V + 1)) {
+            upload(&g->dev.tokinfo, tokinfo.data(), V)) {
             set_error("device upload failed: %s", hipGetErrorString(hipGetLastError()));
             release(g);
             return CG_E_DEVICE;
@@ -160,13 +173,13 @@ int cg_apply_mask_sample(const void *d_logits, int32_t dtype, int32_t batch, int
                          float *d_out_logprob, void *stream) {
     if (dtype != 0 && dtype != 1) return arg_error("dtype must be 0 (float32) or 1 (bfloat16)");
     if (batch < 0 || vocab < 1) return arg_error("bad batch / vocab");
-    if (batch > 65535) return arg_error("batch above 65535");
     if (row_stride < vocab) return arg_error("row_stride < vocab");
     if (words_per_row < (vocab + 63) / 64) return arg_error("words_per_row < ceil(vocab / 64)");
     if (batch == 0) return CG_OK;
-    if (!d_logits || !d_mask || !d_temperature || !d_seed || !d_step || !d_workspace || !d_out_ids || !d_out_logprob)
+    if (!d_logits || !d_mask || !d_temperature || !d_seed || !d_step || !d_out_ids || !d_out_logprob)
         return arg_error("NULL device pointer");
-    if ((uintptr_t)d_workspace % 16) return arg_error("workspace must be 16-byte aligned");
+    if (sample_workspace_bytes(batch, vocab) > 0 && (!d_workspace || (uintptr_t)d_workspace % 16))
+        return arg_error("workspace must be a 16-byte aligned device buffer");
     return launch_sample(d_logits, dtype, batch, vocab, row_stride, d_mask, words_per_row, d_temperature, d_seed,
                          d_step, d_workspace, d_out_ids, d_out_logprob, (hipStream_t)stream);
 }

@@ -43,7 +43,7 @@ constexpr int kMaxTokenLen = 32;
 
 // Per-grammar constants needed by every walker.
 struct WalkConsts {
-    uint32_t s_body;   // state of a string body at a code-point boundary
+    uint32_t s_body;   // state of a string body at a code-point boundary (0xFFFF: no strings)
     uint32_t accept;   // the single accepting state (no outgoing bytes)
     uint32_t start;    // start state
     uint32_t ws_max;   // longest whitespace run
@@ -78,45 +78,65 @@ __host__ __device__ inline void store_walker(cg_state &s, const Walker &w) {
 
 // One byte.  Returns false if the byte is refused (the walker is then
 // unspecified but every state id in it stays < q_limit, so a dead lane may
-// keep indexing the table safely).
+// keep indexing the table safely).  The common ops (move, whitespace, string
+// code point) are straight-line; string open/close and container push/pop
+// take the rare branch.
 __host__ __device__ inline bool step_byte(Walker &w, uint32_t b, const uint64_t *comb, const WalkConsts &k) {
     const uint64_t e = comb[w.q + b];
     const uint32_t lo = (uint32_t)e, hi = (uint32_t)(e >> 32);
     bool ok = (lo & 0xFFFFu) == w.q;
     uint32_t nq = lo >> 16;
-    const uint32_t op = hi & 0xFu, arg = hi >> 4;
+    const uint32_t op = hi & 0xFu;
     const uint32_t ws1 = (op == OP_WS) ? w.ws + 1 : 0;
     ok = ok && ws1 <= k.ws_max;
     w.ws = ws1;
-    if (op == OP_CHAR) {
-        ok = ok && w.cnt != 0;
-        w.cnt -= 1;
-    } else if (op == OP_STR_OPEN) {
-        w.ret = nq;
-        nq = k.s_body;
-        w.cnt = arg;
-    } else if (op == OP_STR_CLOSE) {
-        nq = w.ret;
-    } else if (op == OP_PUSH) {
-        ok = ok && w.depth < (arg >> 1);
-        w.stk = (w.stk << 1) | (arg & 1u);
-        w.depth += 1;
-    } else if (op == OP_POP) {
-        w.stk >>= 1;
-        w.depth -= 1;
-        nq = (w.depth == 0) ? nq : ((w.stk & 1u) ? (arg >> 14) : (arg & 0x3FFFu));
+    const bool ch = op == OP_CHAR;
+    ok = ok && !(ch && w.cnt == 0);
+    w.cnt -= ch ? 1u : 0u;
+    if (op > OP_CHAR) {
+        const uint32_t arg = hi >> 4;
+        if (op == OP_STR_OPEN) {
+            w.ret = nq;
+            nq = k.s_body;
+            w.cnt = arg;
+        } else if (op == OP_STR_CLOSE) {
+            nq = w.ret;
+        } else if (op == OP_PUSH) {
+            ok = ok && w.depth < (arg >> 1);
+            w.stk = (w.stk << 1) | (arg & 1u);
+            w.depth += 1;
+        } else {
+            w.stk >>= 1;
+            w.depth -= 1;
+            nq = (w.depth == 0) ? nq : ((w.stk & 1u) ? (arg >> 14) : (arg & 0x3FFFu));
+        }
     }
     w.q = nq;
     return ok;
 }
 
+// Per-token summary of a walk through a string body that starts at a
+// code-point boundary (state s_body): the body's transitions depend on
+// nothing but the byte and the code-point budget, so one word per token
+// decides it.  Layout of tokinfo[t]:
+//   bits 0..7   token length in bytes
+//   bits 8..9   STR_IN (the token ends inside the string), STR_QUOTE (an
+//               unescaped quote closes the string at byte `pos`), STR_DEAD
+//   bits 10..15 code points the token adds to the string before it ends or
+//               the quote (each needs one unit of the budget cnt)
+//   bits 16..20 pos
+enum : uint32_t { STR_IN = 0, STR_QUOTE = 2, STR_DEAD = 3 };
+
+__host__ __device__ inline uint32_t tok_len(uint32_t info) { return info & 0xFFu; }
+__host__ __device__ inline uint32_t tok_kind(uint32_t info) { return (info >> 8) & 3u; }
+__host__ __device__ inline uint32_t tok_chars(uint32_t info) { return (info >> 10) & 63u; }
+__host__ __device__ inline uint32_t tok_pos(uint32_t info) { return (info >> 16) & 31u; }
+
 // Device copy of a compiled grammar.
 struct DeviceTables {
     uint64_t *comb = nullptr;     // [comb_len]
     uint32_t *tokw = nullptr;     // [nw][V] token bytes, 4 per word, little-endian, zero padded
-    uint8_t *toklen = nullptr;    // [V]
-    uint8_t *blob = nullptr;      // token bytes, concatenated
-    uint32_t *offsets = nullptr;  // [V+1]
+    uint32_t *tokinfo = nullptr;  // [V] length + string-body summary
 };
 
 }  // namespace cg

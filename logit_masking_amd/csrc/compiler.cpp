@@ -891,6 +891,9 @@ void trim_and_pack(Builder &B, cg_grammar *g) {
     if (max_base > (int)kMaxStateId)
         throw CompileError{CG_E_LIMIT, "$: automaton too large (" + std::to_string(order.size()) + " states)"};
     const uint32_t comb_len = (uint32_t)max_base + 1 + 256;
+    if (comb_len * sizeof(uint64_t) > 60 * 1024)
+        throw CompileError{CG_E_LIMIT, "$: transition table of " + std::to_string(comb_len * 8) +
+                                           " bytes exceeds the 60 KiB staged in LDS"};
     uint64_t *comb = (uint64_t *)malloc(sizeof(uint64_t) * comb_len);
     const uint32_t start_id = (uint32_t)base[B.start];
     for (uint32_t i = 0; i < comb_len; i++) comb[i] = (uint64_t)kEmptyOwner | ((uint64_t)start_id << 16);
@@ -912,7 +915,7 @@ void trim_and_pack(Builder &B, cg_grammar *g) {
     g->n_states = (int)order.size();
     g->k.start = start_id;
     g->k.accept = (uint32_t)base[B.accept];
-    g->k.s_body = B.s_body >= 0 ? (uint32_t)base[B.s_body] : start_id;
+    g->k.s_body = (B.s_body >= 0 && reach[B.s_body]) ? (uint32_t)base[B.s_body] : 0xFFFFu;
     g->k.ws_max = (uint32_t)B.S.ws_max;
     g->k.q_limit = (uint32_t)max_base + 1;
 }

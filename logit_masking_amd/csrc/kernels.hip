@@ -41,10 +41,16 @@ __global__ void k_init(cg_state *__restrict__ states, int B, uint32_t start) {
     states[r] = s;
 }
 
-__global__ void k_advance(const uint64_t *__restrict__ comb, WalkConsts k, const uint8_t *__restrict__ blob,
-                          const uint32_t *__restrict__ off, int V, cg_state *__restrict__ states, int B,
-                          const int32_t *__restrict__ ids, int32_t *__restrict__ steps, int32_t *__restrict__ status,
-                          uint32_t gen_cap) {
+// One lane per row; the transition table is staged in LDS first so the
+// byte walk is a chain of LDS lookups, not of L2 round trips.
+__global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ comb, uint32_t comb_len, WalkConsts k,
+                                                 const uint32_t *__restrict__ tokw, const uint32_t *__restrict__ tokinfo,
+                                                 int nw, int V, cg_state *__restrict__ states, int B,
+                                                 const int32_t *__restrict__ ids, int32_t *__restrict__ steps,
+                                                 int32_t *__restrict__ status, uint32_t gen_cap) {
+    extern __shared__ uint64_t lds_comb[];
+    for (uint32_t i = threadIdx.x; i < comb_len; i += blockDim.x) lds_comb[i] = comb[i];
+    __syncthreads();
     int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= B) return;
     const int id = ids[r];
@@ -57,10 +63,13 @@ __global__ void k_advance(const uint64_t *__restrict__ comb, WalkConsts k, const
         status[r] = CG_ROW_REJECTED;
         return;
     }
-    const uint32_t a = off[id], e = off[id + 1];
+    const uint32_t n = tok_len(tokinfo[id]);
     Walker w = load_walker(s);
-    bool ok = a < e;
-    for (uint32_t i = a; ok && i < e; i++) ok = step_byte(w, blob[i], comb, k);
+    bool ok = n > 0;
+    for (uint32_t i = 0; ok && i < n; i++) {
+        const uint32_t word = tokw[(size_t)(i >> 2) * V + id];
+        ok = step_byte(w, (word >> (8 * (i & 3))) & 0xFFu, lds_comb, k);
+    }
     if (!ok) {
         status[r] = CG_ROW_REJECTED;
         return;
@@ -86,62 +95,88 @@ __global__ void k_advance(const uint64_t *__restrict__ comb, WalkConsts k, const
 // ---------------------------------------------------------------------------
 // fill_bitmask
 // ---------------------------------------------------------------------------
-__device__ inline int wave_max_i32(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-    return v;
+
+constexpr int kMaxRowsPerItem = 64;
+
+// Byte Bi of the token (compile-time index: the walk is fully unrolled, so
+// the token words stay in registers with no dynamic indexing).  A lane walks
+// bytes [start, end) of its token while alive; the wave leaves as soon as no
+// lane has bytes left.
+template <int Bi, int NB, int NW>
+__device__ __forceinline__ void walk_bytes(Walker &wk, bool &alive, const uint32_t (&w)[NW], int start, int end,
+                                           const uint64_t *lds_comb, const WalkConsts &k) {
+    if constexpr (Bi < NB) {
+        if (!__any(alive && Bi < end)) return;
+        if (alive && Bi >= start && Bi < end)
+            alive = step_byte(wk, (w[Bi >> 2] >> ((Bi & 3) * 8)) & 0xFFu, lds_comb, k);
+        walk_bytes<Bi + 1, NB, NW>(wk, alive, w, start, end, lds_comb, k);
+    }
 }
 
-// Work item = (block of 256 consecutive tokens, group of rows).  Each wave
-// owns 64 tokens = one mask word per row; its lanes keep their token's bytes
-// in registers while the loop runs over the rows of the item, so the
-// vocabulary is read once per item, not once per row.
+// Work item = (block of 256 consecutive tokens, an interleaved group of
+// rows r = rg, rg + n_rg, ...).  Each wave owns 64 tokens = one mask word per
+// row; its lanes keep their token's bytes in registers while the loop runs
+// over the item's rows, whose states are staged in LDS.  A row inside an
+// open string at a code-point boundary first consults the token's string
+// summary: most tokens are decided there without walking a byte.
 template <int NW>
 __global__ __launch_bounds__(256) void k_fill(const uint64_t *__restrict__ comb, uint32_t comb_len,
-                                              const uint32_t *__restrict__ tokw, const uint8_t *__restrict__ toklen,
-                                              int V, const cg_state *__restrict__ states, int B,
+                                              const uint32_t *__restrict__ tokw,
+                                              const uint32_t *__restrict__ tokinfo, int V,
+                                              const cg_state *__restrict__ states, int B,
                                               uint64_t *__restrict__ mask, int words_per_row, WalkConsts k,
-                                              int n_tok_blocks, int rows_per_item, int n_items) {
-    extern __shared__ uint64_t lds_comb[];
+                                              int n_tok_blocks, int n_rg, int n_items) {
+    extern __shared__ uint64_t lds[];
+    uint64_t *lds_comb = lds;
+    cg_state *lds_rows = (cg_state *)(lds + comb_len);
     for (uint32_t i = threadIdx.x; i < comb_len; i += blockDim.x) lds_comb[i] = comb[i];
-    __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Wv = (V + 63) >> 6;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int tb = item % n_tok_blocks, rg = item / n_tok_blocks;
+        const int nrows = (B - rg + n_rg - 1) / n_rg;
+        __syncthreads();  // the previous item's rows are no longer read
+        for (int i = threadIdx.x; i < nrows * 3; i += blockDim.x)
+            ((uint64_t *)lds_rows)[i] = ((const uint64_t *)states)[(size_t)(rg + (i / 3) * n_rg) * 3 + (i % 3)];
+        __syncthreads();
         const int word = tb * 4 + wave;
         const int tok = word * 64 + lane;
         uint32_t w[NW];
-        int len = 0;
+        uint32_t info = 0;
         if (tok < V) {
-            len = toklen[tok];
+            info = tokinfo[tok];
 #pragma unroll
             for (int j = 0; j < NW; j++) w[j] = tokw[(size_t)j * V + tok];
         } else {
 #pragma unroll
             for (int j = 0; j < NW; j++) w[j] = 0;
         }
-        const int wmax = wave_max_i32(len);
-        const int r0 = rg * rows_per_item;
-        const int r1 = min(B, r0 + rows_per_item);
-        for (int r = r0; r < r1; r++) {
-            const cg_state s = states[r];
+        const int len = (int)tok_len(info);
+        for (int i = 0; i < nrows; i++) {
+            const cg_state s = lds_rows[i];
+            const int r = rg + i * n_rg;
             uint64_t bits = 0;
             const bool live_row = !(s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) && s.q < k.q_limit &&
                                   s.ret < k.q_limit;
             if (live_row) {
                 Walker wk = load_walker(s);
                 bool alive = len > 0;
-#pragma unroll
-                for (int b = 0; b < NW * 4; b++) {
-                    if (b >= wmax) break;
-                    const bool act = alive && b < len;
-                    if (!__any(act)) break;
-                    if (act) {
-                        const uint32_t byte = (w[b >> 2] >> ((b & 3) * 8)) & 0xFFu;
-                        alive = step_byte(wk, byte, lds_comb, k);
+                int start = 0, end = len;
+                if (s.q == k.s_body) {
+                    // inside a string at a code-point boundary: the token's
+                    // summary decides it, or says where the string closes
+                    const uint32_t kind = tok_kind(info), nch = tok_chars(info);
+                    alive = alive && kind != STR_DEAD && nch <= wk.cnt;
+                    if (kind == STR_QUOTE) {
+                        wk.q = wk.ret;
+                        wk.ws = 0;
+                        wk.cnt -= nch;
+                        start = (int)tok_pos(info) + 1;
+                    } else {
+                        end = 0;
                     }
                 }
+                walk_bytes<0, NW * 4, NW>(wk, alive, w, start, end, lds_comb, k);
                 bits = __ballot(alive);
             }
             if (lane == 0 && word < Wv) mask[(size_t)r * words_per_row + word] = bits;
@@ -152,116 +187,16 @@ __global__ __launch_bounds__(256) void k_fill(const uint64_t *__restrict__ comb,
 // ---------------------------------------------------------------------------
 // mask_softmax_sample
 // ---------------------------------------------------------------------------
-constexpr int kChunk = 2048;           // ids per chunk (32 mask words)
+constexpr int kChunk = 2048;            // ids per chunk (32 mask words)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr double kContend = 2e-5;      // chunks whose screened score is this close to the best are recomputed
-
-struct Partial {
-    float m;   // largest allowed logit of the chunk (-inf if none)
-    int idx;   // its lowest id (-1 if none)
-    double s;  // sum over allowed ids of exp((x - m) / T')
-};
-
-__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+constexpr double kContendChunk = 2e-5;  // screened chunk scores carry < 2e-6 of rounding
 
 template <int DT>
 __device__ inline float load_logit(const void *p, size_t i) {
     if (DT == 0) return ((const float *)p)[i];
-    return bf16_to_f32(((const uint16_t *)p)[i]);
+    return __uint_as_float((uint32_t)((const uint16_t *)p)[i] << 16);
 }
 
-__device__ inline bool better(float v, int i, float bv, int bi) {
-    // larger value wins; equal values -> lower id; any allowed id beats none
-    if (bi < 0) return i >= 0;
-    if (i < 0) return false;
-    return v > bv || (v == bv && i < bi);
-}
-
-// One wave per (row, chunk); 4 chunks per block.  Lane l reads ids
-// c*2048 + g*512 + 8l .. +7 for g = 0..3: every load instruction covers 1 KB
-// (bf16) of contiguous logits across the wave, and one mask byte per group.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void k_sample_a(const void *__restrict__ logits, int V, int64_t stride,
-                                                  const uint64_t *__restrict__ mask, int words_per_row,
-                                                  const float *__restrict__ temp, Partial *__restrict__ part,
-                                                  int K) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int c = blockIdx.x * 4 + wave, r = blockIdx.y;
-    if (c >= K) return;
-    const float T = temp[r];
-    const float kk = T > 0.f ? kLog2e / T : kLog2e;
-    const uint8_t *mrow = (const uint8_t *)(mask + (size_t)r * words_per_row);
-    const size_t rowbase = (size_t)r * (size_t)stride;
-    float x[32];
-    uint32_t mb[4];
-#pragma unroll
-    for (int g = 0; g < 4; g++) {
-        const int e0 = c * kChunk + g * 512 + lane * 8;
-        mb[g] = (e0 < V) ? mrow[e0 >> 3] : 0u;
-        if (VEC && e0 + 8 <= V) {
-            if (DT == 1) {
-                const uint4 v = *(const uint4 *)((const uint16_t *)logits + rowbase + e0);
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    x[g * 8 + 2 * j] = __uint_as_float(u[j] << 16);
-                    x[g * 8 + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
-                }
-            } else {
-                const float4 v0 = *(const float4 *)((const float *)logits + rowbase + e0);
-                const float4 v1 = *(const float4 *)((const float *)logits + rowbase + e0 + 4);
-                x[g * 8 + 0] = v0.x; x[g * 8 + 1] = v0.y; x[g * 8 + 2] = v0.z; x[g * 8 + 3] = v0.w;
-                x[g * 8 + 4] = v1.x; x[g * 8 + 5] = v1.y; x[g * 8 + 6] = v1.z; x[g * 8 + 7] = v1.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; j++) x[g * 8 + j] = (e0 + j < V) ? load_logit<DT>(logits, rowbase + e0 + j) : 0.f;
-            if (e0 + 8 > V) mb[g] &= (e0 >= V) ? 0u : ((1u << (V - e0)) - 1u);
-        }
-    }
-    // masked max, lowest id on ties (ids increase with g, then j)
-    float m = -INFINITY;
-    int mi = -1;
-#pragma unroll
-    for (int g = 0; g < 4; g++)
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int e = c * kChunk + g * 512 + lane * 8 + j;
-            if (((mb[g] >> j) & 1u) && better(x[g * 8 + j], e, m, mi)) {
-                m = x[g * 8 + j];
-                mi = e;
-            }
-        }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float om = __shfl_xor(m, o, 64);
-        const int oi = __shfl_xor(mi, o, 64);
-        if (better(om, oi, m, mi)) {
-            m = om;
-            mi = oi;
-        }
-    }
-    double s = 0.0;
-    if (mi >= 0 && m != -INFINITY) {
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            float sg = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                if ((mb[g] >> j) & 1u) sg += exp2f((x[g * 8 + j] - m) * kk);
-            s += (double)sg;
-        }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (lane == 0) {
-        Partial p;
-        p.m = m;
-        p.idx = mi;
-        p.s = s;
-        part[(size_t)r * K + c] = p;
-    }
-}
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplications and a xor-recombination, key bumped by the
@@ -283,31 +218,56 @@ __device__ inline uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 __device__ inline uint32_t pick_word(uint4 v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 // -ln(-ln u), u = (w + 1/2) 2^-32, in double
-__device__ inline double gumbel(uint32_t w) {
+__device__ inline double gumbel64(uint32_t w) {
     const double u = ((double)w + 0.5) * 2.3283064365386963e-10;
     return -log(-log(u));
 }
 
-// block-wide reductions over 256 threads (4 waves)
-__device__ inline double block_max_d(double v, double *sh) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh[wave] = v;
-    __syncthreads();
-    return fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
+// ---- wave reductions with DPP lane permutes ------------------------------
+// Within each row of 16 lanes: swap neighbours, swap pairs, rotate by 4,
+// rotate by 8 (every lane of the row then holds the row's reduction); the
+// four row results are read with readlane.  No LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+template <class F>
+__device__ __forceinline__ float wave_reduce_f(float v, F op) {
+    v = op(v, __int_as_float(dpp_i<kQuadSwap1>(__float_as_int(v))));
+    v = op(v, __int_as_float(dpp_i<kQuadSwap2>(__float_as_int(v))));
+    v = op(v, __int_as_float(dpp_i<kRowRor4>(__float_as_int(v))));
+    v = op(v, __int_as_float(dpp_i<kRowRor8>(__float_as_int(v))));
+    const int b = __float_as_int(v);
+    return op(op(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+              op(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
-__device__ inline double block_sum_d(double v, double *sh) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh[wave] = v;
-    __syncthreads();
-    return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long u = __double_as_longlong(v);
+    const int lo = dpp_i<CTRL>((int)u), hi = dpp_i<CTRL>((int)(u >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const long long u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)u, l), hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+template <class F>
+__device__ __forceinline__ double wave_reduce_d(double v, F op) {
+    v = op(v, dpp_d<kQuadSwap1>(v));
+    v = op(v, dpp_d<kQuadSwap2>(v));
+    v = op(v, dpp_d<kRowRor4>(v));
+    v = op(v, dpp_d<kRowRor8>(v));
+    return op(op(readlane_d(v, 0), readlane_d(v, 16)), op(readlane_d(v, 32), readlane_d(v, 48)));
+}
+
+__device__ inline float wave_max_f(float v) { return wave_reduce_f(v, [](float a, float b) { return fmaxf(a, b); }); }
+__device__ inline double wave_max_d(double v) { return wave_reduce_d(v, [](double a, double b) { return fmax(a, b); }); }
+__device__ inline double wave_sum_d(double v) { return wave_reduce_d(v, [](double a, double b) { return a + b; }); }
 
 // argmax of (value, index): larger value, then lower index; index -1 = none
 __device__ inline void arg_better(double &v, int &i, double ov, int oi) {
@@ -317,151 +277,521 @@ __device__ inline void arg_better(double &v, int &i, double ov, int oi) {
         i = oi;
     }
 }
+template <int CTRL>
+__device__ __forceinline__ void arg_step(double &v, int &i) {
+    const double ov = dpp_d<CTRL>(v);
+    const int oi = dpp_i<CTRL>(i);
+    arg_better(v, i, ov, oi);
+}
+__device__ inline void wave_argmax(double &v, int &i) {
+    arg_step<kQuadSwap1>(v, i);
+    arg_step<kQuadSwap2>(v, i);
+    arg_step<kRowRor4>(v, i);
+    arg_step<kRowRor8>(v, i);
+    double bv = readlane_d(v, 0);
+    int bi = __builtin_amdgcn_readlane(i, 0);
+    for (int l = 16; l < 64; l += 16) arg_better(bv, bi, readlane_d(v, l), __builtin_amdgcn_readlane(i, l));
+    v = bv;
+    i = bi;
+}
 
-__device__ inline void block_argmax_d(double &v, int &i, double *shv, int *shi) {
+// Lane l holds ids c*2048 + g*512 + 8l + j (g = 0..3, j = 0..7): every load
+// instruction covers one contiguous 1 KB (bf16) / 2 KB (f32) of the row.
+template <int DT>
+struct ChunkRegs {
+    uint32_t d[DT == 1 ? 16 : 32];
+    uint32_t mb[4];
+};
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_chunk(ChunkRegs<DT> &R, const void *logits, size_t rowbase,
+                                           const uint8_t *mrow, int V, int c, int lane) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const double ov = __shfl_xor(v, o, 64);
-        const int oi = __shfl_xor(i, o, 64);
-        arg_better(v, i, ov, oi);
-    }
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) {
-        shv[wave] = v;
-        shi[wave] = i;
-    }
-    __syncthreads();
-    v = shv[0];
-    i = shi[0];
-    for (int k2 = 1; k2 < 4; k2++) arg_better(v, i, shv[k2], shi[k2]);
-}
-
-// log-mass of chunk c recomputed entirely in double (contenders only)
-template <int DT>
-__device__ double chunk_lse_exact(const void *logits, size_t rowbase, const uint8_t *mrow, int V, int c, double T,
-                                  double m, double *sh) {
-    double s = 0.0;
-    for (int e = c * kChunk + threadIdx.x; e < min(V, (c + 1) * kChunk); e += blockDim.x)
-        if ((mrow[e >> 3] >> (e & 7)) & 1u) s += exp(((double)load_logit<DT>(logits, rowbase + e) - m) / T);
-    s = block_sum_d(s, sh);
-    return m / T + log(s);
-}
-
-template <int DT>
-__global__ __launch_bounds__(256) void k_sample_b(const void *__restrict__ logits, int V, int64_t stride,
-                                                  const uint64_t *__restrict__ mask, int words_per_row,
-                                                  const float *__restrict__ temp, const uint64_t *__restrict__ seed,
-                                                  const int32_t *__restrict__ step,
-                                                  const Partial *__restrict__ part, int K,
-                                                  int32_t *__restrict__ out_id, float *__restrict__ out_lp) {
-    __shared__ double shv[4];
-    __shared__ int shi[4];
-    __shared__ int s_cont[8];
-    __shared__ int s_ncont;
-    const int r = blockIdx.x;
-    const float Tf = temp[r];
-    const bool greedy = !(Tf > 0.f);
-    const double T = greedy ? 1.0 : (double)Tf;
-    const Partial *pr = part + (size_t)r * K;
-    // (1) log-normaliser over the chunks, greedy candidate
-    double lse_max = -INFINITY;
-    double gv = -INFINITY;
-    int gi = -1;
-    for (int c = threadIdx.x; c < K; c += blockDim.x) {
-        const Partial p = pr[c];
-        if (p.idx >= 0) {
-            lse_max = fmax(lse_max, (double)p.m / T + log(p.s));
-            arg_better(gv, gi, (double)p.m, p.idx);
+    for (int g = 0; g < 4; g++) {
+        const int e0 = c * kChunk + g * 512 + lane * 8;
+        R.mb[g] = (e0 < V) ? mrow[e0 >> 3] : 0u;
+        if (VEC && e0 + 8 <= V) {
+            if (DT == 1) {
+                const uint4 v = *(const uint4 *)((const uint16_t *)logits + rowbase + e0);
+                R.d[g * 4 + 0] = v.x; R.d[g * 4 + 1] = v.y; R.d[g * 4 + 2] = v.z; R.d[g * 4 + 3] = v.w;
+            } else {
+                const uint4 v0 = *(const uint4 *)((const float *)logits + rowbase + e0);
+                const uint4 v1 = *(const uint4 *)((const float *)logits + rowbase + e0 + 4);
+                R.d[g * 8 + 0] = v0.x; R.d[g * 8 + 1] = v0.y; R.d[g * 8 + 2] = v0.z; R.d[g * 8 + 3] = v0.w;
+                R.d[g * 8 + 4] = v1.x; R.d[g * 8 + 5] = v1.y; R.d[g * 8 + 6] = v1.z; R.d[g * 8 + 7] = v1.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float x = (e0 + j < V) ? load_logit<DT>(logits, rowbase + e0 + j) : 0.f;
+                if (DT == 1) {
+                    const uint32_t u = __float_as_uint(x) >> 16;
+                    if (j & 1) R.d[g * 4 + j / 2] |= u << 16;
+                    else R.d[g * 4 + j / 2] = u;
+                } else {
+                    R.d[g * 8 + j] = __float_as_uint(x);
+                }
+            }
+            if (e0 + 8 > V) R.mb[g] &= (e0 >= V) ? 0u : ((1u << (V - e0)) - 1u);
         }
     }
-    lse_max = block_max_d(lse_max, shv);
-    block_argmax_d(gv, gi, shv, shi);
-    if (gi < 0) {  // nothing allowed (finished row)
+}
+
+// logit j of group g, or -inf where the mask bit is clear (a sign-extended
+// 1-bit field selects between the value and -inf)
+template <int DT>
+__device__ __forceinline__ float masked_x(const ChunkRegs<DT> &R, int g, int j) {
+    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)R.mb[g], j, 1);
+    uint32_t u;
+    if (DT == 1) u = (j & 1) ? (R.d[g * 4 + j / 2] & 0xFFFF0000u) : (R.d[g * 4 + j / 2] << 16);
+    else u = R.d[g * 8 + j];
+    return __uint_as_float((sel & u) | (~sel & 0xFF800000u));
+}
+
+// masked max m and sum over allowed ids of 2^((x - m) kk), kk = log2(e) / T'
+template <int DT>
+__device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, float kk, float &m_out, double &s_out,
+                                             bool &any_out) {
+    float xm[32];
+    float m = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            xm[g * 8 + j] = masked_x<DT>(R, g, j);
+            m = fmaxf(m, xm[g * 8 + j]);
+        }
+    any_out = __any(R.mb[0] | R.mb[1] | R.mb[2] | R.mb[3]);
+    m_out = -INFINITY;
+    s_out = 0.0;
+    if (!any_out) return;
+    m = wave_max_f(m);
+    m_out = m;
+    if (m == -INFINITY) return;  // every allowed logit is -inf
+    // 2^((x - m) kk): x - m is exact for the largest terms, so the dominant
+    // term is exactly 1 whatever the magnitude of m (masked terms are 2^-inf = 0)
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        float sg = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) sg += __builtin_amdgcn_exp2f((xm[g * 8 + j] - m) * kk);
+        s += sg;
+    }
+    s_out = wave_sum_d((double)s);
+}
+
+// ---- block-wide reductions (kWaves waves) --------------------------------
+constexpr int kWaves = 16;            // one workgroup of 1024 threads per row
+static_assert(kWaves == 16, "slot reductions read one slot per lane of a 16-lane row");
+
+// Each wave reduces in registers, lane 0 parks the result in slot[wave];
+// after one barrier every wave reads the 16 slots with lanes 0..15 and
+// reduces that row of lanes with DPP.  One barrier, no second pass.
+__device__ __forceinline__ double slots_max_d(const double *slot) {
+    double v = slot[threadIdx.x & 15];
+    v = fmax(v, dpp_d<kQuadSwap1>(v));
+    v = fmax(v, dpp_d<kQuadSwap2>(v));
+    v = fmax(v, dpp_d<kRowRor4>(v));
+    v = fmax(v, dpp_d<kRowRor8>(v));
+    return readlane_d(v, 0);
+}
+__device__ __forceinline__ double slots_sum_d(const double *slot) {
+    double v = slot[threadIdx.x & 15];
+    v += dpp_d<kQuadSwap1>(v);
+    v += dpp_d<kQuadSwap2>(v);
+    v += dpp_d<kRowRor4>(v);
+    v += dpp_d<kRowRor8>(v);
+    return readlane_d(v, 0);
+}
+__device__ __forceinline__ void slots_argmax(const double *sv, const int *si, double &v, int &i) {
+    v = sv[threadIdx.x & 15];
+    i = si[threadIdx.x & 15];
+    arg_step<kQuadSwap1>(v, i);
+    arg_step<kQuadSwap2>(v, i);
+    arg_step<kRowRor4>(v, i);
+    arg_step<kRowRor8>(v, i);
+    v = readlane_d(v, 0);
+    i = __builtin_amdgcn_readlane(i, 0);
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+    v = min(v, dpp_i<kQuadSwap1>(v));
+    v = min(v, dpp_i<kQuadSwap2>(v));
+    v = min(v, dpp_i<kRowRor4>(v));
+    v = min(v, dpp_i<kRowRor8>(v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+struct ChunkInfo {
+    double g;     // chunk noise G(1, c) (sampled rows)
+    double s;     // sum over allowed ids of 2^((x - m) kk)
+    float m;      // largest allowed logit
+    int any;      // the chunk has an allowed id
+};
+
+struct Decision {
+    double lmax, mv, lse_all, cs1, win;
+    float tv1;
+    int mc, chosen;
+    bool exact_chunk, exact_token;
+};
+
+struct Slots {
+    double a[kWaves], b[kWaves];
+    float f[kWaves], h[kWaves];
+    int i[kWaves], j[kWaves];
+    Decision dc;
+};
+
+// log-mass of chunk c recomputed entirely in double by the whole workgroup
+template <int DT>
+__device__ double chunk_lse_exact(const void *logits, size_t rowbase, const uint8_t *mrow, int V, int c, double T,
+                                  double m, double *slot) {
+    double s = 0.0;
+    for (int e = c * kChunk + (int)threadIdx.x; e < min(V, (c + 1) * kChunk); e += blockDim.x)
+        if ((mrow[e >> 3] >> (e & 7)) & 1u) s += exp(((double)load_logit<DT>(logits, rowbase + e) - m) / T);
+    s = wave_sum_d(s);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = s;
+    __syncthreads();
+    return m / T + log(slots_sum_d(slot));
+}
+
+// G(i) in float for screening, from v_log_f32 only: -ln u for u <= 1/2;
+// above, with v = 1 - u (exact from w): a 4-term series of -ln(1 - v) for
+// v < 2^-7, else -ln(1 - v) rounded from float (relative error < 4e-6).
+// Absolute error of the result < 1e-5.
+__device__ inline float gumbel32(uint32_t w) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    float t;
+    if (w < 0x80000000u) {
+        t = -kLn2 * __builtin_amdgcn_logf(((float)w + 0.5f) * 2.3283064365386963e-10f);
+    } else {
+        const float v = ((float)(0xFFFFFFFFu - w) + 0.5f) * 2.3283064365386963e-10f;
+        t = (v < 0.0078125f) ? v * (1.f + v * (0.5f + v * (0.33333334f + v * 0.25f)))
+                             : -kLn2 * __builtin_amdgcn_logf(1.f - v);
+    }
+    return -kLn2 * __builtin_amdgcn_logf(t);
+}
+
+// top two of (value, index) with the larger value first (lower index on ties)
+struct Top2 {
+    float v1, v2;
+    int i1;
+};
+__device__ __forceinline__ void top2_merge(Top2 &a, float bv1, int bi1, float bv2) {
+    const bool b_first = bi1 >= 0 && (a.i1 < 0 || bv1 > a.v1 || (bv1 == a.v1 && bi1 < a.i1));
+    if (b_first) {
+        a.v2 = fmaxf(a.v1, bv2);
+        a.v1 = bv1;
+        a.i1 = bi1;
+    } else {
+        a.v2 = fmaxf(a.v2, bv1);
+    }
+}
+template <int CTRL>
+__device__ __forceinline__ void top2_step(Top2 &a) {
+    const float v1 = __int_as_float(dpp_i<CTRL>(__float_as_int(a.v1)));
+    const float v2 = __int_as_float(dpp_i<CTRL>(__float_as_int(a.v2)));
+    const int i1 = dpp_i<CTRL>(a.i1);
+    top2_merge(a, v1, i1, v2);
+}
+// wave-wide top-2 (every lane of each 16-lane row holds the row's; the
+// caller combines rows)
+__device__ __forceinline__ void top2_rows(Top2 &a) {
+    top2_step<kQuadSwap1>(a);
+    top2_step<kQuadSwap2>(a);
+    top2_step<kRowRor4>(a);
+    top2_step<kRowRor8>(a);
+}
+__device__ __forceinline__ Top2 top2_wave(Top2 a) {
+    top2_rows(a);
+    Top2 r;
+    r.v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v1), 0));
+    r.v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v2), 0));
+    r.i1 = __builtin_amdgcn_readlane(a.i1, 0);
+    for (int l = 16; l < 64; l += 16)
+        top2_merge(r, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v1), l)),
+                   __builtin_amdgcn_readlane(a.i1, l),
+                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v2), l)));
+    return r;
+}
+// the same for chunk scores, in double (they can be large for heavy-tailed logits)
+struct Top2d {
+    double v1, v2;
+    int i1;
+};
+__device__ __forceinline__ void top2d_merge(Top2d &a, double bv1, int bi1, double bv2) {
+    const bool b_first = bi1 >= 0 && (a.i1 < 0 || bv1 > a.v1 || (bv1 == a.v1 && bi1 < a.i1));
+    if (b_first) {
+        a.v2 = fmax(a.v1, bv2);
+        a.v1 = bv1;
+        a.i1 = bi1;
+    } else {
+        a.v2 = fmax(a.v2, bv1);
+    }
+}
+template <int CTRL>
+__device__ __forceinline__ void top2d_step(Top2d &a) {
+    const double v1 = dpp_d<CTRL>(a.v1), v2 = dpp_d<CTRL>(a.v2);
+    const int i1 = dpp_i<CTRL>(a.i1);
+    top2d_merge(a, v1, i1, v2);
+}
+__device__ __forceinline__ void top2d_rows(Top2d &a) {
+    top2d_step<kQuadSwap1>(a);
+    top2d_step<kQuadSwap2>(a);
+    top2d_step<kRowRor4>(a);
+    top2d_step<kRowRor8>(a);
+}
+__device__ __forceinline__ Top2d top2d_wave(Top2d a) {
+    top2d_rows(a);
+    Top2d r{readlane_d(a.v1, 0), readlane_d(a.v2, 0), __builtin_amdgcn_readlane(a.i1, 0)};
+    for (int l = 16; l < 64; l += 16)
+        top2d_merge(r, readlane_d(a.v1, l), __builtin_amdgcn_readlane(a.i1, l), readlane_d(a.v2, l));
+    return r;
+}
+__device__ __forceinline__ Top2d top2d_slots(const double *v1, const int *i1, const double *v2) {
+    const int k = threadIdx.x & 15;
+    Top2d a{v1[k], v2[k], i1[k]};
+    top2d_rows(a);
+    return Top2d{readlane_d(a.v1, 0), readlane_d(a.v2, 0), __builtin_amdgcn_readlane(a.i1, 0)};
+}
+
+// block-wide: slots of 16 waves, each wave reduces them with a 16-lane row
+__device__ __forceinline__ Top2 top2_slots(const float *v1, const int *i1, const float *v2) {
+    Top2 a;
+    const int k = threadIdx.x & 15;
+    a.v1 = v1[k];
+    a.i1 = i1[k];
+    a.v2 = v2[k];
+    top2_rows(a);
+    Top2 r;
+    r.v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v1), 0));
+    r.v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v2), 0));
+    r.i1 = __builtin_amdgcn_readlane(a.i1, 0);
+    return r;
+}
+
+// One workgroup per row.  Its 16 waves stream the row's 2048-id chunks
+// (wave w takes chunks w, w + 16, ...; the next chunk's loads are issued
+// before the current one is reduced) and leave one summary per chunk in LDS;
+// then the whole workgroup forms the log-normaliser and picks the token.
+// No state crosses workgroups, so no device-wide fence is ever needed.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
+                                                 const uint64_t *__restrict__ mask, int words_per_row,
+                                                 const float *__restrict__ temp, const uint64_t *__restrict__ seed,
+                                                 const int32_t *__restrict__ step, int K,
+                                                 int32_t *__restrict__ out_id, float *__restrict__ out_lp) {
+    extern __shared__ ChunkInfo ci[];
+    __shared__ Slots sl[4];
+    __shared__ float xstash[kChunk];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = blockIdx.x;
+    const float Tf = temp[r];
+    const uint64_t sd = seed[r];
+    const uint32_t stp = (uint32_t)step[r];
+    const bool greedy = !(Tf > 0.f);
+    const double T = greedy ? 1.0 : (double)Tf;
+    const float kk = greedy ? kLog2e : kLog2e / Tf;
+    const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
+    const uint8_t *mrow = (const uint8_t *)(mask + (size_t)r * words_per_row);
+    const size_t rowbase = (size_t)r * (size_t)stride;
+    {
+        ChunkRegs<DT> cur, nxt;
+        int c = wave;
+        if (c < K) load_chunk<DT, VEC>(cur, logits, rowbase, mrow, V, c, lane);
+        // chunk noise G(1, c) for this wave's chunks, while the loads fly
+        const int cg = wave + kWaves * lane;
+        if (!greedy && cg < K) {
+            const uint4 o = philox4x32_10(make_uint4((uint32_t)cg >> 2, stp, 1u, 0u), k0, k1);
+            ci[cg].g = gumbel64(pick_word(o, cg & 3));
+        }
+        for (; c < K; c += kWaves) {
+            if (c + kWaves < K) load_chunk<DT, VEC>(nxt, logits, rowbase, mrow, V, c + kWaves, lane);
+            float m;
+            double s;
+            bool any;
+            reduce_chunk<DT>(cur, kk, m, s, any);
+            if (lane == 0) {
+                ci[c].m = m;
+                ci[c].s = s;
+                ci[c].any = any ? 1 : 0;
+            }
+            cur = nxt;
+        }
+    }
+    __syncthreads();
+    // ---- the row's decision: wave 0 reduces the chunk summaries ----------
+    // (1) log-mass L_c = m/T + ln s per chunk (ln from v_log_f32: the chunk
+    // sums carry ~1e-6 of float rounding anyway), the largest logit (lowest
+    // chunk) and the two best chunk scores L_c + G(1, c); (2) the
+    // log-normaliser.  Published in LDS for the other waves.
+    constexpr double kLn2d = 0.6931471805599453;
+    const double invT = 1.0 / T;
+    Decision &dc = sl[0].dc;
+    if (wave == 0) {
+        double lc = -INFINITY, mv = -INFINITY;
+        int mc = -1;
+        Top2d cs{-INFINITY, -INFINITY, -1};
+        for (int c = lane; c < K; c += 64) {
+            const ChunkInfo x = ci[c];
+            if (!x.any) continue;
+            const double l = (x.s > 0.0) ? (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s)
+                                         : -INFINITY;
+            lc = fmax(lc, l);
+            arg_better(mv, mc, (double)x.m, c);
+            if (!greedy && l > -INFINITY) top2d_merge(cs, l + x.g, c, -INFINITY);
+        }
+        lc = wave_max_d(lc);
+        wave_argmax(mv, mc);
+        if (!greedy) cs = top2d_wave(cs);
+        if (lane == 0) {
+            dc.lmax = lc;
+            dc.mv = mv;
+            dc.mc = mc;
+            dc.chosen = greedy ? mc : cs.i1;
+            dc.exact_chunk = !greedy && cs.i1 >= 0 && !(cs.v1 - cs.v2 > kContendChunk);
+            dc.cs1 = cs.v1;
+        }
+    }
+    __syncthreads();
+    if (dc.mc < 0) {  // nothing allowed: a finished row
         if (threadIdx.x == 0) {
             out_id[r] = -1;
             out_lp[r] = 0.f;
         }
         return;
     }
-    double acc = 0.0;
-    for (int c = threadIdx.x; c < K; c += blockDim.x) {
-        const Partial p = pr[c];
-        if (p.idx >= 0) acc += exp((double)p.m / T + log(p.s) - lse_max);
+    if (dc.exact_chunk) {
+        // two chunks within the screening window: decide on exact log-masses (rare)
+        double bb = -INFINITY;
+        int bbc = -1;
+        for (int c = 0; c < K; c++) {
+            const ChunkInfo x = ci[c];
+            if (!x.any || !(x.s > 0.0)) continue;
+            const double l = (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s);
+            if (l + x.g < dc.cs1 - 2 * kContendChunk) continue;
+            arg_better(bb, bbc, chunk_lse_exact<DT>(logits, rowbase, mrow, V, c, T, (double)x.m, sl[1].a) + x.g, c);
+        }
+        if (threadIdx.x == 0) dc.chosen = bbc;
+        __syncthreads();
     }
-    const double lse_all = lse_max + log(block_sum_d(acc, shv));
-    if (greedy) {
+    const int chosen = dc.chosen;
+    if (chosen < 0) {  // every allowed logit is -inf: no distribution to draw from
         if (threadIdx.x == 0) {
-            out_id[r] = gi;
-            out_lp[r] = (float)(gv - lse_all);
+            out_id[r] = -1;
+            out_lp[r] = 0.f;
         }
         return;
     }
-    const uint64_t sd = seed[r];
-    const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
-    const uint32_t stp = (uint32_t)step[r];
-    const size_t rowbase = (size_t)r * (size_t)stride;
-    const uint8_t *mrow = (const uint8_t *)(mask + (size_t)r * words_per_row);
-    // (2) chunk choice: L_c + G(1, c)
-    double best = -INFINITY;
-    int bc = -1;
-    for (int c = threadIdx.x; c < K; c += blockDim.x) {
-        const Partial p = pr[c];
-        if (p.idx < 0) continue;
-        const uint4 o = philox4x32_10(make_uint4((uint32_t)c >> 2, stp, 1u, 0u), k0, k1);
-        arg_better(best, bc, (double)p.m / T + log(p.s) + gumbel(pick_word(o, c & 3)), c);
-    }
-    block_argmax_d(best, bc, shv, shi);
-    // screened scores carry ~1e-6 of rounding: recompute close contenders exactly
-    if (threadIdx.x == 0) s_ncont = 0;
-    __syncthreads();
-    for (int c = threadIdx.x; c < K; c += blockDim.x) {
-        const Partial p = pr[c];
-        if (p.idx < 0) continue;
-        const uint4 o = philox4x32_10(make_uint4((uint32_t)c >> 2, stp, 1u, 0u), k0, k1);
-        const double sc = (double)p.m / T + log(p.s) + gumbel(pick_word(o, c & 3));
-        if (sc >= best - kContend) {
-            const int slot = atomicAdd(&s_ncont, 1);
-            if (slot < 8) s_cont[slot] = c;
+    // (3) inside the chunk, waves 0-3, 8 ids per lane: the logits and the
+    // token noise start while wave 0 forms the normaliser
+    const bool tok_wave = wave < 4;
+    const int e = chosen * kChunk + wave * 512 + lane * 8;
+    uint32_t mb = 0;
+    float xv[8];
+    uint4 o0 = make_uint4(0, 0, 0, 0), o1 = make_uint4(0, 0, 0, 0);
+    if (tok_wave) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) xv[j] = (e + j < V) ? load_logit<DT>(logits, rowbase + e + j) : 0.f;
+        mb = (e < V) ? mrow[e >> 3] : 0u;
+        if (e + 8 > V) mb &= (e >= V) ? 0u : ((1u << (V - e)) - 1u);
+        if (!greedy && mb) {
+            o0 = philox4x32_10(make_uint4((uint32_t)e >> 2, stp, 0u, 0u), k0, k1);
+            o1 = philox4x32_10(make_uint4(((uint32_t)e >> 2) + 1u, stp, 0u, 0u), k0, k1);
         }
     }
-    __syncthreads();
-    const int ncont = min(s_ncont, 8);
-    if (ncont > 1) {
-        double bb = -INFINITY;
-        int bbc = -1;
-        for (int t = 0; t < ncont; t++) {
-            const int c = s_cont[t];
-            const Partial p = pr[c];
-            const double l = chunk_lse_exact<DT>(logits, rowbase, mrow, V, c, T, (double)p.m, shv);
-            const uint4 o = philox4x32_10(make_uint4((uint32_t)c >> 2, stp, 1u, 0u), k0, k1);
-            arg_better(bb, bbc, l + gumbel(pick_word(o, c & 3)), c);
+    if (wave == 0) {
+        float acc = 0.f;
+        for (int c = lane; c < K; c += 64) {
+            const ChunkInfo x = ci[c];
+            if (!x.any || !(x.s > 0.0)) continue;
+            const double l = (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s);
+            acc += __builtin_amdgcn_exp2f((float)((l - dc.lmax) * 1.4426950408889634));
         }
-        bc = bbc;
+        const double sum = wave_sum_d((double)acc);
+        if (lane == 0) dc.lse_all = dc.lmax + kLn2d * (double)__builtin_amdgcn_logf((float)sum);
     }
-    // (3) token choice inside chunk bc: x_i / T + G(0, i)
-    double tv = -INFINITY;
-    int ti = -1;
-    {
-        const int e0 = bc * kChunk + threadIdx.x * 8;
-        if (e0 < V) {
-            const uint32_t mbits = mrow[e0 >> 3];
-            if (mbits) {
-                const uint4 o0 = philox4x32_10(make_uint4((uint32_t)e0 >> 2, stp, 0u, 0u), k0, k1);
-                const uint4 o1 = philox4x32_10(make_uint4(((uint32_t)e0 >> 2) + 1u, stp, 0u, 0u), k0, k1);
-                for (int j = 0; j < 8 && e0 + j < V; j++) {
-                    if (!((mbits >> j) & 1u)) continue;
-                    const uint32_t wv = pick_word(j < 4 ? o0 : o1, j & 3);
-                    const double sc = (double)load_logit<DT>(logits, rowbase + e0 + j) / T + gumbel(wv);
-                    arg_better(tv, ti, sc, e0 + j);
-                }
+    if (greedy) {
+        // the lowest id of the chunk holding the largest logit
+        int im = 0x7FFFFFFF;
+        if (tok_wave)
+            for (int j = 7; j >= 0; j--)
+                if (((mb >> j) & 1u) && (double)xv[j] == dc.mv) im = e + j;
+        if (tok_wave) {
+            im = wave_min_i(im);
+            if (lane == 0) sl[2].i[wave] = im;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int best = min(min(sl[2].i[0], sl[2].i[1]), min(sl[2].i[2], sl[2].i[3]));
+            out_id[r] = best;
+            out_lp[r] = (float)(dc.mv - dc.lse_all);
+        }
+        return;
+    }
+    // sampled: argmax_i x_i / T + G(0, i) screened in float; the winner is
+    // exact unless the best two are within the screening error (x/T rounding
+    // < 1e-6 |x/T|, G < 1e-5), in which case the contenders are recomputed
+    Top2 ts{-INFINITY, -INFINITY, -1};
+    if (tok_wave) {
+        const float it = 1.0f / Tf;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if ((mb >> j) & 1u) top2_merge(ts, xv[j] * it + gumbel32(pick_word(j < 4 ? o0 : o1, j & 3)), e + j, -INFINITY);
+        ts = top2_wave(ts);
+        if (lane == 0) {
+            sl[2].f[wave] = ts.v1;
+            sl[2].h[wave] = ts.v2;
+            sl[2].i[wave] = ts.i1;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) xstash[wave * 512 + lane * 8 + j] = xv[j];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        Top2 t{-INFINITY, -INFINITY, -1};
+        for (int k = 0; k < 4; k++) top2_merge(t, sl[2].f[k], sl[2].i[k], sl[2].h[k]);
+        const double win = 1e-4 + 2e-6 * fabs((double)t.v1);
+        const bool unique = (double)t.v1 - (double)t.v2 > win;
+        if (lane == 0) {
+            dc.exact_token = !unique;
+            dc.win = win;
+            dc.tv1 = t.v1;
+            if (unique) {
+                out_id[r] = t.i1;
+                out_lp[r] = (float)((double)xstash[t.i1 - chosen * kChunk] / T - dc.lse_all);
             }
         }
     }
-    block_argmax_d(tv, ti, shv, shi);
+    __syncthreads();
+    if (!dc.exact_token) return;
+    // contenders recomputed in double (rare)
+    double tv = -INFINITY;
+    int ti = -1;
+    if (tok_wave) {
+        const float it = 1.0f / Tf;
+        for (int j = 0; j < 8; j++) {
+            if (!((mb >> j) & 1u)) continue;
+            const uint32_t w = pick_word(j < 4 ? o0 : o1, j & 3);
+            if ((double)(xv[j] * it + gumbel32(w)) >= (double)dc.tv1 - dc.win)
+                arg_better(tv, ti, (double)xv[j] / T + gumbel64(w), e + j);
+        }
+        wave_argmax(tv, ti);
+        if (lane == 0) {
+            sl[3].b[wave] = tv;
+            sl[3].j[wave] = ti;
+        }
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        out_id[r] = ti;
-        out_lp[r] = (ti >= 0) ? (float)((double)load_logit<DT>(logits, rowbase + ti) / T - lse_all) : 0.f;
+        double v = sl[3].b[0];
+        int i = sl[3].j[0];
+        for (int k = 1; k < 4; k++) arg_better(v, i, sl[3].b[k], sl[3].j[k]);
+        out_id[r] = i;
+        out_lp[r] = (float)((double)xstash[i - chosen * kChunk] / T - dc.lse_all);
     }
 }
 
@@ -486,35 +816,31 @@ int launch_init(const cg_grammar *g, cg_state *states, int B, hipStream_t st) {
 int launch_advance(const cg_grammar *g, cg_state *states, int B, const int32_t *ids, int32_t *steps,
                    int32_t *status, hipStream_t st) {
     if (B == 0) return CG_OK;
-    hipLaunchKernelGGL(k_advance, dim3((B + 127) / 128), dim3(128), 0, st, g->dev.comb, g->k, g->dev.blob,
-                       g->dev.offsets, g->V, states, B, ids, steps, status, g->gen_cap);
+    const size_t lds = (size_t)g->comb_len * sizeof(uint64_t);
+    hipLaunchKernelGGL(k_advance, dim3((B + 255) / 256), dim3(256), lds, st, g->dev.comb, g->comb_len, g->k,
+                       g->dev.tokw, g->dev.tokinfo, g->nw, g->V, states, B, ids, steps, status, g->gen_cap);
     return launch_status("advance");
 }
 
 template <int NW>
 static int launch_fill_nw(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr,
                           hipStream_t st) {
-    const size_t lds = (size_t)g->comb_len * sizeof(uint64_t);
-    static int configured_bytes = 0;
-    if ((int)lds > configured_bytes) {
-        if (hipFuncSetAttribute((const void *)k_fill<NW>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-            hipSuccess) {
-            set_error("fill_bitmask: table of %zu bytes does not fit in LDS", lds);
-            return CG_E_LIMIT;
-        }
-        configured_bytes = (int)lds;
+    const size_t lds = (size_t)g->comb_len * sizeof(uint64_t) + kMaxRowsPerItem * sizeof(cg_state);
+    if (lds > 64 * 1024) {
+        set_error("fill_bitmask: table of %zu bytes does not fit in LDS", lds);
+        return CG_E_LIMIT;
     }
-    const int ncu = g->n_cu;
-    const int per_cu = std::max(1, std::min(4, (int)((160 * 1024) / std::max<size_t>(lds, 1))));
+    const int per_cu = std::max(1, std::min(8, (int)((160 * 1024) / lds)));
     const int n_tok_blocks = (g->V + 255) / 256;
-    const int grid_cap = ncu * per_cu;
-    long long want = (long long)B * n_tok_blocks;
-    int rows_per_item = (int)std::max<long long>(1, std::min<long long>(B, (want + 2LL * grid_cap - 1) / (2LL * grid_cap)));
-    const int n_rg = (B + rows_per_item - 1) / rows_per_item;
+    const int grid_cap = g->n_cu * per_cu;
+    // about four items per workgroup, at most kMaxRowsPerItem rows per item
+    long long want_rg = (4LL * grid_cap + n_tok_blocks - 1) / n_tok_blocks;
+    int n_rg = (int)std::min<long long>(B, std::max<long long>(want_rg, (B + kMaxRowsPerItem - 1) / kMaxRowsPerItem));
+    n_rg = std::max(1, n_rg);
     const int n_items = n_rg * n_tok_blocks;
     const int grid = std::max(1, std::min(n_items, grid_cap));
     hipLaunchKernelGGL(k_fill<NW>, dim3(grid), dim3(256), lds, st, g->dev.comb, g->comb_len, g->dev.tokw,
-                       g->dev.toklen, g->V, states, B, mask, wpr, g->k, n_tok_blocks, rows_per_item, n_items);
+                       g->dev.tokinfo, g->V, states, B, mask, wpr, g->k, n_tok_blocks, n_rg, n_items);
     return launch_status("fill_bitmask");
 }
 
@@ -533,30 +859,35 @@ int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *ma
 }
 
 size_t sample_workspace_bytes(int B, int V) {
-    const size_t K = (size_t)(V + kChunk - 1) / kChunk;
-    return (size_t)B * K * sizeof(Partial);
+    (void)B;
+    (void)V;
+    return 0;  // partials live in LDS
 }
 
 int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, const uint64_t *mask, int wpr,
                   const float *temp, const uint64_t *seed, const int32_t *step, void *ws, int32_t *out_id,
                   float *out_lp, hipStream_t st) {
+    (void)ws;
     if (B == 0) return CG_OK;
     const int K = (V + kChunk - 1) / kChunk;
+    const size_t lds = (size_t)K * sizeof(ChunkInfo);
+    if (lds > 48 * 1024) {
+        set_error("apply_mask_sample: vocab above %d", 48 * 1024 / (int)sizeof(ChunkInfo) * kChunk);
+        return CG_E_ARG;
+    }
     const int es = dt == 0 ? 4 : 2;
     const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * es) % 16 == 0);
-    Partial *part = (Partial *)ws;
-    dim3 ga((K + 3) / 4, B);
+#define CG_LAUNCH_SAMPLE(D, VV)                                                                                   \
+    hipLaunchKernelGGL((k_sample<D, VV>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask, wpr, temp, \
+                       seed, step, K, out_id, out_lp)
     if (dt == 0) {
-        if (vec) hipLaunchKernelGGL((k_sample_a<0, true>), ga, dim3(256), 0, st, logits, V, stride, mask, wpr, temp, part, K);
-        else hipLaunchKernelGGL((k_sample_a<0, false>), ga, dim3(256), 0, st, logits, V, stride, mask, wpr, temp, part, K);
-        hipLaunchKernelGGL(k_sample_b<0>, dim3(B), dim3(256), 0, st, logits, V, stride, mask, wpr, temp, seed, step,
-                           part, K, out_id, out_lp);
+        if (vec) CG_LAUNCH_SAMPLE(0, true);
+        else CG_LAUNCH_SAMPLE(0, false);
     } else {
-        if (vec) hipLaunchKernelGGL((k_sample_a<1, true>), ga, dim3(256), 0, st, logits, V, stride, mask, wpr, temp, part, K);
-        else hipLaunchKernelGGL((k_sample_a<1, false>), ga, dim3(256), 0, st, logits, V, stride, mask, wpr, temp, part, K);
-        hipLaunchKernelGGL(k_sample_b<1>, dim3(B), dim3(256), 0, st, logits, V, stride, mask, wpr, temp, seed, step,
-                           part, K, out_id, out_lp);
+        if (vec) CG_LAUNCH_SAMPLE(1, true);
+        else CG_LAUNCH_SAMPLE(1, false);
     }
+#undef CG_LAUNCH_SAMPLE
     return launch_status("apply_mask_sample");
 }
 

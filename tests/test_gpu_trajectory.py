@@ -57,7 +57,8 @@ def _run(cfg, B, steps, V=None, T=None, check_rows=None, gen_cap=W.GEN_CAP):
             if i < 0:
                 assert ids_dev[r] == -1, (s, r)
                 continue
-            if min(info["margin_chunk"], info["margin_token"]) < 1e-6:
+            if T > 0 and min(info["margin_chunk"], info["margin_token"]) < 1e-6:
+                # sampled near-tie: both sides adopt the device's pick
                 ties += 1
                 assert bits[ids_dev[r]]
             else:
