@@ -113,6 +113,7 @@ def main():
     temp = torch.full((B,), T, dtype=torch.float32, device=dev)
     seed = torch.from_numpy(np.array(W.row_seeds(CONFIG, B), dtype=np.uint64).view(np.int64)).to(dev)
     ws = cg.new_workspace(B, V, dev)
+    fws = g.new_fill_workspace(B, dev)
     ids_hist = torch.full((total, B), -1, dtype=torch.int32, device=dev)
     lp = torch.empty(B, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -121,7 +122,7 @@ def main():
         ids = ids_hist[s]
         if ev is not None:
             ev[0].record(stream)
-        g.fill_bitmask(st, mask, stream)
+        g.fill_bitmask(st, mask, fws, stream)
         if ev is not None:
             ev[1].record(stream)
         cg.apply_mask_sample(pool[s % npool], mask, temp, seed, steps, ws, ids, lp, stream=stream)

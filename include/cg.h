@@ -146,6 +146,10 @@ int cg_grammar_info(const cg_grammar *g, cg_info *info);
 /* Set d_states[0..batch) to the start of the grammar (flags cleared). */
 int cg_init_state(const cg_grammar *g, cg_state *d_states, int32_t batch, void *stream);
 
+/* Bytes of the workspace cg_fill_bitmask needs for `batch` rows of this
+ * grammar (0 if batch < 1; 0 on a bad handle). */
+size_t cg_fill_workspace_bytes(const cg_grammar *g, int32_t batch);
+
 /*
  * Packed token bitmask: bit (t & 63) of d_mask[r * words_per_row + (t >> 6)]
  * is 1 iff row r is not finished and the bytes of token t are a legal
@@ -155,9 +159,13 @@ int cg_init_state(const cg_grammar *g, cg_state *d_states, int32_t batch, void *
  * left untouched.  Depends only on the states, so it may run before the
  * logits exist ("Evaluator aware decoding", "Why isn't this in production
  * APIs yet?": masks come from pure automaton state ahead of the step).
+ * d_workspace: cg_fill_workspace_bytes(g, batch) bytes of device memory,
+ *   16-byte aligned, owned by the caller (the per-row list of token tiles
+ *   to walk); its contents need no initialisation and are scratch after the
+ *   call.  Calls that share a workspace must not overlap.
  */
 int cg_fill_bitmask(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
-                    int32_t words_per_row, void *stream);
+                    int32_t words_per_row, void *d_workspace, void *stream);
 
 /* Bytes of the workspace cg_apply_mask_sample needs for (batch, vocab) (0 if batch or vocab < 1). */
 size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab);

@@ -20,7 +20,8 @@ STATE_BYTES = 24
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # Symbols the C ABI (include/cg.h) exports.
-EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask",
+EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
+           "cg_fill_bitmask",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
 
 
@@ -58,7 +59,9 @@ def lib():
         L.cg_free_grammar.restype = None
         L.cg_grammar_info.argtypes = [vp, ctypes.POINTER(Info)]
         L.cg_init_state.argtypes = [vp, vp, i32, vp]
-        L.cg_fill_bitmask.argtypes = [vp, vp, i32, vp, i32, vp]
+        L.cg_fill_workspace_bytes.argtypes = [vp, i32]
+        L.cg_fill_workspace_bytes.restype = sz
+        L.cg_fill_bitmask.argtypes = [vp, vp, i32, vp, i32, vp, vp]
         L.cg_sample_workspace_bytes.argtypes = [i32, i32]
         L.cg_sample_workspace_bytes.restype = sz
         L.cg_apply_mask_sample.argtypes = [vp, i32, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -149,13 +152,27 @@ class Grammar:
         _dev(states, torch.uint8, "states", 2)
         _check(lib().cg_init_state(self._h, _ptr(states), states.shape[0], _stream(stream)))
 
-    def fill_bitmask(self, states, mask, stream=None):
+    def fill_workspace_bytes(self, B: int) -> int:
+        return int(lib().cg_fill_workspace_bytes(self._h, B))
+
+    def new_fill_workspace(self, B: int, device="cuda"):
+        """Device buffer for fill_bitmask over B rows (no initialisation needed)."""
+        import torch
+        return torch.empty(max(2, (self.fill_workspace_bytes(B) + 15) // 16 * 2), dtype=torch.int64, device=device)
+
+    def fill_bitmask(self, states, mask, workspace=None, stream=None):
+        """workspace: from new_fill_workspace(B); None allocates one for this call."""
         import torch
         _dev(states, torch.uint8, "states", 2)
         _dev(mask, torch.int64, "mask", 2)
         if mask.shape[0] < states.shape[0]:
             raise ValueError("mask has fewer rows than states")
-        _check(lib().cg_fill_bitmask(self._h, _ptr(states), states.shape[0], _ptr(mask), mask.shape[1],
+        B = states.shape[0]
+        if workspace is None:
+            workspace = self.new_fill_workspace(B, states.device)
+        if workspace.numel() * workspace.element_size() < self.fill_workspace_bytes(B):
+            raise ValueError("fill workspace too small")
+        _check(lib().cg_fill_bitmask(self._h, _ptr(states), B, _ptr(mask), mask.shape[1], _ptr(workspace),
                                      _stream(stream)))
 
     def advance(self, states, ids, steps, status, stream=None):

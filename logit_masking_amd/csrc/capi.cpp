@@ -12,8 +12,11 @@ const char *last_error();
 int launch_init(const cg_grammar *g, cg_state *states, int B, hipStream_t st);
 int launch_advance(const cg_grammar *g, cg_state *states, int B, const int32_t *ids, int32_t *steps,
                    int32_t *status, hipStream_t st);
-int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, hipStream_t st);
+int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws,
+                hipStream_t st);
+int fill_plan_stride(const cg_grammar *g);
 size_t sample_workspace_bytes(int B, int V);
+size_t fill_lds_bytes(const cg_grammar *g, int items_per_row);
 int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, const uint64_t *mask, int wpr,
                   const float *temp, const uint64_t *seed, const int32_t *step, void *ws, int32_t *out_id,
                   float *out_lp, hipStream_t st);
@@ -44,6 +47,16 @@ void release(cg_grammar *g) {
         (void)hipFree(g->dev.comb);
         (void)hipFree(g->dev.tokw);
         (void)hipFree(g->dev.tokinfo);
+        (void)hipFree(g->dev.legal);
+        (void)hipFree(g->dev.lex_idlen);
+        (void)hipFree(g->dev.lex_jump);
+        (void)hipFree(g->dev.lex_w);
+        (void)hipFree(g->dev.lex_tile);
+        (void)hipFree(g->dev.q_idlen);
+        (void)hipFree(g->dev.q_posch);
+        (void)hipFree(g->dev.q_w);
+        (void)hipFree(g->dev.q_tile);
+        (void)hipFree(g->dev.strbits);
         (void)hipSetDevice(cur);
     }
     free(g->host_comb);
@@ -66,6 +79,94 @@ uint32_t string_summary(const cg_grammar *g, const uint8_t *s, uint32_t n) {
         q = lo >> 16;
     }
     return (STR_IN << 8) | (chars << 10);
+}
+
+// Candidate tables of the fill kernel (see DeviceTables).  In lexicographic
+// order, tokens sharing their first bytes sit in the same 64-token tiles: a
+// row then visits only tiles holding a key it can accept.
+struct FillHost {
+    std::vector<uint64_t> legal, strbits;
+    std::vector<uint32_t> lex_idlen, lex_jump, lex_w, q_idlen, q_posch, q_w;
+    std::vector<uint2> lex_tile, q_tile;
+};
+
+void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint32_t *tok_offsets,
+                       const std::vector<uint32_t> &tokinfo, FillHost &f) {
+    constexpr uint32_t kPad = 0xFFFFFFFFu;
+    const uint32_t V = (uint32_t)g->V, nw = (uint32_t)g->nw, Wv = (V + 63) / 64;
+    auto bytes = [&](uint32_t t) { return tok_bytes + tok_offsets[t]; };
+    auto len = [&](uint32_t t) { return tok_offsets[t + 1] - tok_offsets[t]; };
+    auto less_from = [&](uint32_t a, uint32_t oa, uint32_t b, uint32_t ob) {
+        const uint32_t na = len(a) - oa, nb = len(b) - ob;
+        const int c = memcmp(bytes(a) + oa, bytes(b) + ob, std::min(na, nb));
+        if (c != 0) return c < 0;
+        if (na != nb) return na < nb;
+        return a < b;
+    };
+    // bytes with a transition out of each state
+    f.legal.assign((size_t)g->k.q_limit * 4, 0ull);
+    for (uint32_t q = 0; q < g->k.q_limit; q++)
+        for (uint32_t b = 0; b < 256; b++)
+            if ((g->host_comb[q + b] & 0xFFFFu) == q) f.legal[(size_t)q * 4 + (b >> 6)] |= 1ull << (b & 63);
+    auto pad = [&](std::vector<uint32_t> &order) { order.resize((order.size() + kTile - 1) / kTile * kTile, kPad); };
+    auto pack = [&](const std::vector<uint32_t> &order, std::vector<uint32_t> &idlen, std::vector<uint32_t> &w) {
+        const size_t n = order.size();
+        idlen.assign(std::max<size_t>(n, 1), 0u);
+        w.assign(std::max<size_t>(nw * n, 1), 0u);
+        for (size_t i = 0; i < n; i++) {
+            const uint32_t t = order[i];
+            if (t == kPad) continue;
+            idlen[i] = t | len(t) << 24;
+            for (uint32_t j = 0; j < len(t); j++) w[(j >> 2) * n + i] |= (uint32_t)bytes(t)[j] << (8 * (j & 3));
+        }
+    };
+    // key span of each tile over its real tokens (keys never decrease along a list)
+    auto spans = [&](const std::vector<uint32_t> &order, auto key, std::vector<uint2> &tile) {
+        tile.clear();
+        for (size_t i = 0; i < order.size(); i += kTile) {
+            size_t j = i + kTile - 1;
+            while (order[j] == kPad) j--;
+            tile.push_back(make_uint2(key(order[i]), key(order[j])));
+        }
+        if (tile.empty()) tile.push_back(make_uint2(1, 0));  // placeholder, never read
+    };
+    std::vector<uint32_t> lex, q;
+    for (uint32_t t = 0; t < V; t++) {
+        if (len(t) == 0) continue;
+        lex.push_back(t);
+        if (tok_kind(tokinfo[t]) == STR_QUOTE) q.push_back(t);
+    }
+    auto qoff = [&](uint32_t t) { return tok_pos(tokinfo[t]) + 1; };
+    std::sort(lex.begin(), lex.end(), [&](uint32_t a, uint32_t b) { return less_from(a, 0, b, 0); });
+    std::sort(q.begin(), q.end(), [&](uint32_t a, uint32_t b) { return less_from(a, qoff(a), b, qoff(b)); });
+    pad(lex);
+    pad(q);
+    pack(lex, f.lex_idlen, f.lex_w);
+    pack(q, f.q_idlen, f.q_w);
+    spans(lex, [&](uint32_t t) { return lead_key(bytes(t)[0], len(t) > 1 ? bytes(t)[1] : 0u, len(t)); }, f.lex_tile);
+    spans(q, [&](uint32_t t) { return qoff(t) == len(t) ? 0u : bytes(t)[qoff(t)] + 1u; }, f.q_tile);
+    // the jump: where the token's first quote is, and how the bytes after it
+    // read as string content
+    f.lex_jump.assign(std::max<size_t>(lex.size(), 1), kNoQuote);
+    for (size_t i = 0; i < lex.size(); i++) {
+        const uint32_t t = lex[i];
+        if (t == kPad || g->k.s_body >= g->k.q_limit) continue;
+        const uint8_t *b = bytes(t);
+        const uint8_t *qp = (const uint8_t *)memchr(b, '"', len(t));
+        if (!qp) continue;
+        const uint32_t at = (uint32_t)(qp - b);
+        f.lex_jump[i] = at | string_summary(g, b + at + 1, len(t) - at - 1);
+    }
+    f.q_posch.assign(std::max<size_t>(q.size(), 1), 0u);
+    for (size_t i = 0; i < q.size(); i++)
+        if (q[i] != kPad) f.q_posch[i] = tok_pos(tokinfo[q[i]]) | tok_chars(tokinfo[q[i]]) << 8;
+    // tokens that end inside the string, per budget
+    f.strbits.assign((size_t)kStrBitsets * Wv, 0ull);
+    for (uint32_t t = 0; t < V; t++) {
+        if (len(t) == 0 || tok_kind(tokinfo[t]) != STR_IN) continue;
+        for (uint32_t c = tok_chars(tokinfo[t]); c < (uint32_t)kStrBitsets; c++)
+            f.strbits[(size_t)c * Wv + (t >> 6)] |= 1ull << (t & 63);
+    }
 }
 
 }  // namespace
@@ -123,8 +224,31 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
             tokinfo[t] = n | string_summary(g, tok_bytes + a, n);
             for (uint32_t i = 0; i < n; i++) tokw[(size_t)(i >> 2) * V + t] |= (uint32_t)tok_bytes[a + i] << (8 * (i & 3));
         }
+        int lds_max = 0;
+        if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+            lds_max > 0)
+            g->lds_max = lds_max;
+        FillHost f;
+        build_fill_tables(g, tok_bytes, tok_offsets, tokinfo, f);
+        g->lex_tiles = (int32_t)(f.lex_idlen.size() / kTile);
+        g->q_tiles = (int32_t)(f.q_idlen.size() / kTile);
+        if (fill_lds_bytes(g, 1) + 1024 > (size_t)g->lds_max) {
+            set_error("transition table of %u slots needs %zu bytes of LDS in fill_bitmask, the device has %d",
+                      g->comb_len, fill_lds_bytes(g, 1), g->lds_max);
+            release(g);
+            return CG_E_LIMIT;
+        }
         if (upload(&g->dev.comb, g->host_comb, g->comb_len) || upload(&g->dev.tokw, tokw.data(), tokw.size()) ||
-            upload(&g->dev.tokinfo, tokinfo.data(), V)) {
+            upload(&g->dev.tokinfo, tokinfo.data(), V) || upload(&g->dev.legal, f.legal.data(), f.legal.size()) ||
+            upload(&g->dev.lex_idlen, f.lex_idlen.data(), f.lex_idlen.size()) ||
+            upload(&g->dev.lex_jump, f.lex_jump.data(), f.lex_jump.size()) ||
+            upload(&g->dev.lex_w, f.lex_w.data(), f.lex_w.size()) ||
+            upload(&g->dev.lex_tile, f.lex_tile.data(), f.lex_tile.size()) ||
+            upload(&g->dev.q_idlen, f.q_idlen.data(), f.q_idlen.size()) ||
+            upload(&g->dev.q_posch, f.q_posch.data(), f.q_posch.size()) ||
+            upload(&g->dev.q_w, f.q_w.data(), f.q_w.size()) ||
+            upload(&g->dev.q_tile, f.q_tile.data(), f.q_tile.size()) ||
+            upload(&g->dev.strbits, f.strbits.data(), f.strbits.size())) {
             set_error("device upload failed: %s", hipGetErrorString(hipGetLastError()));
             release(g);
             return CG_E_DEVICE;
@@ -154,12 +278,19 @@ int cg_init_state(const cg_grammar *g, cg_state *d_states, int32_t batch, void *
     return launch_init(g, d_states, batch, (hipStream_t)stream);
 }
 
+size_t cg_fill_workspace_bytes(const cg_grammar *g, int32_t batch) {
+    if (!on_device(g) || batch < 1) return 0;
+    return (size_t)batch * (size_t)fill_plan_stride(g) * sizeof(uint32_t);
+}
+
 int cg_fill_bitmask(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
-                    int32_t words_per_row, void *stream) {
+                    int32_t words_per_row, void *d_workspace, void *stream) {
     if (!on_device(g)) return arg_error("grammar has no device tables");
     if (batch < 0 || (batch > 0 && (!d_states || !d_mask))) return arg_error("bad states / mask / batch");
     if (words_per_row < (g->V + 63) / 64) return arg_error("words_per_row < ceil(vocab_size / 64)");
-    return launch_fill(g, d_states, batch, d_mask, words_per_row, (hipStream_t)stream);
+    if (batch > 0 && (!d_workspace || (uintptr_t)d_workspace % 16))
+        return arg_error("workspace must be a 16-byte aligned device buffer of cg_fill_workspace_bytes bytes");
+    return launch_fill(g, d_states, batch, d_mask, words_per_row, d_workspace, (hipStream_t)stream);
 }
 
 size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab) {

@@ -132,11 +132,40 @@ __host__ __device__ inline uint32_t tok_kind(uint32_t info) { return (info >> 8)
 __host__ __device__ inline uint32_t tok_chars(uint32_t info) { return (info >> 10) & 63u; }
 __host__ __device__ inline uint32_t tok_pos(uint32_t info) { return (info >> 16) & 31u; }
 
+// Candidate keys of the fill.  A non-empty token's key is its first two
+// bytes: b1 * 257 + (length 1 ? 0 : b2 + 1), so that in lexicographic order
+// keys never decrease.  A token after the closing quote of a string is keyed
+// by the byte after the quote: 0 if the quote ends the token, else byte + 1.
+constexpr int kKeysPerLead = 257;
+constexpr int kTile = 64;          // tokens per candidate tile (one wave)
+constexpr int kStrBitsets = 33;    // in-string bitsets for budgets 0..32 code points
+constexpr uint32_t kNoQuote = 63;  // jump field of a token without a quote
+
+__host__ __device__ inline uint32_t lead_key(uint32_t b1, uint32_t b2, uint32_t len) {
+    return b1 * kKeysPerLead + (len == 1 ? 0u : b2 + 1u);
+}
+
 // Device copy of a compiled grammar.
 struct DeviceTables {
     uint64_t *comb = nullptr;     // [comb_len]
     uint32_t *tokw = nullptr;     // [nw][V] token bytes, 4 per word, little-endian, zero padded
     uint32_t *tokinfo = nullptr;  // [V] length + string-body summary
+    uint64_t *legal = nullptr;    // [q_limit][4] bytes with a transition out of state q (256-bit set)
+    // Fill candidates: the non-empty tokens in lexicographic order, padded
+    // with empty entries (idlen 0) to whole 64-token tiles.
+    uint32_t *lex_idlen = nullptr;   // [lex_tiles * 64] id | len << 24
+    uint32_t *lex_jump = nullptr;    // [lex_tiles * 64] first quote position (kNoQuote: none) | string
+                                     //       summary of the bytes after it (tokinfo layout, bits 8..20)
+    uint32_t *lex_w = nullptr;       // [nw][lex_tiles * 64] token bytes
+    uint2 *lex_tile = nullptr;       // [lex_tiles] first and last key of each tile
+    // Tokens that close a string opened before them, sorted by the bytes
+    // after the quote, padded the same way.
+    uint32_t *q_idlen = nullptr;     // [q_tiles * 64] id | len << 24
+    uint32_t *q_posch = nullptr;     // [q_tiles * 64] quote position | code points before it << 8
+    uint32_t *q_w = nullptr;         // [nw][q_tiles * 64]
+    uint2 *q_tile = nullptr;         // [q_tiles] first and last after-quote key of each tile
+    uint64_t *strbits = nullptr;     // [33][ceil(V / 64)] tokens that stay inside a string from a
+                                     //       code-point boundary within a budget of c code points
 };
 
 }  // namespace cg
@@ -151,6 +180,9 @@ struct cg_grammar {
     uint32_t gen_cap = 2048;
     int device = -1;         // HIP device the tables live on (-1: host only)
     int n_cu = 256;          // compute units of that device
+    int lds_max = 65536;     // LDS bytes a workgroup may use on that device
+    int32_t lex_tiles = 0;   // candidate tiles of the lexicographic list
+    int32_t q_tiles = 0;     // and of the string-closing list
     double compile_ms = 0;
     uint64_t *host_comb = nullptr;
     cg::DeviceTables dev;

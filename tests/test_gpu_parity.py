@@ -317,3 +317,25 @@ def test_sample_fp32_greedy_ties(torch_dev):
     lp = torch.empty(B, dtype=torch.float32, device="cuda")
     cg.apply_mask_sample(logits, mask, temp, seed, step, cg.new_workspace(B, V), ids, lp)
     assert ids.cpu().tolist() == [100, 10, 0]
+
+
+def test_fill_workspace_reuse_and_size(torch_dev):
+    """The fill workspace needs no initialisation and may be reused by later
+    calls with fewer rows; a workspace that is too small is refused."""
+    torch = torch_dev
+    say("fill workspace")
+    g, og, blob, off, toks = _setup(3, 20000)
+    seqs, rows = _walks(og, toks, 24, 0xF111, 40)
+    st, _, _ = device_rows(g, seqs)
+    ws = g.new_fill_workspace(24)
+    ws.fill_(-1)  # stale contents must not matter
+    want, _ = oracle_masks(og, rows, blob, off)
+    for B in (24, 7):
+        mask = torch.full((B, g.W), 0x5A5A5A5A5A5A5A5A, dtype=torch.int64, device="cuda")
+        g.fill_bitmask(st[:B].contiguous(), mask, ws)
+        torch.cuda.synchronize()
+        _compare_masks(mask.cpu().numpy().view(np.uint64), want[:B], len(toks), f"workspace reuse B={B}")
+    assert g.fill_workspace_bytes(24) > g.fill_workspace_bytes(7) > 0 == g.fill_workspace_bytes(0)
+    small = torch.empty(max(1, g.fill_workspace_bytes(7) // 8 - 1), dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        g.fill_bitmask(st[:8].contiguous(), torch.empty((8, g.W), dtype=torch.int64, device="cuda"), small)
