@@ -527,6 +527,7 @@ __device__ __forceinline__ double wave_reduce_d(double v, F op) {
 __device__ inline float wave_max_f(float v) { return wave_reduce_f(v, [](float a, float b) { return fmaxf(a, b); }); }
 __device__ inline double wave_max_d(double v) { return wave_reduce_d(v, [](double a, double b) { return fmax(a, b); }); }
 __device__ inline double wave_sum_d(double v) { return wave_reduce_d(v, [](double a, double b) { return a + b; }); }
+__device__ inline float wave_sum_f(float v) { return wave_reduce_f(v, [](float a, float b) { return a + b; }); }
 
 // argmax of (value, index): larger value, then lower index; index -1 = none
 __device__ inline void arg_better(double &v, int &i, double ov, int oi) {
@@ -607,37 +608,69 @@ __device__ __forceinline__ float masked_x(const ChunkRegs<DT> &R, int g, int j) 
     return __uint_as_float((sel & u) | (~sel & 0xFF800000u));
 }
 
-// masked max m and sum over allowed ids of 2^((x - m) kk), kk = log2(e) / T'
+// Mask byte -> for each of its four bf16 pairs a 32-bit select mask (a half
+// of ones per allowed id), so that one bit-select per pair masks two logits.
+__device__ __forceinline__ void init_pair_lut(uint4 *lut) {
+    const uint32_t v = threadIdx.x;
+    if (v < 256) {
+        uint32_t m[4];
+#pragma unroll
+        for (int p = 0; p < 4; p++)
+            m[p] = (((v >> (2 * p)) & 1u) ? 0x0000FFFFu : 0u) | (((v >> (2 * p + 1)) & 1u) ? 0xFFFF0000u : 0u);
+        lut[v] = make_uint4(m[0], m[1], m[2], m[3]);
+    }
+}
+
+// masked max m and sum over allowed ids of 2^((x - m) kk), kk = log2(e) / T'.
+// The exponent is one fma, x kk - r(m kk), whose only error beyond a single
+// rounding is the constant offset m kk - r(m kk); that offset is taken out of
+// the chunk sum once, in double precision.  The 64 lane sums (each of 32
+// terms <= 1) are added as a tree in float: relative error ~1e-6.  Groups of
+// 8 ids with no allowed id skip the exponentials (most of a structural row).
 template <int DT>
-__device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, float kk, float &m_out, double &s_out,
-                                             bool &any_out) {
-    float xm[32];
-    float m = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < 4; g++)
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            xm[g * 8 + j] = masked_x<DT>(R, g, j);
-            m = fmaxf(m, xm[g * 8 + j]);
-        }
+__device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4 *lut, float kk, float &m_out,
+                                             double &s_out, bool &any_out) {
     any_out = __any(R.mb[0] | R.mb[1] | R.mb[2] | R.mb[3]);
     m_out = -INFINITY;
     s_out = 0.0;
     if (!any_out) return;
+    float xm[32];
+    float m = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        if (DT == 1) {
+            const uint4 sel = lut[R.mb[g]];
+            const uint32_t sp[4] = {sel.x, sel.y, sel.z, sel.w};
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                const uint32_t u = (R.d[g * 4 + p] & sp[p]) | (~sp[p] & 0xFF80FF80u);
+                xm[g * 8 + 2 * p] = __uint_as_float(u << 16);
+                xm[g * 8 + 2 * p + 1] = __uint_as_float(u & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++) xm[g * 8 + j] = masked_x<DT>(R, g, j);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) m = fmaxf(m, xm[g * 8 + j]);
+    }
     m = wave_max_f(m);
     m_out = m;
     if (m == -INFINITY) return;  // every allowed logit is -inf
-    // 2^((x - m) kk): x - m is exact for the largest terms, so the dominant
-    // term is exactly 1 whatever the magnitude of m (masked terms are 2^-inf = 0)
+    const float mk = m * kk;
     float s = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; g++) {
-        float sg = 0.f;
+        if (R.mb[g]) {
+            float sg = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; j++) sg += __builtin_amdgcn_exp2f((xm[g * 8 + j] - m) * kk);
-        s += sg;
+            for (int j = 0; j < 8; j++) sg += __builtin_amdgcn_exp2f(__builtin_fmaf(xm[g * 8 + j], kk, -mk));
+            s += sg;
+        }
     }
-    s_out = wave_sum_d((double)s);
+    // every term carries the factor 2^(m kk - r(m kk)); divide it out
+    const double off = (double)m * (double)kk - (double)mk;
+    s_out = (double)wave_sum_f(s) * (1.0 - off * 0.6931471805599453);
 }
 
 // ---- block-wide reductions (kWaves waves) --------------------------------
@@ -837,15 +870,30 @@ __device__ __forceinline__ Top2 top2_slots(const float *v1, const int *i1, const
 // before the current one is reduced) and leave one summary per chunk in LDS;
 // then the whole workgroup forms the log-normaliser and picks the token.
 // No state crosses workgroups, so no device-wide fence is ever needed.
+// Per-wave copy of the best chunk seen so far (bf16 rows): the chunk's logits
+// in id order (4 KB) and its mask bytes, so the pick inside the chosen chunk
+// reads LDS instead of HBM.
+constexpr int kStashWords = kChunk / 2;  // bf16 pairs per chunk
+struct Stash {
+    uint32_t d[kWaves][kStashWords];
+    uint32_t mb[kWaves][64];
+    int c[kWaves];
+};
+
+// byte offset of the stash in dynamic LDS: after the chunk summaries, 16-byte aligned
+__host__ __device__ inline size_t stash_offset(int K) { return ((size_t)K * sizeof(ChunkInfo) + 15) / 16 * 16; }
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
                                                  const uint64_t *__restrict__ mask, int words_per_row,
                                                  const float *__restrict__ temp, const uint64_t *__restrict__ seed,
-                                                 const int32_t *__restrict__ step, int K,
+                                                 const int32_t *__restrict__ step, int K, int use_stash,
                                                  int32_t *__restrict__ out_id, float *__restrict__ out_lp) {
-    extern __shared__ ChunkInfo ci[];
+    extern __shared__ uint64_t dyn[];
+    ChunkInfo *ci = (ChunkInfo *)dyn;
+    Stash *st = (Stash *)((char *)dyn + stash_offset(K));  // valid when use_stash (bf16 only)
     __shared__ Slots sl[4];
-    __shared__ float xstash[kChunk];
+    __shared__ uint4 lut[256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = blockIdx.x;
     const float Tf = temp[r];
@@ -853,42 +901,69 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const uint32_t stp = (uint32_t)step[r];
     const bool greedy = !(Tf > 0.f);
     const double T = greedy ? 1.0 : (double)Tf;
+    const double invT = 1.0 / T;
     const float kk = greedy ? kLog2e : kLog2e / Tf;
     const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
     const uint8_t *mrow = (const uint8_t *)(mask + (size_t)r * words_per_row);
     const size_t rowbase = (size_t)r * (size_t)stride;
+    constexpr double kLn2d = 0.6931471805599453;
+    const bool stash = DT == 1 && use_stash;
+    if (DT == 1) init_pair_lut(lut);
+    if (stash && lane == 0) st->c[wave] = -1;
     {
-        ChunkRegs<DT> cur, nxt;
+        // chunks per wave in flight: the one being reduced and the next two
+        // (bf16), or the next one (float32, whose chunks take twice the registers)
+        constexpr int kAhead = DT == 1 ? 2 : 1;
+        ChunkRegs<DT> cur, nxt, nxt2;
         int c = wave;
         if (c < K) load_chunk<DT, VEC>(cur, logits, rowbase, mrow, V, c, lane);
-        // chunk noise G(1, c) for this wave's chunks, while the loads fly
+        if (kAhead == 2 && c + kWaves < K) load_chunk<DT, VEC>(nxt, logits, rowbase, mrow, V, c + kWaves, lane);
+        // chunk noise G(1, c) for this wave's chunks (c = wave + 16 lane), while the loads fly
         const int cg = wave + kWaves * lane;
         if (!greedy && cg < K) {
             const uint4 o = philox4x32_10(make_uint4((uint32_t)cg >> 2, stp, 1u, 0u), k0, k1);
             ci[cg].g = gumbel64(pick_word(o, cg & 3));
         }
+        __syncthreads();  // the mask table
+        double best = -INFINITY;
         for (; c < K; c += kWaves) {
-            if (c + kWaves < K) load_chunk<DT, VEC>(nxt, logits, rowbase, mrow, V, c + kWaves, lane);
+            if (c + kAhead * kWaves < K)
+                load_chunk<DT, VEC>(kAhead == 2 ? nxt2 : nxt, logits, rowbase, mrow, V, c + kAhead * kWaves, lane);
             float m;
             double s;
             bool any;
-            reduce_chunk<DT>(cur, kk, m, s, any);
+            reduce_chunk<DT>(cur, lut, kk, m, s, any);
             if (lane == 0) {
                 ci[c].m = m;
                 ci[c].s = s;
                 ci[c].any = any ? 1 : 0;
             }
+            if (stash && any) {
+                // the same score the row's decision ranks chunks by
+                double score = (double)m;
+                if (!greedy)
+                    score = (s > 0.0) ? (double)m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)s) + ci[c].g
+                                      : -INFINITY;
+                if (score > best) {
+                    best = score;
+#pragma unroll
+                    for (int g = 0; g < 4; g++)
+                        *(uint4 *)&st->d[wave][g * 256 + lane * 4] =
+                            make_uint4(cur.d[g * 4], cur.d[g * 4 + 1], cur.d[g * 4 + 2], cur.d[g * 4 + 3]);
+                    st->mb[wave][lane] = cur.mb[0] | cur.mb[1] << 8 | cur.mb[2] << 16 | cur.mb[3] << 24;
+                    if (lane == 0) st->c[wave] = c;
+                }
+            }
             cur = nxt;
+            if (kAhead == 2) nxt = nxt2;
         }
     }
     __syncthreads();
     // ---- the row's decision: wave 0 reduces the chunk summaries ----------
     // (1) log-mass L_c = m/T + ln s per chunk (ln from v_log_f32: the chunk
     // sums carry ~1e-6 of float rounding anyway), the largest logit (lowest
-    // chunk) and the two best chunk scores L_c + G(1, c); (2) the
-    // log-normaliser.  Published in LDS for the other waves.
-    constexpr double kLn2d = 0.6931471805599453;
-    const double invT = 1.0 / T;
+    // chunk), the two best chunk scores L_c + G(1, c); (2) the
+    // log-normaliser.  Published in LDS.
     Decision &dc = sl[0].dc;
     if (wave == 0) {
         double lc = -INFINITY, mv = -INFINITY;
@@ -906,8 +981,18 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         lc = wave_max_d(lc);
         wave_argmax(mv, mc);
         if (!greedy) cs = top2d_wave(cs);
+        float acc = 0.f;
+        if (lc > -INFINITY)
+            for (int c = lane; c < K; c += 64) {
+                const ChunkInfo x = ci[c];
+                if (!x.any || !(x.s > 0.0)) continue;
+                const double l = (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s);
+                acc += __builtin_amdgcn_exp2f((float)((l - lc) * 1.4426950408889634));
+            }
+        const double sum = wave_sum_d((double)acc);
         if (lane == 0) {
             dc.lmax = lc;
+            dc.lse_all = lc + kLn2d * (double)__builtin_amdgcn_logf((float)sum);
             dc.mv = mv;
             dc.mc = mc;
             dc.chosen = greedy ? mc : cs.i1;
@@ -945,47 +1030,57 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         }
         return;
     }
-    // (3) inside the chunk, waves 0-3, 8 ids per lane: the logits and the
-    // token noise start while wave 0 forms the normaliser
-    const bool tok_wave = wave < 4;
-    const int e = chosen * kChunk + wave * 512 + lane * 8;
-    uint32_t mb = 0;
-    float xv[8];
-    uint4 o0 = make_uint4(0, 0, 0, 0), o1 = make_uint4(0, 0, 0, 0);
-    if (tok_wave) {
+    // (3) inside the chunk: threads 0..511 take 4 ids each, e = 4t .. 4t + 3
+    // (one Philox block), from the stash of the wave that reduced the chunk,
+    // else from HBM
+    const int t = threadIdx.x;
+    const bool tok = t < kChunk / 4;
+    const int e = chosen * kChunk + 4 * t;
+    const int ws = chosen % kWaves;
+    const bool from_stash = stash && st->c[ws] == chosen;
+    float xq[4] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t mb4 = 0;  // mask bits of e .. e + 3
+    if (tok) {
+        if (from_stash) {
+            const uint2 dw = *(const uint2 *)&st->d[ws][2 * t];
+            xq[0] = __uint_as_float(dw.x << 16);
+            xq[1] = __uint_as_float(dw.x & 0xFFFF0000u);
+            xq[2] = __uint_as_float(dw.y << 16);
+            xq[3] = __uint_as_float(dw.y & 0xFFFF0000u);
+            const int li = 4 * t;
+            mb4 = (st->mb[ws][(li & 511) >> 3] >> (8 * (li >> 9) + (li & 7))) & 15u;
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; j++) xv[j] = (e + j < V) ? load_logit<DT>(logits, rowbase + e + j) : 0.f;
-        mb = (e < V) ? mrow[e >> 3] : 0u;
-        if (e + 8 > V) mb &= (e >= V) ? 0u : ((1u << (V - e)) - 1u);
-        if (!greedy && mb) {
-            o0 = philox4x32_10(make_uint4((uint32_t)e >> 2, stp, 0u, 0u), k0, k1);
-            o1 = philox4x32_10(make_uint4(((uint32_t)e >> 2) + 1u, stp, 0u, 0u), k0, k1);
+            for (int j = 0; j < 4; j++)
+                if (e + j < V) {
+                    xq[j] = load_logit<DT>(logits, rowbase + e + j);
+                    mb4 |= ((mrow[(e + j) >> 3] >> ((e + j) & 7)) & 1u) << j;
+                }
         }
     }
-    if (wave == 0) {
-        float acc = 0.f;
-        for (int c = lane; c < K; c += 64) {
-            const ChunkInfo x = ci[c];
-            if (!x.any || !(x.s > 0.0)) continue;
-            const double l = (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s);
-            acc += __builtin_amdgcn_exp2f((float)((l - dc.lmax) * 1.4426950408889634));
+    auto x_of = [&](int id) -> float {  // logit of an id of the chosen chunk
+        const int li = id - chosen * kChunk;
+        if (from_stash) {
+            const uint32_t dw = st->d[ws][li >> 1];
+            return __uint_as_float((li & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
         }
-        const double sum = wave_sum_d((double)acc);
-        if (lane == 0) dc.lse_all = dc.lmax + kLn2d * (double)__builtin_amdgcn_logf((float)sum);
-    }
+        return load_logit<DT>(logits, rowbase + id);
+    };
+    constexpr int kTokWaves = kChunk / 4 / 64;
     if (greedy) {
         // the lowest id of the chunk holding the largest logit
         int im = 0x7FFFFFFF;
-        if (tok_wave)
-            for (int j = 7; j >= 0; j--)
-                if (((mb >> j) & 1u) && (double)xv[j] == dc.mv) im = e + j;
-        if (tok_wave) {
+#pragma unroll
+        for (int j = 3; j >= 0; j--)
+            if (((mb4 >> j) & 1u) && (double)xq[j] == dc.mv) im = e + j;
+        if (wave < kTokWaves) {
             im = wave_min_i(im);
             if (lane == 0) sl[2].i[wave] = im;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
-            const int best = min(min(sl[2].i[0], sl[2].i[1]), min(sl[2].i[2], sl[2].i[3]));
+            int best = sl[2].i[0];
+            for (int w = 1; w < kTokWaves; w++) best = min(best, sl[2].i[w]);
             out_id[r] = best;
             out_lp[r] = (float)(dc.mv - dc.lse_all);
         }
@@ -994,34 +1089,35 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     // sampled: argmax_i x_i / T + G(0, i) screened in float; the winner is
     // exact unless the best two are within the screening error (x/T rounding
     // < 1e-6 |x/T|, G < 1e-5), in which case the contenders are recomputed
-    Top2 ts{-INFINITY, -INFINITY, -1};
-    if (tok_wave) {
-        const float it = 1.0f / Tf;
+    const float it = 1.0f / Tf;
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (mb4) o = philox4x32_10(make_uint4((uint32_t)e >> 2, stp, 0u, 0u), k0, k1);
+    const uint32_t wq[4] = {o.x, o.y, o.z, o.w};
+    if (wave < kTokWaves) {
+        Top2 ts{-INFINITY, -INFINITY, -1};
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            if ((mb >> j) & 1u) top2_merge(ts, xv[j] * it + gumbel32(pick_word(j < 4 ? o0 : o1, j & 3)), e + j, -INFINITY);
+        for (int j = 0; j < 4; j++)
+            if ((mb4 >> j) & 1u) top2_merge(ts, xq[j] * it + gumbel32(wq[j]), e + j, -INFINITY);
         ts = top2_wave(ts);
         if (lane == 0) {
             sl[2].f[wave] = ts.v1;
             sl[2].h[wave] = ts.v2;
             sl[2].i[wave] = ts.i1;
         }
-#pragma unroll
-        for (int j = 0; j < 8; j++) xstash[wave * 512 + lane * 8 + j] = xv[j];
     }
     __syncthreads();
     if (wave == 0) {
-        Top2 t{-INFINITY, -INFINITY, -1};
-        for (int k = 0; k < 4; k++) top2_merge(t, sl[2].f[k], sl[2].i[k], sl[2].h[k]);
-        const double win = 1e-4 + 2e-6 * fabs((double)t.v1);
-        const bool unique = (double)t.v1 - (double)t.v2 > win;
+        Top2 tt{-INFINITY, -INFINITY, -1};
+        for (int k = 0; k < kTokWaves; k++) top2_merge(tt, sl[2].f[k], sl[2].i[k], sl[2].h[k]);
+        const double win = 1e-4 + 2e-6 * fabs((double)tt.v1);
+        const bool unique = (double)tt.v1 - (double)tt.v2 > win;
         if (lane == 0) {
             dc.exact_token = !unique;
             dc.win = win;
-            dc.tv1 = t.v1;
+            dc.tv1 = tt.v1;
             if (unique) {
-                out_id[r] = t.i1;
-                out_lp[r] = (float)((double)xstash[t.i1 - chosen * kChunk] / T - dc.lse_all);
+                out_id[r] = tt.i1;
+                out_lp[r] = (float)((double)x_of(tt.i1) / T - dc.lse_all);
             }
         }
     }
@@ -1030,14 +1126,13 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     // contenders recomputed in double (rare)
     double tv = -INFINITY;
     int ti = -1;
-    if (tok_wave) {
-        const float it = 1.0f / Tf;
-        for (int j = 0; j < 8; j++) {
-            if (!((mb >> j) & 1u)) continue;
-            const uint32_t w = pick_word(j < 4 ? o0 : o1, j & 3);
-            if ((double)(xv[j] * it + gumbel32(w)) >= (double)dc.tv1 - dc.win)
-                arg_better(tv, ti, (double)xv[j] / T + gumbel64(w), e + j);
-        }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        if (!((mb4 >> j) & 1u)) continue;
+        if ((double)(xq[j] * it + gumbel32(wq[j])) >= (double)dc.tv1 - dc.win)
+            arg_better(tv, ti, (double)xq[j] / T + gumbel64(wq[j]), e + j);
+    }
+    if (wave < kTokWaves) {
         wave_argmax(tv, ti);
         if (lane == 0) {
             sl[3].b[wave] = tv;
@@ -1048,9 +1143,9 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     if (threadIdx.x == 0) {
         double v = sl[3].b[0];
         int i = sl[3].j[0];
-        for (int k = 1; k < 4; k++) arg_better(v, i, sl[3].b[k], sl[3].j[k]);
+        for (int k = 1; k < kTokWaves; k++) arg_better(v, i, sl[3].b[k], sl[3].j[k]);
         out_id[r] = i;
-        out_lp[r] = (float)((double)xstash[i - chosen * kChunk] / T - dc.lse_all);
+        out_lp[r] = (float)((double)x_of(i) / T - dc.lse_all);
     }
 }
 
@@ -1161,16 +1256,29 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
     (void)ws;
     if (B == 0) return CG_OK;
     const int K = (V + kChunk - 1) / kChunk;
-    const size_t lds = (size_t)K * sizeof(ChunkInfo);
-    if (lds > 48 * 1024) {
+    const size_t lds_ci = (size_t)K * sizeof(ChunkInfo);
+    if (lds_ci > 48 * 1024) {
         set_error("apply_mask_sample: vocab above %d", 48 * 1024 / (int)sizeof(ChunkInfo) * kChunk);
         return CG_E_ARG;
     }
+    // bf16 rows keep each wave's best chunk in LDS when it fits
+    int dev = 0, lds_max = 65536;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        lds_max = 65536;
+    const size_t static_lds = 4 * sizeof(Slots) + 256 * sizeof(uint4);
+    const int use_stash = dt == 1 && stash_offset(K) + sizeof(Stash) + static_lds + 256 <= (size_t)lds_max;
+    const size_t lds = use_stash ? stash_offset(K) + sizeof(Stash) : lds_ci;
     const int es = dt == 0 ? 4 : 2;
     const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * es) % 16 == 0);
-#define CG_LAUNCH_SAMPLE(D, VV)                                                                                   \
-    hipLaunchKernelGGL((k_sample<D, VV>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask, wpr, temp, \
-                       seed, step, K, out_id, out_lp)
+#define CG_LAUNCH_SAMPLE(D, VV)                                                                                  \
+    do {                                                                                                         \
+        if (lds > 64 * 1024 && hipFuncSetAttribute((const void *)k_sample<D, VV>,                                \
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) \
+            return launch_status("apply_mask_sample (LDS attribute)");                                           \
+        hipLaunchKernelGGL((k_sample<D, VV>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask, wpr, \
+                           temp, seed, step, K, use_stash, out_id, out_lp);                                      \
+    } while (0)
     if (dt == 0) {
         if (vec) CG_LAUNCH_SAMPLE(0, true);
         else CG_LAUNCH_SAMPLE(0, false);
