@@ -23,6 +23,33 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E
 CONFIG = 3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_sample_hbm_traffic_toolcall_v128k_b256.md")
+KERNEL_SRC = os.path.join(ROOT, "logit_masking_amd", "csrc", "sample.hip")
+
+
+def kernel_source_sha():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per k_sample launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a device copy of known size),
+    or None when the kernels have changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("sample.hip sha256") != kernel_source_sha():
+        return None
+    try:
+        return float(vals["hbm bytes per launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def pct(a, q):
@@ -84,6 +111,8 @@ def main():
     ap.add_argument("--pool", type=int, default=64, help="distinct logits buffers cycled over the steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 64 MiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: rows shard across GPUs with no exchange, and multi-GPU runs are not "
@@ -178,7 +207,7 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(sample_gbps / HBM_PEAK_GBPS, 4),
-        "traffic": None,
+        "traffic": recorded_traffic(),
     }
     out = {
         "metric": "token-checks/s (fill_bitmask) + masked-sample GB/s vs HBM peak; µs/step",
@@ -215,6 +244,13 @@ def main():
         "table_bytes": info["table_bytes"],
         "roofline": roofline,
     }
+    if args.calib_copy:
+        src = torch.empty(32 << 20, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            torch.neg(src, out=dst)  # an elementwise kernel: reads and writes 64 MiB
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = src.numel() * 2
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(ids_hist.cpu().numpy(), B, V, blob, off, args.cpu_budget)
     print(json.dumps(out))

@@ -193,4 +193,14 @@ namespace cg {
 // Returns CG_OK or an error code (message via set_error).
 int compile_spec(const char *spec, size_t len, cg_grammar *g);
 void set_error(const char *fmt, ...);
+
+// HIP launch error of the last launch, as a CG_E_DEVICE with a message.
+inline int launch_status(const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error("%s: %s", what, hipGetErrorString(e));
+        return CG_E_DEVICE;
+    }
+    return CG_OK;
+}
 }  // namespace cg

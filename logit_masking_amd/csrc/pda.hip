@@ -1,0 +1,561 @@
+// pda.hip -- gfx950 kernels of the automaton side of the constrained-decoding
+// step ("Constrained decoding", "The guarantee": a pushdown automaton masks
+// the logits at every step).
+//
+//   k_init        rows at the start state
+//   k_advance     one lane per row walks the chosen token
+//   k_fill_plan   token bitmask, part 1: per row the base words (zero, or the
+//                 tokens that stay inside an open string) and the list of
+//                 token tiles worth walking, chosen by the row's legal first
+//                 and second bytes
+//   k_fill_walk   token bitmask, part 2: one lane per listed token walks it
+//                 through the transition table staged in LDS
+//
+// Nothing here is a dense contraction, so there is no MFMA: the work is
+// table lookups, integer ALU and latency.
+#include <algorithm>
+
+#include "cg_internal.hpp"
+
+namespace cg {
+
+// ---------------------------------------------------------------------------
+// init / advance
+// ---------------------------------------------------------------------------
+__global__ void k_init(cg_state *__restrict__ states, int B, uint32_t start) {
+    int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= B) return;
+    cg_state s;
+    s.q = (uint16_t)start;
+    s.ret = (uint16_t)start;
+    s.cnt = 0;
+    s.stk = 0;
+    s.depth = 0;
+    s.ws = 0;
+    s.flags = 0;
+    s.pad0 = 0;
+    s.pad1 = 0;
+    states[r] = s;
+}
+
+// Copy n table slots to LDS with up to 16 loads per thread in flight before
+// the first store (a plain load/store loop waits out one round trip per slot).
+__device__ __forceinline__ void stage_table(uint64_t *dst, const uint64_t *__restrict__ src, uint32_t n) {
+    constexpr int kInFlight = 16;
+    for (uint32_t base = 0; base < n; base += kInFlight * blockDim.x) {
+        uint64_t v[kInFlight];
+#pragma unroll
+        for (int j = 0; j < kInFlight; j++) {
+            const uint32_t i = base + j * blockDim.x + threadIdx.x;
+            v[j] = i < n ? src[i] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < kInFlight; j++) {
+            const uint32_t i = base + j * blockDim.x + threadIdx.x;
+            if (i < n) dst[i] = v[j];
+        }
+    }
+}
+
+// One lane per row.  The row's id, configuration and token bytes are loaded
+// first, then the transition table is staged in LDS while those loads fly,
+// so the byte walk is a chain of LDS lookups, not of L2 round trips.
+__global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ comb, uint32_t comb_len, WalkConsts k,
+                                                 const uint32_t *__restrict__ tokw, const uint32_t *__restrict__ tokinfo,
+                                                 int nw, int V, cg_state *__restrict__ states, int B,
+                                                 const int32_t *__restrict__ ids, int32_t *__restrict__ steps,
+                                                 int32_t *__restrict__ status, uint32_t gen_cap) {
+    extern __shared__ uint64_t lds_comb[];
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    const bool row = r < B;
+    const int id = row ? ids[r] : -1;
+    cg_state s{};
+    int st0 = 0;
+    if (row) {
+        s = states[r];
+        st0 = steps[r];
+    }
+    const bool valid = id >= 0 && id < V && !(s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) && s.q < k.q_limit &&
+                       s.ret < k.q_limit;
+    uint32_t n = 0;
+    uint32_t words[kMaxTokenLen / 4];
+#pragma unroll
+    for (int j = 0; j < kMaxTokenLen / 4; j++) words[j] = 0;
+    if (valid) {
+        n = tok_len(tokinfo[id]);
+#pragma unroll
+        for (int j = 0; j < kMaxTokenLen / 4; j++)
+            if (j < nw) words[j] = tokw[(size_t)j * V + id];
+    }
+    stage_table(lds_comb, comb, comb_len);
+    __syncthreads();
+    if (!row) return;
+    if (id < 0) {
+        status[r] = CG_ROW_NOOP;
+        return;
+    }
+    if (!valid) {
+        status[r] = CG_ROW_REJECTED;
+        return;
+    }
+    Walker w = load_walker(s);
+    bool ok = n > 0;
+#pragma unroll
+    for (int i = 0; i < kMaxTokenLen; i++) {  // unrolled: the word index is a constant
+        if (!ok || (uint32_t)i >= n) break;
+        ok = step_byte(w, (words[i >> 2] >> (8 * (i & 3))) & 0xFFu, lds_comb, k);
+    }
+    if (!ok) {
+        status[r] = CG_ROW_REJECTED;
+        return;
+    }
+    store_walker(s, w);
+    const int st = st0 + 1;
+    steps[r] = st;
+    int res = CG_ROW_OK;
+    uint8_t fl = 0;
+    if (w.q == k.accept) {
+        fl |= CG_FLAG_DONE;
+        res = CG_ROW_DONE;
+    }
+    if ((uint32_t)st >= gen_cap) {
+        fl |= CG_FLAG_CAPPED;
+        if (res == CG_ROW_OK) res = CG_ROW_CAPPED;
+    }
+    s.flags = fl;
+    states[r] = s;
+    status[r] = res;
+}
+
+// ---------------------------------------------------------------------------
+// fill_bitmask
+// ---------------------------------------------------------------------------
+//
+// A mask bit is the outcome of walking the token's bytes from the row's
+// configuration.  Almost every token dies within its first two bytes, so the
+// walk is done only where it can succeed.  Tokens are kept in lexicographic
+// order cut into 64-token tiles whose key spans (first two bytes) are known.
+//
+//   k_fill_plan   one workgroup per row.  Writes the row's base words: zero,
+//                 or for a row inside a string at a code-point boundary the
+//                 precomputed set of tokens that stay inside the string
+//                 within its code-point budget (decided by their count
+//                 alone).  Then lists the tiles worth walking:
+//     general row one lane per byte finds the legal first bytes and the
+//                 state after each; a key (b1, b2) is a candidate if that
+//                 state has any transition on b2 (a per-state 256-bit set);
+//                 a tile is listed if its span holds a candidate key.
+//     string row  the tokens whose quote closes the string, sorted by the
+//                 byte after the quote; a tile is listed if that byte can
+//                 follow the string.
+//   k_fill_walk   (row, slice): slice s walks the listed tiles s, s + S, ...
+//                 of its row, one lane per token, through the transition
+//                 table staged in LDS.  A walk that opens a string at the
+//                 token's first quote jumps over the string content with the
+//                 token's precomputed summary of the bytes after that quote.
+//                 Accepted tokens are OR-ed into the mask with 64-bit atomics.
+constexpr int kFillThreads = 256;
+constexpr int kFillWaves = kFillThreads / 64;
+
+__device__ __forceinline__ bool row_live(const cg_state &s, const WalkConsts &k) {
+    return !(s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) && s.q < k.q_limit && s.ret < k.q_limit;
+}
+
+struct FillArgs {
+    const uint64_t *comb;
+    uint32_t comb_len;
+    WalkConsts k;
+    const uint64_t *legal;
+    const uint32_t *lex_idlen, *lex_jump, *lex_w;
+    const uint2 *lex_tile;
+    int lex_tiles;
+    const uint32_t *q_idlen, *q_posch, *q_w;
+    const uint2 *q_tile;
+    int q_tiles;
+    const uint64_t *strbits;
+    int Wv;
+    const cg_state *states;
+    unsigned long long *mask;
+    int words_per_row;
+    uint32_t *plan;       // per row: [0] listed tiles, [1..] their indices
+    int plan_stride;      // u32 per row
+    int B;
+};
+
+// Byte Bi of the token (compile-time index: the walk is fully unrolled, so
+// the token words stay in registers with no dynamic indexing).  A lane walks
+// bytes [start, end) of its token while alive; the wave leaves as soon as no
+// lane has bytes left.  `jump` (kNoQuote: none) is the token's first quote
+// position and the string summary of the bytes after it.
+template <int Bi, int NB, int NW>
+__device__ __forceinline__ void walk_bytes(Walker &wk, bool &alive, const uint32_t (&w)[NW], int &start, int &end,
+                                           uint32_t jump, const uint64_t *lds_comb, const WalkConsts &k) {
+    if constexpr (Bi < NB) {
+        if (!__any(alive && Bi < end)) return;
+        if (alive && Bi >= start && Bi < end) {
+            alive = step_byte(wk, (w[Bi >> 2] >> ((Bi & 3) * 8)) & 0xFFu, lds_comb, k);
+            if (alive && (jump & 63u) == (uint32_t)Bi && wk.q == k.s_body) {
+                // the quote opened a string: the rest of the token is string
+                // content up to its closing quote, if any
+                const uint32_t kind = tok_kind(jump), nch = tok_chars(jump);
+                alive = kind != STR_DEAD && nch <= wk.cnt;
+                if (kind == STR_QUOTE) {
+                    wk.q = wk.ret;
+                    wk.ws = 0;
+                    wk.cnt -= nch;
+                    start = Bi + 2 + (int)tok_pos(jump);
+                } else {
+                    end = 0;
+                }
+            }
+        }
+        walk_bytes<Bi + 1, NB, NW>(wk, alive, w, start, end, jump, lds_comb, k);
+    }
+}
+
+__device__ __forceinline__ bool bit_of(const uint64_t *words, uint32_t j) { return (words[j >> 6] >> (j & 63)) & 1u; }
+
+// Any set bit in positions [lo, hi] of a 256-bit set.
+__device__ __forceinline__ bool any_bits(const uint64_t *words, uint32_t lo, uint32_t hi) {
+    for (uint32_t wi = lo >> 6; wi <= (hi >> 6); wi++) {
+        uint64_t m = words[wi];
+        if (wi == (lo >> 6)) m &= ~0ull << (lo & 63);
+        if (wi == (hi >> 6)) m &= ~0ull >> (63 - (hi & 63));
+        if (m) return true;
+    }
+    return false;
+}
+
+// Does the key span [kf, kl] of a tile hold a candidate key of the row?
+// Key 0 of a legal lead byte (its one-byte token) always is; key j > 0 is
+// if the state after the lead byte has a transition on byte j - 1 (the
+// 256-bit sets of those states, one per legal lead byte, are in `second`).
+__device__ __forceinline__ bool span_legal(uint32_t kf, uint32_t kl, const uint64_t *valid1,
+                                           const uint64_t *second) {
+    const uint32_t b_lo = kf / kKeysPerLead, b_hi = kl / kKeysPerLead;
+    for (uint32_t wi = b_lo >> 6; wi <= (b_hi >> 6); wi++) {
+        uint64_t m = valid1[wi];
+        if (wi == (b_lo >> 6)) m &= ~0ull << (b_lo & 63);
+        if (wi == (b_hi >> 6)) m &= ~0ull >> (63 - (b_hi & 63));
+        while (m) {
+            const uint32_t b = wi * 64 + (uint32_t)__builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t base = b * kKeysPerLead;
+            const uint32_t lo = b == b_lo ? kf - base : 0u, hi = b == b_hi ? kl - base : kKeysPerLead - 1u;
+            if (lo == 0 || any_bits(second + b * 4, lo - 1, hi - 1)) return true;
+        }
+    }
+    return false;
+}
+
+// Append the flagged tiles of this wave to the item's tile list.
+__device__ __forceinline__ void append_tiles(bool act, uint32_t t, uint32_t *list, uint32_t *count) {
+    const uint64_t m = __ballot(act);
+    if (m == 0) return;
+    const int lane = threadIdx.x & 63;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(count, (uint32_t)__popcll(m));
+    base = __shfl(base, 0);
+    if (act) list[base + __popcll(m & ((1ull << lane) - 1ull))] = t;
+}
+
+template <int NW>
+__device__ __forceinline__ uint32_t byte_at(const uint32_t (&w)[NW], uint32_t i) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < NW; j++) x = (uint32_t)j == (i >> 2) ? w[j] : x;
+    return (x >> (8 * (i & 3))) & 0xFFu;
+}
+
+// One tile's worth of a lane: its token (or padding) and where its walk starts.
+template <int NW>
+struct LaneTok {
+    uint32_t il, aux;  // id | len << 24; jump (lexicographic list) or quote position | chars (string list)
+    uint32_t w[NW];
+};
+
+template <int NW>
+__device__ __forceinline__ void load_lane(LaneTok<NW> &x, bool in_str, int i, const FillArgs &a) {
+    if (in_str) {
+        const int n = a.q_tiles * kTile;
+        x.il = a.q_idlen[i];
+        x.aux = a.q_posch[i];
+#pragma unroll
+        for (int j = 0; j < NW; j++) x.w[j] = a.q_w[(size_t)j * n + i];
+    } else {
+        const int n = a.lex_tiles * kTile;
+        x.il = a.lex_idlen[i];
+        x.aux = a.lex_jump[i];
+#pragma unroll
+        for (int j = 0; j < NW; j++) x.w[j] = a.lex_w[(size_t)j * n + i];
+    }
+}
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanKeys = 8;  // tile keys each plan thread loads up front
+
+__global__ __launch_bounds__(kPlanThreads) void k_fill_plan(FillArgs a) {
+    __shared__ uint64_t valid1[4];
+    __shared__ uint64_t second[256 * 4];
+    __shared__ uint32_t n_active;
+    const WalkConsts &k = a.k;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x;
+    const cg_state s = a.states[r];
+    uint32_t *plan = a.plan + (size_t)r * a.plan_stride;
+    unsigned long long *out = a.mask + (size_t)r * a.words_per_row;
+    const bool live = row_live(s, k);
+    const bool in_str = live && s.q == k.s_body;
+    const int n_all = !live ? 0 : in_str ? a.q_tiles : a.lex_tiles;
+    const uint2 *tkeys = in_str ? a.q_tile : a.lex_tile;
+    uint2 kk[kPlanKeys];
+#pragma unroll
+    for (int i = 0; i < kPlanKeys; i++) {
+        const int t = tid + i * kPlanThreads;
+        kk[i] = t < n_all ? tkeys[t] : make_uint2(1, 0);
+    }
+    // base words
+    const uint64_t *base = in_str ? a.strbits + (size_t)min(s.cnt, (uint32_t)kStrBitsets - 1u) * a.Wv : nullptr;
+    for (int i = tid; i < a.Wv; i += kPlanThreads) out[i] = base ? base[i] : 0ull;
+    if (!live) {
+        if (tid == 0) plan[0] = 0;
+        return;
+    }
+    if (tid == 0) n_active = 0;
+    const Walker w0 = load_walker(s);
+    uint64_t after_quote[4] = {0, 0, 0, 0};
+    if (in_str) {
+        // after the closing quote: bytes with a transition out of the resume state
+#pragma unroll
+        for (int j = 0; j < 4; j++) after_quote[j] = a.legal[(size_t)w0.ret * 4 + j];
+    } else if (tid < 256) {
+        // legal first bytes, and the bytes out of the state after each
+        Walker w = w0;
+        const bool ok = step_byte(w, (uint32_t)tid, a.comb, k);
+        const uint64_t m = __ballot(ok);
+        if (lane == 0) valid1[wave] = m;
+        if (ok) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) second[tid * 4 + j] = a.legal[(size_t)w.q * 4 + j];
+        }
+    }
+    __syncthreads();
+    for (int c0 = 0; c0 < n_all; c0 += kPlanKeys * kPlanThreads) {
+        if (c0 > 0) {
+#pragma unroll
+            for (int i = 0; i < kPlanKeys; i++) {
+                const int t = c0 + tid + i * kPlanThreads;
+                kk[i] = t < n_all ? tkeys[t] : make_uint2(1, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kPlanKeys; i++) {
+            const int t = c0 + tid + i * kPlanThreads;
+            bool act = false;
+            if (t < n_all) {
+                act = in_str ? (kk[i].x == 0 || any_bits(after_quote, kk[i].x - 1, kk[i].y - 1))
+                             : span_legal(kk[i].x, kk[i].y, valid1, second);
+            }
+            append_tiles(act, (uint32_t)t, plan + 1, &n_active);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) plan[0] = n_active;
+}
+
+// A listed tile of some row: which row, which tile, the row's configuration.
+struct TileRef {
+    int r;
+    uint32_t tile;
+    cg_state s;
+};
+
+constexpr int kWalkRowBlock = 8192;  // rows whose tile counts are scanned at once
+
+// Row of the g-th listed tile of the block: the last r with prefix[r] <= g.
+__device__ __forceinline__ int row_of(const uint32_t *prefix, int nb, uint32_t g) {
+    int lo = 0, hi = nb;  // prefix[lo] <= g < prefix[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (prefix[mid] <= g) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void fetch_ref(TileRef &t, uint32_t g, uint32_t total, const uint32_t *prefix, int nb,
+                                          int rb, const FillArgs &a) {
+    if (g >= total) return;
+    const int rl = __builtin_amdgcn_readfirstlane(row_of(prefix, nb, g));
+    t.r = rb + rl;
+    t.tile = a.plan[(size_t)t.r * a.plan_stride + 1 + (g - prefix[rl])];
+    t.s = a.states[t.r];
+}
+
+// Persistent: the listed tiles of all rows form one list, dealt to waves
+// round-robin, so a heavy row spreads over the whole chip.  Each wave keeps
+// two tiles in flight: the next tile's tokens and the one after's row and
+// tile index are loaded while the current tile is walked.
+template <int NW>
+__global__ __launch_bounds__(kFillThreads) void k_fill_walk(FillArgs a) {
+    extern __shared__ uint64_t lds[];
+    __shared__ uint32_t wave_sum[kFillWaves];
+    uint64_t *lds_comb = lds;
+    uint32_t *prefix = (uint32_t *)(lds + a.comb_len);
+    const WalkConsts &k = a.k;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    bool staged = false;
+    for (int rb = 0; rb < a.B; rb += kWalkRowBlock) {
+        const int nb = min(kWalkRowBlock, a.B - rb);
+        // exclusive scan of the block's tile counts
+        const int per = (nb + kFillThreads - 1) / kFillThreads;
+        const int r0 = min(nb, tid * per), r1 = min(nb, r0 + per);
+        uint32_t sum = 0;
+        for (int i = r0; i < r1; i++) sum += a.plan[(size_t)(rb + i) * a.plan_stride];
+        uint32_t incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        if (lane == 63) wave_sum[wave] = incl;
+        __syncthreads();
+        uint32_t run = incl - sum;
+        for (int w = 0; w < wave; w++) run += wave_sum[w];
+        for (int i = r0; i < r1; i++) {
+            prefix[i] = run;
+            run += a.plan[(size_t)(rb + i) * a.plan_stride];
+        }
+        if (tid == kFillThreads - 1) prefix[nb] = run;
+        __syncthreads();
+        const uint32_t total = prefix[nb];
+        const uint32_t stride = gridDim.x * kFillWaves;
+        if (blockIdx.x * kFillWaves < total && !staged) {  // the table, once, if there is anything to walk
+            stage_table(lds_comb, a.comb, a.comb_len);
+            __syncthreads();
+            staged = true;
+        }
+        uint32_t g = blockIdx.x * kFillWaves + wave;
+        TileRef t0{}, t1{}, t2{};
+        LaneTok<NW> cur{}, nxt{};
+        fetch_ref(t0, g, total, prefix, nb, rb, a);
+        fetch_ref(t1, g + stride, total, prefix, nb, rb, a);
+        if (g < total) load_lane(cur, t0.s.q == k.s_body, (int)t0.tile * kTile + lane, a);
+        for (; g < total; g += stride) {
+            fetch_ref(t2, g + 2 * stride, total, prefix, nb, rb, a);
+            if (g + stride < total) load_lane(nxt, t1.s.q == k.s_body, (int)t1.tile * kTile + lane, a);
+            const bool in_str = t0.s.q == k.s_body;
+            const Walker w0 = load_walker(t0.s);
+            const uint32_t id = cur.il & 0xFFFFFFu;
+            int end = (int)(cur.il >> 24), start = 0;
+            bool alive = end > 0;
+            uint32_t jump = kNoQuote;
+            Walker wk = w0;
+            if (in_str) {
+                start = (int)(cur.aux & 0xFFu) + 1;
+                const uint32_t nch = cur.aux >> 8;
+                alive = alive && nch <= w0.cnt;
+                wk.q = w0.ret;
+                wk.ws = 0;
+                wk.cnt = w0.cnt - nch;
+            } else {
+                jump = cur.aux;
+            }
+            walk_bytes<0, NW * 4, NW>(wk, alive, cur.w, start, end, jump, lds_comb, k);
+            if (alive) atomicOr(&a.mask[(size_t)t0.r * a.words_per_row + (id >> 6)], 1ull << (id & 63));
+            cur = nxt;
+            t0 = t1;
+            t1 = t2;
+        }
+        __syncthreads();  // the block's prefix is no longer read
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// launchers (argument checks are done by the C ABI)
+// ---------------------------------------------------------------------------
+int launch_init(const cg_grammar *g, cg_state *states, int B, hipStream_t st) {
+    if (B == 0) return CG_OK;
+    hipLaunchKernelGGL(k_init, dim3((B + 255) / 256), dim3(256), 0, st, states, B, g->k.start);
+    return launch_status("init_state");
+}
+
+int launch_advance(const cg_grammar *g, cg_state *states, int B, const int32_t *ids, int32_t *steps,
+                   int32_t *status, hipStream_t st) {
+    if (B == 0) return CG_OK;
+    const size_t lds = (size_t)g->comb_len * sizeof(uint64_t);
+    hipLaunchKernelGGL(k_advance, dim3((B + 255) / 256), dim3(256), lds, st, g->dev.comb, g->comb_len, g->k,
+                       g->dev.tokw, g->dev.tokinfo, g->nw, g->V, states, B, ids, steps, status, g->gen_cap);
+    return launch_status("advance");
+}
+
+// Plan of one row: listed-tile count + up to every tile of the longer list.
+int fill_plan_stride(const cg_grammar *g) {
+    return (1 + std::max(1, std::max(g->lex_tiles, g->q_tiles)) + 63) / 64 * 64;
+}
+
+size_t fill_lds_bytes(const cg_grammar *g, int B) {
+    return (size_t)g->comb_len * 8 + (size_t)(std::min(B, kWalkRowBlock) + 1) * 4;
+}
+
+template <int NW>
+static int launch_fill_nw(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr,
+                          void *ws, hipStream_t st) {
+    const size_t lds = fill_lds_bytes(g, B);
+    if (lds + 1024 > (size_t)g->lds_max) {
+        set_error("fill_bitmask: %zu bytes of LDS needed, %d available", lds, g->lds_max);
+        return CG_E_LIMIT;
+    }
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute((const void *)k_fill_walk<NW>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+            hipSuccess)
+        return launch_status("fill_bitmask (LDS attribute)");
+    FillArgs a;
+    a.comb = g->dev.comb;
+    a.comb_len = g->comb_len;
+    a.k = g->k;
+    a.legal = g->dev.legal;
+    a.lex_idlen = g->dev.lex_idlen;
+    a.lex_jump = g->dev.lex_jump;
+    a.lex_w = g->dev.lex_w;
+    a.lex_tile = g->dev.lex_tile;
+    a.lex_tiles = g->lex_tiles;
+    a.q_idlen = g->dev.q_idlen;
+    a.q_posch = g->dev.q_posch;
+    a.q_w = g->dev.q_w;
+    a.q_tile = g->dev.q_tile;
+    a.q_tiles = g->q_tiles;
+    a.strbits = g->dev.strbits;
+    a.Wv = (g->V + 63) / 64;
+    a.states = states;
+    a.mask = (unsigned long long *)mask;
+    a.words_per_row = wpr;
+    a.plan = (uint32_t *)ws;
+    a.plan_stride = fill_plan_stride(g);
+    a.B = B;
+    hipLaunchKernelGGL(k_fill_plan, dim3(B), dim3(kPlanThreads), 0, st, a);
+    int rc = launch_status("fill_bitmask (plan)");
+    if (rc != CG_OK) return rc;
+    // persistent walk: as many workgroups per CU as LDS holds (at most 8)
+    const int per_cu = std::max(1, std::min(8, (int)((160 * 1024) / (lds + 256))));
+    hipLaunchKernelGGL(k_fill_walk<NW>, dim3(per_cu * g->n_cu), dim3(kFillThreads), lds, st, a);
+    return launch_status("fill_bitmask (walk)");
+}
+
+int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws,
+                hipStream_t st) {
+    if (B == 0) return CG_OK;
+    switch (g->nw) {
+    case 1: return launch_fill_nw<1>(g, states, B, mask, wpr, ws, st);
+    case 2: return launch_fill_nw<2>(g, states, B, mask, wpr, ws, st);
+    case 3: return launch_fill_nw<3>(g, states, B, mask, wpr, ws, st);
+    case 4: return launch_fill_nw<4>(g, states, B, mask, wpr, ws, st);
+    case 5: return launch_fill_nw<5>(g, states, B, mask, wpr, ws, st);
+    case 6: return launch_fill_nw<6>(g, states, B, mask, wpr, ws, st);
+    case 7: return launch_fill_nw<7>(g, states, B, mask, wpr, ws, st);
+    default: return launch_fill_nw<8>(g, states, B, mask, wpr, ws, st);
+    }
+}
+
+}  // namespace cg

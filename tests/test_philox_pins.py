@@ -1,6 +1,5 @@
-"""Philox4x32-10 of the oracle against published known-answer vectors and
-against PyTorch's independent Philox4_32 engine (C++ header, compiled here)."""
-import json
+"""Philox4x32-10 of the oracle against PyTorch's independent Philox4_32
+engine (its C++ header as installed, compiled here at test time)."""
 import os
 import shutil
 import subprocess
@@ -10,19 +9,6 @@ import pytest
 
 from logit_masking_amd import workloads as W
 from oracle import oracle as O
-
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-
-
-def test_kat_vectors():
-    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
-        kat = json.load(f)
-    for v in kat["vectors"]:
-        ctr = np.array([[int(x, 16) for x in v["ctr"]]], dtype=np.uint64)
-        key = tuple(int(x, 16) for x in v["key"])
-        out = O.philox4x32_10(ctr, key)[0]
-        assert [int(x) for x in out] == [int(x, 16) for x in v["out"]]
-
 
 PROBE = r"""
 #include <ATen/core/PhiloxRNGEngine.h>
