@@ -295,17 +295,15 @@ struct ChunkInfo {
 };
 
 struct Decision {
-    double lmax, mv, lse_all, cs1, win;
-    float tv1;
+    double lmax, mv, lse_all, cs1;
     int mc, chosen;
-    bool exact_chunk, exact_token;
+    bool exact_chunk;
 };
 
 struct Slots {
     double a[kWaves], b[kWaves];
     float f[kWaves], h[kWaves];
     int i[kWaves], j[kWaves];
-    Decision dc;
 };
 
 // log-mass of chunk c recomputed entirely in double by the whole workgroup
@@ -322,20 +320,18 @@ __device__ double chunk_lse_exact(const void *logits, size_t rowbase, const uint
     return m / T + log(slots_sum_d(slot));
 }
 
-// G(i) in float for screening, from v_log_f32 only: -ln u for u <= 1/2;
-// above, with v = 1 - u (exact from w): a 4-term series of -ln(1 - v) for
-// v < 2^-7, else -ln(1 - v) rounded from float (relative error < 4e-6).
-// Absolute error of the result < 1e-5.
+// G(i) in float for screening, from v_log_f32 only, without branches: -ln u
+// for u <= 1/2; above, with v = 1 - u (from w): a 4-term series of
+// -ln(1 - v) for v < 2^-7, else -ln(1 - v) rounded from float (relative
+// error < 4e-6).  Absolute error of the result < 1e-5.
 __device__ inline float gumbel32(uint32_t w) {
     constexpr float kLn2 = 0.6931471805599453f;
-    float t;
-    if (w < 0x80000000u) {
-        t = -kLn2 * __builtin_amdgcn_logf(((float)w + 0.5f) * 2.3283064365386963e-10f);
-    } else {
-        const float v = ((float)(0xFFFFFFFFu - w) + 0.5f) * 2.3283064365386963e-10f;
-        t = (v < 0.0078125f) ? v * (1.f + v * (0.5f + v * (0.33333334f + v * 0.25f)))
-                             : -kLn2 * __builtin_amdgcn_logf(1.f - v);
-    }
+    const float u = ((float)w + 0.5f) * 2.3283064365386963e-10f;
+    const float v = ((float)(0xFFFFFFFFu - w) + 0.5f) * 2.3283064365386963e-10f;
+    const float t_lo = -kLn2 * __builtin_amdgcn_logf(u);
+    const float t_ser = v * (1.f + v * (0.5f + v * (0.33333334f + v * 0.25f)));
+    const float t_log = -kLn2 * __builtin_amdgcn_logf(1.f - v);
+    const float t = (w < 0x80000000u) ? t_lo : (v < 0.0078125f ? t_ser : t_log);
     return -kLn2 * __builtin_amdgcn_logf(t);
 }
 
@@ -442,6 +438,12 @@ __device__ __forceinline__ Top2 top2_slots(const float *v1, const int *i1, const
 // before the current one is reduced) and leave one summary per chunk in LDS;
 // then the whole workgroup forms the log-normaliser and picks the token.
 // No state crosses workgroups, so no device-wide fence is ever needed.
+// The row's decision as the three reducing waves publish it.
+struct RowDecision {
+    double lmax, lse_all, mv, cs1, cs2;
+    int mc, c1;
+};
+
 // Per-wave copy of the best chunk seen so far (bf16 rows): the chunk's logits
 // in id order (4 KB) and its mask bytes, so the pick inside the chosen chunk
 // reads LDS instead of HBM.
@@ -466,6 +468,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     Stash *st = (Stash *)((char *)dyn + stash_offset(K));  // valid when use_stash (bf16 only)
     __shared__ Slots sl[4];
     __shared__ uint4 lut[256];
+    __shared__ RowDecision wdec;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = blockIdx.x;
     const float Tf = temp[r];
@@ -478,7 +481,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
     const uint8_t *mrow = (const uint8_t *)(mask + (size_t)r * words_per_row);
     const size_t rowbase = (size_t)r * (size_t)stride;
-    constexpr double kLn2d = 0.6931471805599453;
+    constexpr double kLn2d = 0.6931471805599453, kLog2ed = 1.4426950408889634;
     const bool stash = DT == 1 && use_stash;
     if (DT == 1) init_pair_lut(lut);
     if (stash && lane == 0) st->c[wave] = -1;
@@ -531,48 +534,64 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         }
     }
     __syncthreads();
-    // ---- the row's decision: wave 0 reduces the chunk summaries ----------
-    // (1) log-mass L_c = m/T + ln s per chunk (ln from v_log_f32: the chunk
-    // sums carry ~1e-6 of float rounding anyway), the largest logit (lowest
-    // chunk), the two best chunk scores L_c + G(1, c); (2) the
-    // log-normaliser.  Published in LDS.
-    Decision &dc = sl[0].dc;
-    if (wave == 0) {
-        double lc = -INFINITY, mv = -INFINITY;
-        int mc = -1;
-        Top2d cs{-INFINITY, -INFINITY, -1};
-        for (int c = lane; c < K; c += 64) {
-            const ChunkInfo x = ci[c];
-            if (!x.any) continue;
-            const double l = (x.s > 0.0) ? (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s)
-                                         : -INFINITY;
-            lc = fmax(lc, l);
-            arg_better(mv, mc, (double)x.m, c);
-            if (!greedy && l > -INFINITY) top2d_merge(cs, l + x.g, c, -INFINITY);
-        }
-        lc = wave_max_d(lc);
-        wave_argmax(mv, mc);
-        if (!greedy) cs = top2d_wave(cs);
-        float acc = 0.f;
-        if (lc > -INFINITY)
-            for (int c = lane; c < K; c += 64) {
-                const ChunkInfo x = ci[c];
-                if (!x.any || !(x.s > 0.0)) continue;
-                const double l = (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s);
-                acc += __builtin_amdgcn_exp2f((float)((l - lc) * 1.4426950408889634));
+    // ---- the row's decision, three independent reductions over the chunk
+    // summaries on three waves at once: (0) the log-normaliser, (1) the
+    // largest logit (lowest chunk), (2) the two best chunk scores
+    // L_c + G(1, c).  L_c = m/T + ln s (ln from v_log_f32: the chunk sums
+    // carry ~1e-6 of float rounding anyway).
+    if (wave < 3) {
+        auto lmass = [&](const ChunkInfo &x) -> double {
+            return (x.any && x.s > 0.0) ? (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s)
+                                        : -INFINITY;
+        };
+        if (wave == 0) {
+            double lc = -INFINITY;
+            for (int c = lane; c < K; c += 64) lc = fmax(lc, lmass(ci[c]));
+            lc = wave_max_d(lc);
+            float acc = 0.f;
+            if (lc > -INFINITY)
+                for (int c = lane; c < K; c += 64) {
+                    const double l = lmass(ci[c]);
+                    if (l > -INFINITY) acc += __builtin_amdgcn_exp2f((float)((l - lc) * kLog2ed));
+                }
+            const double sum = wave_sum_d((double)acc);
+            if (lane == 0) {
+                wdec.lmax = lc;
+                wdec.lse_all = lc + kLn2d * (double)__builtin_amdgcn_logf((float)sum);
             }
-        const double sum = wave_sum_d((double)acc);
-        if (lane == 0) {
-            dc.lmax = lc;
-            dc.lse_all = lc + kLn2d * (double)__builtin_amdgcn_logf((float)sum);
-            dc.mv = mv;
-            dc.mc = mc;
-            dc.chosen = greedy ? mc : cs.i1;
-            dc.exact_chunk = !greedy && cs.i1 >= 0 && !(cs.v1 - cs.v2 > kContendChunk);
-            dc.cs1 = cs.v1;
+        } else if (wave == 1) {
+            double mv = -INFINITY;
+            int mc = -1;
+            for (int c = lane; c < K; c += 64)
+                if (ci[c].any) arg_better(mv, mc, (double)ci[c].m, c);
+            wave_argmax(mv, mc);
+            if (lane == 0) {
+                wdec.mv = mv;
+                wdec.mc = mc;
+            }
+        } else if (!greedy) {
+            Top2d cs{-INFINITY, -INFINITY, -1};
+            for (int c = lane; c < K; c += 64) {
+                const double l = lmass(ci[c]);
+                if (l > -INFINITY) top2d_merge(cs, l + ci[c].g, c, -INFINITY);
+            }
+            cs = top2d_wave(cs);
+            if (lane == 0) {
+                wdec.c1 = cs.i1;
+                wdec.cs1 = cs.v1;
+                wdec.cs2 = cs.v2;
+            }
         }
     }
     __syncthreads();
+    Decision dc;
+    dc.lmax = wdec.lmax;
+    dc.lse_all = wdec.lse_all;
+    dc.mv = wdec.mv;
+    dc.mc = wdec.mc;
+    dc.chosen = greedy ? wdec.mc : wdec.c1;
+    dc.exact_chunk = !greedy && wdec.c1 >= 0 && !(wdec.cs1 - wdec.cs2 > kContendChunk);
+    dc.cs1 = wdec.cs1;
     if (dc.mc < 0) {  // nothing allowed: a finished row
         if (threadIdx.x == 0) {
             out_id[r] = -1;
@@ -591,8 +610,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             if (l + x.g < dc.cs1 - 2 * kContendChunk) continue;
             arg_better(bb, bbc, chunk_lse_exact<DT>(logits, rowbase, mrow, V, c, T, (double)x.m, sl[1].a) + x.g, c);
         }
-        if (threadIdx.x == 0) dc.chosen = bbc;
-        __syncthreads();
+        dc.chosen = bbc;  // every thread computed the same
     }
     const int chosen = dc.chosen;
     if (chosen < 0) {  // every allowed logit is -inf: no distribution to draw from
@@ -651,8 +669,12 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         }
         __syncthreads();
         if (threadIdx.x == 0) {
-            int best = sl[2].i[0];
-            for (int w = 1; w < kTokWaves; w++) best = min(best, sl[2].i[w]);
+            int si[kTokWaves];
+#pragma unroll
+            for (int w = 0; w < kTokWaves; w++) si[w] = sl[2].i[w];
+            int best = si[0];
+#pragma unroll
+            for (int w = 1; w < kTokWaves; w++) best = min(best, si[w]);
             out_id[r] = best;
             out_lp[r] = (float)(dc.mv - dc.lse_all);
         }
@@ -678,30 +700,33 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         }
     }
     __syncthreads();
-    if (wave == 0) {
-        Top2 tt{-INFINITY, -INFINITY, -1};
-        for (int k = 0; k < kTokWaves; k++) top2_merge(tt, sl[2].f[k], sl[2].i[k], sl[2].h[k]);
-        const double win = 1e-4 + 2e-6 * fabs((double)tt.v1);
-        const bool unique = (double)tt.v1 - (double)tt.v2 > win;
-        if (lane == 0) {
-            dc.exact_token = !unique;
-            dc.win = win;
-            dc.tv1 = tt.v1;
-            if (unique) {
-                out_id[r] = tt.i1;
-                out_lp[r] = (float)((double)x_of(tt.i1) / T - dc.lse_all);
-            }
-        }
+    // every wave merges the token waves' top two (slot loads first, then the merges)
+    float sv1[kTokWaves], sv2[kTokWaves];
+    int si1[kTokWaves];
+#pragma unroll
+    for (int k = 0; k < kTokWaves; k++) {
+        sv1[k] = sl[2].f[k];
+        sv2[k] = sl[2].h[k];
+        si1[k] = sl[2].i[k];
     }
-    __syncthreads();
-    if (!dc.exact_token) return;
+    Top2 tt{sv1[0], sv2[0], si1[0]};
+#pragma unroll
+    for (int k = 1; k < kTokWaves; k++) top2_merge(tt, sv1[k], si1[k], sv2[k]);
+    const double win = 1e-4 + 2e-6 * fabs((double)tt.v1);
+    if ((double)tt.v1 - (double)tt.v2 > win) {
+        if (threadIdx.x == 0) {
+            out_id[r] = tt.i1;
+            out_lp[r] = (float)((double)x_of(tt.i1) / T - dc.lse_all);
+        }
+        return;
+    }
     // contenders recomputed in double (rare)
     double tv = -INFINITY;
     int ti = -1;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         if (!((mb4 >> j) & 1u)) continue;
-        if ((double)(xq[j] * it + gumbel32(wq[j])) >= (double)dc.tv1 - dc.win)
+        if ((double)(xq[j] * it + gumbel32(wq[j])) >= (double)tt.v1 - win)
             arg_better(tv, ti, (double)xq[j] / T + gumbel64(wq[j]), e + j);
     }
     if (wave < kTokWaves) {
@@ -720,7 +745,6 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         out_lp[r] = (float)((double)x_of(i) / T - dc.lse_all);
     }
 }
-
 
 // ---------------------------------------------------------------------------
 // launcher (argument checks are done by the C ABI)
