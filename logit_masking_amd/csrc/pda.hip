@@ -154,8 +154,8 @@ __global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ co
 //                 token's first quote jumps over the string content with the
 //                 token's precomputed summary of the bytes after that quote.
 //                 Accepted tokens are OR-ed into the mask with 64-bit atomics.
-constexpr int kFillThreads = 256;
-constexpr int kFillWaves = kFillThreads / 64;
+constexpr int kWalkThreads = 1024;  // one walk workgroup per CU
+constexpr int kWalkWaves = kWalkThreads / 64;
 
 __device__ __forceinline__ bool row_live(const cg_state &s, const WalkConsts &k) {
     return !(s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) && s.q < k.q_limit && s.ret < k.q_limit;
@@ -397,21 +397,27 @@ __device__ __forceinline__ void fetch_ref(TileRef &t, uint32_t g, uint32_t total
 // two tiles in flight: the next tile's tokens and the one after's row and
 // tile index are loaded while the current tile is walked.
 template <int NW>
-__global__ __launch_bounds__(kFillThreads) void k_fill_walk(FillArgs a) {
+__global__ __launch_bounds__(kWalkThreads) void k_fill_walk(FillArgs a) {
     extern __shared__ uint64_t lds[];
-    __shared__ uint32_t wave_sum[kFillWaves];
+    __shared__ uint32_t wave_sum[kWalkWaves];
     uint64_t *lds_comb = lds;
     uint32_t *prefix = (uint32_t *)(lds + a.comb_len);
     const WalkConsts &k = a.k;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    bool staged = false;
+    // the table is staged while the first block's tile counts are scanned
+    // (nearly every workgroup has tiles to walk)
+    stage_table(lds_comb, a.comb, a.comb_len);
     for (int rb = 0; rb < a.B; rb += kWalkRowBlock) {
         const int nb = min(kWalkRowBlock, a.B - rb);
         // exclusive scan of the block's tile counts
-        const int per = (nb + kFillThreads - 1) / kFillThreads;
+        const int per = (nb + kWalkThreads - 1) / kWalkThreads;
         const int r0 = min(nb, tid * per), r1 = min(nb, r0 + per);
         uint32_t sum = 0;
-        for (int i = r0; i < r1; i++) sum += a.plan[(size_t)(rb + i) * a.plan_stride];
+        for (int i = r0; i < r1; i++) {
+            const uint32_t n = a.plan[(size_t)(rb + i) * a.plan_stride];
+            prefix[i] = n;  // the count, until the scan below replaces it
+            sum += n;
+        }
         uint32_t incl = sum;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -423,19 +429,15 @@ __global__ __launch_bounds__(kFillThreads) void k_fill_walk(FillArgs a) {
         uint32_t run = incl - sum;
         for (int w = 0; w < wave; w++) run += wave_sum[w];
         for (int i = r0; i < r1; i++) {
+            const uint32_t n = prefix[i];
             prefix[i] = run;
-            run += a.plan[(size_t)(rb + i) * a.plan_stride];
+            run += n;
         }
-        if (tid == kFillThreads - 1) prefix[nb] = run;
+        if (tid == kWalkThreads - 1) prefix[nb] = run;
         __syncthreads();
         const uint32_t total = prefix[nb];
-        const uint32_t stride = gridDim.x * kFillWaves;
-        if (blockIdx.x * kFillWaves < total && !staged) {  // the table, once, if there is anything to walk
-            stage_table(lds_comb, a.comb, a.comb_len);
-            __syncthreads();
-            staged = true;
-        }
-        uint32_t g = blockIdx.x * kFillWaves + wave;
+        const uint32_t stride = gridDim.x * kWalkWaves;
+        uint32_t g = blockIdx.x * kWalkWaves + wave;
         TileRef t0{}, t1{}, t2{};
         LaneTok<NW> cur{}, nxt{};
         fetch_ref(t0, g, total, prefix, nb, rb, a);
@@ -537,9 +539,8 @@ static int launch_fill_nw(const cg_grammar *g, const cg_state *states, int B, ui
     hipLaunchKernelGGL(k_fill_plan, dim3(B), dim3(kPlanThreads), 0, st, a);
     int rc = launch_status("fill_bitmask (plan)");
     if (rc != CG_OK) return rc;
-    // persistent walk: as many workgroups per CU as LDS holds (at most 8)
-    const int per_cu = std::max(1, std::min(8, (int)((160 * 1024) / (lds + 256))));
-    hipLaunchKernelGGL(k_fill_walk<NW>, dim3(per_cu * g->n_cu), dim3(kFillThreads), lds, st, a);
+    // persistent walk: one 16-wave workgroup per CU
+    hipLaunchKernelGGL(k_fill_walk<NW>, dim3(g->n_cu), dim3(kWalkThreads), lds, st, a);
     return launch_status("fill_bitmask (walk)");
 }
 
