@@ -1,7 +1,8 @@
 """Benchmark of the constrained-decoding hot path on one MI355X.
 
-A step is one pass of the whole path over the batch: fill_bitmask ->
-apply_mask_sample -> advance.  Workload: the tool-call grammar (8 tools),
+A step is one pass of the whole path over the batch: fill_bitmask, then
+mask_softmax_sample + advance in one launch (cg_sample_advance; --separate
+runs cg_apply_mask_sample and cg_advance as two launches).  Workload: the tool-call grammar (8 tools),
 vocabulary 128,256, batch 256, bf16 N(0, 3^2) logits, T = 0.7 Philox
 Gumbel sampling, a 256-step trajectory from the start state (the 256-token
 bench cap of "Constrained decoding", "What it is worth"), engine cap 2048.
@@ -111,6 +112,8 @@ def main():
     ap.add_argument("--pool", type=int, default=64, help="distinct logits buffers cycled over the steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="cg_apply_mask_sample and cg_advance as two launches instead of cg_sample_advance")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 64 MiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -154,10 +157,16 @@ def main():
         g.fill_bitmask(st, mask, fws, stream)
         if ev is not None:
             ev[1].record(stream)
-        cg.apply_mask_sample(pool[s % npool], mask, temp, seed, steps, ws, ids, lp, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        g.advance(st, ids, steps, status, stream)
+        if args.separate:
+            cg.apply_mask_sample(pool[s % npool], mask, temp, seed, steps, ws, ids, lp, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+            g.advance(st, ids, steps, status, stream)
+        else:
+            # mask_softmax_sample + advance in one launch
+            g.sample_advance(pool[s % npool], mask, temp, seed, steps, ws, ids, lp, st, status, stream)
+            if ev is not None:
+                ev[2].record(stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -195,13 +204,16 @@ def main():
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     assert np.array_equal(steps.cpu().numpy(), st_h), "replay diverged from the timed trajectory"
 
-    # masked sample: every logit (bf16) and mask word read once, id + logprob written
+    # masked sample: every logit (bf16) and mask word read once, id + logprob
+    # written; fused, also each row's state, step and status
     sample_bytes = B * V * 2 + B * g.W * 8 + B * 8
+    if not args.separate:
+        sample_bytes += B * (2 * 24 + 2 * 4 + 4)
     sample_gbps = sample_bytes / (samp_ms.mean() * 1e-3) / 1e9
     fill_checks = B * V / (fill_ms.mean() * 1e-3)
     dominant = "fill_bitmask" if fill_ms.mean() >= samp_ms.mean() else "mask_softmax_sample"
     roofline = {
-        "kernel": "k_sample (mask_softmax_sample)",
+        "kernel": "k_sample (mask_softmax_sample" + (")" if args.separate else " + advance, one launch)"),
         "bound": "hbm",
         "achieved": round(sample_gbps, 1),
         "peak": HBM_PEAK_GBPS,
@@ -234,7 +246,7 @@ def main():
                     "p99": round(1e3 * pct(fill_ms, 99), 2)},
         "us_sample": {"mean": round(1e3 * samp_ms.mean(), 2), "p50": round(1e3 * pct(samp_ms, 50), 2),
                       "p99": round(1e3 * pct(samp_ms, 99), 2)},
-        "us_advance": {"mean": round(1e3 * adv_ms.mean(), 2)},
+        "us_advance": {"mean": round(1e3 * adv_ms.mean(), 2)} if args.separate else "fused into us_sample",
         "wall_us_per_step": round(1e6 * wall / args.steps, 2),
         "dominant_kernel": dominant,
         "rows_done": int((flags & 1).sum()),

@@ -13,6 +13,7 @@
  *   cg_fill_bitmask      packed token bitmask per row (device)
  *   cg_apply_mask_sample masked softmax + greedy / Gumbel-max pick (device)
  *   cg_advance           walk the chosen tokens, update rows (device)
+ *   cg_sample_advance    the last two in one launch (device)
  *   cg_try_input         where a candidate string is refused (host)
  *
  * Conventions
@@ -196,6 +197,21 @@ int cg_apply_mask_sample(const void *d_logits, int32_t dtype, int32_t batch, int
                          const uint64_t *d_mask, int32_t words_per_row, const float *d_temperature,
                          const uint64_t *d_seed, const int32_t *d_step, void *d_workspace, int32_t *d_out_ids,
                          float *d_out_logprob, void *stream);
+
+/*
+ * cg_apply_mask_sample followed by cg_advance on the picked ids, in one launch:
+ * the same picks, log-probabilities, states, steps and statuses as the two
+ * calls in sequence (vocab = the grammar's vocabulary).  d_step is read by
+ * the sampler (Philox counter) and then incremented for accepted tokens.
+ * The workgroup that picks a row's token also walks it, so the chosen id
+ * never round-trips through memory between the two steps ("Constrained
+ * decoding", "The guarantee": sampling runs after masking, and the sampled
+ * token is the automaton's next transition).
+ */
+int cg_sample_advance(const cg_grammar *g, const void *d_logits, int32_t dtype, int32_t batch, int64_t row_stride,
+                      const uint64_t *d_mask, int32_t words_per_row, const float *d_temperature,
+                      const uint64_t *d_seed, int32_t *d_step, void *d_workspace, int32_t *d_out_ids,
+                      float *d_out_logprob, cg_state *d_states, int32_t *d_status, void *stream);
 
 /*
  * Walk d_token_ids[r] for every row: -1 is a no-op (CG_ROW_NOOP).  A token

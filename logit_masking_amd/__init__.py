@@ -21,7 +21,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # Symbols the C ABI (include/cg.h) exports.
 EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
-           "cg_fill_bitmask",
+           "cg_fill_bitmask", "cg_sample_advance",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
 
 
@@ -66,9 +66,10 @@ def lib():
         L.cg_sample_workspace_bytes.restype = sz
         L.cg_apply_mask_sample.argtypes = [vp, i32, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.cg_advance.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.cg_sample_advance.argtypes = [vp, vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
         L.cg_last_error.restype = ctypes.c_char_p
-        for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask",
+        for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask", "cg_sample_advance",
                      "cg_apply_mask_sample", "cg_advance", "cg_try_input"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -174,6 +175,37 @@ class Grammar:
             raise ValueError("fill workspace too small")
         _check(lib().cg_fill_bitmask(self._h, _ptr(states), B, _ptr(mask), mask.shape[1], _ptr(workspace),
                                      _stream(stream)))
+
+    def sample_advance(self, logits, mask, temperature, seed, steps, workspace, out_ids, out_logprob, states,
+                       status, stream=None):
+        """cg_sample_advance: apply_mask_sample + advance in one launch (same
+        tensors and meanings as those two calls; steps is read, then bumped)."""
+        import torch
+        if logits.dtype == torch.float32:
+            dt = DTYPE_F32
+        elif logits.dtype == torch.bfloat16:
+            dt = DTYPE_BF16
+        else:
+            raise ValueError("logits must be float32 or bfloat16")
+        if not logits.is_cuda or logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[1] < self.V:
+            raise ValueError("logits must be a 2-D device tensor [B, >= vocab] with unit column stride")
+        B = logits.shape[0]
+        _dev(mask, torch.int64, "mask", 2)
+        _dev(temperature, torch.float32, "temperature", 1)
+        _dev(seed, torch.int64, "seed", 1)
+        _dev(states, torch.uint8, "states", 2)
+        for t, n in ((steps, "steps"), (out_ids, "out_ids"), (status, "status")):
+            _dev(t, torch.int32, n, 1)
+        _dev(out_logprob, torch.float32, "out_logprob", 1)
+        if workspace.numel() * workspace.element_size() < sample_workspace_bytes(B, self.V):
+            raise ValueError("workspace too small")
+        for t, n in ((mask, "mask"), (temperature, "temperature"), (seed, "seed"), (steps, "steps"),
+                     (out_ids, "out_ids"), (out_logprob, "out_logprob"), (states, "states"), (status, "status")):
+            if t.shape[0] < B:
+                raise ValueError(f"{n} has fewer rows than logits")
+        _check(lib().cg_sample_advance(self._h, _ptr(logits), dt, B, logits.stride(0), _ptr(mask), mask.shape[1],
+                                       _ptr(temperature), _ptr(seed), _ptr(steps), _ptr(workspace), _ptr(out_ids),
+                                       _ptr(out_logprob), _ptr(states), _ptr(status), _stream(stream)))
 
     def advance(self, states, ids, steps, status, stream=None):
         import torch

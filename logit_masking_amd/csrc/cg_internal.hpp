@@ -115,6 +115,62 @@ __host__ __device__ inline bool step_byte(Walker &w, uint32_t b, const uint64_t 
     return ok;
 }
 
+// Copy n table slots to LDS with up to 16 loads per thread in flight before
+// the first store (a plain load/store loop waits out one round trip per slot).
+__device__ inline void stage_table(uint64_t *dst, const uint64_t *__restrict__ src, uint32_t n) {
+    constexpr int kInFlight = 16;
+    for (uint32_t base = 0; base < n; base += kInFlight * blockDim.x) {
+        uint64_t v[kInFlight];
+#pragma unroll
+        for (int j = 0; j < kInFlight; j++) {
+            const uint32_t i = base + j * blockDim.x + threadIdx.x;
+            v[j] = i < n ? src[i] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < kInFlight; j++) {
+            const uint32_t i = base + j * blockDim.x + threadIdx.x;
+            if (i < n) dst[i] = v[j];
+        }
+    }
+}
+
+// Commit token `id` (its n bytes in words[], 4 per word) to a row: the
+// cg_advance rules.  -1 is a no-op; an id out of range, a finished row or a
+// refused byte leaves the row unchanged (REJECTED); otherwise the row takes
+// the walked configuration, step + 1, and DONE / CAPPED flags.  Returns the
+// status; `s` and `step` are updated only when the token is accepted.
+__host__ __device__ inline int commit_token(cg_state &s, int &step, int id, int V, uint32_t n,
+                                            const uint32_t (&words)[kMaxTokenLen / 4], const uint64_t *comb,
+                                            const WalkConsts &k, uint32_t gen_cap) {
+    if (id < 0) return CG_ROW_NOOP;
+    if (id >= V || (s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) || s.q >= k.q_limit || s.ret >= k.q_limit)
+        return CG_ROW_REJECTED;
+    Walker w = load_walker(s);
+    bool ok = n > 0;
+#pragma unroll
+    for (int i = 0; i < kMaxTokenLen; i++) {  // unrolled: the word index is a constant
+        if (!ok || (uint32_t)i >= n) break;
+        ok = step_byte(w, (words[i >> 2] >> (8 * (i & 3))) & 0xFFu, comb, k);
+    }
+    if (!ok) return CG_ROW_REJECTED;
+    store_walker(s, w);
+    step += 1;
+    int res = CG_ROW_OK;
+    uint8_t fl = 0;
+    if (w.q == k.accept) {
+        fl |= CG_FLAG_DONE;
+        res = CG_ROW_DONE;
+    }
+    if ((uint32_t)step >= gen_cap) {
+        fl |= CG_FLAG_CAPPED;
+        if (res == CG_ROW_OK) res = CG_ROW_CAPPED;
+    }
+    s.flags = fl;
+    s.pad0 = 0;
+    s.pad1 = 0;
+    return res;
+}
+
 // Per-token summary of a walk through a string body that starts at a
 // code-point boundary (state s_body): the body's transitions depend on
 // nothing but the byte and the code-point budget, so one word per token

@@ -38,25 +38,6 @@ __global__ void k_init(cg_state *__restrict__ states, int B, uint32_t start) {
     states[r] = s;
 }
 
-// Copy n table slots to LDS with up to 16 loads per thread in flight before
-// the first store (a plain load/store loop waits out one round trip per slot).
-__device__ __forceinline__ void stage_table(uint64_t *dst, const uint64_t *__restrict__ src, uint32_t n) {
-    constexpr int kInFlight = 16;
-    for (uint32_t base = 0; base < n; base += kInFlight * blockDim.x) {
-        uint64_t v[kInFlight];
-#pragma unroll
-        for (int j = 0; j < kInFlight; j++) {
-            const uint32_t i = base + j * blockDim.x + threadIdx.x;
-            v[j] = i < n ? src[i] : 0ull;
-        }
-#pragma unroll
-        for (int j = 0; j < kInFlight; j++) {
-            const uint32_t i = base + j * blockDim.x + threadIdx.x;
-            if (i < n) dst[i] = v[j];
-        }
-    }
-}
-
 // One lane per row.  The row's id, configuration and token bytes are loaded
 // first, then the transition table is staged in LDS while those loads fly,
 // so the byte walk is a chain of LDS lookups, not of L2 round trips.
@@ -90,40 +71,12 @@ __global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ co
     stage_table(lds_comb, comb, comb_len);
     __syncthreads();
     if (!row) return;
-    if (id < 0) {
-        status[r] = CG_ROW_NOOP;
-        return;
+    int st = st0;
+    const int res = commit_token(s, st, id, V, n, words, lds_comb, k, gen_cap);
+    if (res == CG_ROW_OK || res == CG_ROW_DONE || res == CG_ROW_CAPPED) {
+        states[r] = s;
+        steps[r] = st;
     }
-    if (!valid) {
-        status[r] = CG_ROW_REJECTED;
-        return;
-    }
-    Walker w = load_walker(s);
-    bool ok = n > 0;
-#pragma unroll
-    for (int i = 0; i < kMaxTokenLen; i++) {  // unrolled: the word index is a constant
-        if (!ok || (uint32_t)i >= n) break;
-        ok = step_byte(w, (words[i >> 2] >> (8 * (i & 3))) & 0xFFu, lds_comb, k);
-    }
-    if (!ok) {
-        status[r] = CG_ROW_REJECTED;
-        return;
-    }
-    store_walker(s, w);
-    const int st = st0 + 1;
-    steps[r] = st;
-    int res = CG_ROW_OK;
-    uint8_t fl = 0;
-    if (w.q == k.accept) {
-        fl |= CG_FLAG_DONE;
-        res = CG_ROW_DONE;
-    }
-    if ((uint32_t)st >= gen_cap) {
-        fl |= CG_FLAG_CAPPED;
-        if (res == CG_ROW_OK) res = CG_ROW_CAPPED;
-    }
-    s.flags = fl;
-    states[r] = s;
     status[r] = res;
 }
 

@@ -454,6 +454,22 @@ struct Stash {
     int c[kWaves];
 };
 
+// The grammar side of the fused sample + advance: after the pick, the
+// workgroup's first thread walks the chosen token from the row's
+// configuration (cg_advance's rules) through the table staged in LDS.
+struct AdvanceArgs {
+    const uint64_t *comb;  // null: sample only
+    uint32_t comb_len;
+    uint32_t comb_off;     // byte offset of the staged table in dynamic LDS
+    WalkConsts k;
+    const uint32_t *tokw, *tokinfo;
+    int nw, V;
+    cg_state *states;
+    int32_t *steps;        // the same array as the sampler's step (read first, then bumped)
+    int32_t *status;
+    uint32_t gen_cap;
+};
+
 // byte offset of the stash in dynamic LDS: after the chunk summaries, 16-byte aligned
 __host__ __device__ inline size_t stash_offset(int K) { return ((size_t)K * sizeof(ChunkInfo) + 15) / 16 * 16; }
 
@@ -462,7 +478,8 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
                                                  const uint64_t *__restrict__ mask, int words_per_row,
                                                  const float *__restrict__ temp, const uint64_t *__restrict__ seed,
                                                  const int32_t *__restrict__ step, int K, int use_stash,
-                                                 int32_t *__restrict__ out_id, float *__restrict__ out_lp) {
+                                                 int32_t *__restrict__ out_id, float *__restrict__ out_lp,
+                                                 AdvanceArgs adv) {
     extern __shared__ uint64_t dyn[];
     ChunkInfo *ci = (ChunkInfo *)dyn;
     Stash *st = (Stash *)((char *)dyn + stash_offset(K));  // valid when use_stash (bf16 only)
@@ -485,6 +502,13 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const bool stash = DT == 1 && use_stash;
     if (DT == 1) init_pair_lut(lut);
     if (stash && lane == 0) st->c[wave] = -1;
+    // fused advance: the table is staged while the logits stream
+    const bool fuse = adv.comb != nullptr;
+    uint64_t *lds_comb = (uint64_t *)((char *)dyn + adv.comb_off);
+    if (fuse) stage_table(lds_comb, adv.comb, adv.comb_len);
+    // the pick (thread 0): every exit path below leaves it here
+    int pick = -1;
+    float pick_lp = 0.f;
     {
         // chunks per wave in flight: the one being reduced and the next two
         // (bf16), or the next one (float32, whose chunks take twice the registers)
@@ -592,13 +616,8 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     dc.chosen = greedy ? wdec.mc : wdec.c1;
     dc.exact_chunk = !greedy && wdec.c1 >= 0 && !(wdec.cs1 - wdec.cs2 > kContendChunk);
     dc.cs1 = wdec.cs1;
-    if (dc.mc < 0) {  // nothing allowed: a finished row
-        if (threadIdx.x == 0) {
-            out_id[r] = -1;
-            out_lp[r] = 0.f;
-        }
-        return;
-    }
+    do {
+    if (dc.mc < 0) break;  // nothing allowed: a finished row
     if (dc.exact_chunk) {
         // two chunks within the screening window: decide on exact log-masses (rare)
         double bb = -INFINITY;
@@ -613,13 +632,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         dc.chosen = bbc;  // every thread computed the same
     }
     const int chosen = dc.chosen;
-    if (chosen < 0) {  // every allowed logit is -inf: no distribution to draw from
-        if (threadIdx.x == 0) {
-            out_id[r] = -1;
-            out_lp[r] = 0.f;
-        }
-        return;
-    }
+    if (chosen < 0) break;  // every allowed logit is -inf: no distribution to draw from
     // (3) inside the chunk: threads 0..511 take 4 ids each, e = 4t .. 4t + 3
     // (one Philox block), from the stash of the wave that reduced the chunk,
     // else from HBM
@@ -675,10 +688,10 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             int best = si[0];
 #pragma unroll
             for (int w = 1; w < kTokWaves; w++) best = min(best, si[w]);
-            out_id[r] = best;
-            out_lp[r] = (float)(dc.mv - dc.lse_all);
+            pick = best;
+            pick_lp = (float)(dc.mv - dc.lse_all);
         }
-        return;
+        break;
     }
     // sampled: argmax_i x_i / T + G(0, i) screened in float; the winner is
     // exact unless the best two are within the screening error (x/T rounding
@@ -715,10 +728,10 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const double win = 1e-4 + 2e-6 * fabs((double)tt.v1);
     if ((double)tt.v1 - (double)tt.v2 > win) {
         if (threadIdx.x == 0) {
-            out_id[r] = tt.i1;
-            out_lp[r] = (float)((double)x_of(tt.i1) / T - dc.lse_all);
+            pick = tt.i1;
+            pick_lp = (float)((double)x_of(tt.i1) / T - dc.lse_all);
         }
-        return;
+        break;
     }
     // contenders recomputed in double (rare)
     double tv = -INFINITY;
@@ -741,9 +754,33 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         double v = sl[3].b[0];
         int i = sl[3].j[0];
         for (int k = 1; k < kTokWaves; k++) arg_better(v, i, sl[3].b[k], sl[3].j[k]);
-        out_id[r] = i;
-        out_lp[r] = (float)((double)x_of(i) / T - dc.lse_all);
+        pick = i;
+        pick_lp = (float)((double)x_of(i) / T - dc.lse_all);
     }
+    } while (0);
+    // ---- epilogue: thread 0 publishes the pick and, fused, commits it ---------
+    if (threadIdx.x != 0) return;
+    out_id[r] = pick;
+    out_lp[r] = pick_lp;
+    if (!fuse) return;
+    cg_state row_state = adv.states[r];  // loaded with the token bytes: one round trip
+    uint32_t words[kMaxTokenLen / 4];
+    uint32_t n = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxTokenLen / 4; j++) words[j] = 0;
+    if (pick >= 0 && pick < adv.V) {
+        n = tok_len(adv.tokinfo[pick]);
+#pragma unroll
+        for (int j = 0; j < kMaxTokenLen / 4; j++)
+            if (j < adv.nw) words[j] = adv.tokw[(size_t)j * adv.V + pick];
+    }
+    int stp1 = (int)stp;
+    const int res = commit_token(row_state, stp1, pick, adv.V, n, words, lds_comb, adv.k, adv.gen_cap);
+    if (res == CG_ROW_OK || res == CG_ROW_DONE || res == CG_ROW_CAPPED) {
+        adv.states[r] = row_state;
+        adv.steps[r] = stp1;
+    }
+    adv.status[r] = res;
 }
 
 // ---------------------------------------------------------------------------
@@ -757,7 +794,8 @@ size_t sample_workspace_bytes(int B, int V) {
 
 int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, const uint64_t *mask, int wpr,
                   const float *temp, const uint64_t *seed, const int32_t *step, void *ws, int32_t *out_id,
-                  float *out_lp, hipStream_t st) {
+                  float *out_lp, const cg_grammar *g, cg_state *states, int32_t *steps_rw, int32_t *status,
+                  hipStream_t st) {
     (void)ws;
     if (B == 0) return CG_OK;
     const int K = (V + kChunk - 1) / kChunk;
@@ -766,14 +804,36 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
         set_error("apply_mask_sample: vocab above %d", 48 * 1024 / (int)sizeof(ChunkInfo) * kChunk);
         return CG_E_ARG;
     }
-    // bf16 rows keep each wave's best chunk in LDS when it fits
     int dev = 0, lds_max = 65536;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         lds_max = 65536;
-    const size_t static_lds = 4 * sizeof(Slots) + 256 * sizeof(uint4);
-    const int use_stash = dt == 1 && stash_offset(K) + sizeof(Stash) + static_lds + 256 <= (size_t)lds_max;
-    const size_t lds = use_stash ? stash_offset(K) + sizeof(Stash) : lds_ci;
+    const size_t static_lds = 4 * sizeof(Slots) + 256 * sizeof(uint4) + sizeof(RowDecision) + 256;
+    const size_t table = g ? (size_t)g->comb_len * 8 : 0;
+    // bf16 rows keep each wave's best chunk in LDS when it fits beside the table
+    const int use_stash =
+        dt == 1 && stash_offset(K) + sizeof(Stash) + table + static_lds <= (size_t)lds_max;
+    const size_t base = use_stash ? stash_offset(K) + sizeof(Stash) : (lds_ci + 15) / 16 * 16;
+    const size_t lds = base + table;
+    if (lds + static_lds > (size_t)lds_max) {
+        set_error("sample_advance: %zu bytes of LDS needed, %d available", lds + static_lds, lds_max);
+        return CG_E_LIMIT;
+    }
+    AdvanceArgs adv{};
+    if (g) {
+        adv.comb = g->dev.comb;
+        adv.comb_len = g->comb_len;
+        adv.comb_off = (uint32_t)base;
+        adv.k = g->k;
+        adv.tokw = g->dev.tokw;
+        adv.tokinfo = g->dev.tokinfo;
+        adv.nw = g->nw;
+        adv.V = g->V;
+        adv.states = states;
+        adv.steps = steps_rw;
+        adv.status = status;
+        adv.gen_cap = g->gen_cap;
+    }
     const int es = dt == 0 ? 4 : 2;
     const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * es) % 16 == 0);
 #define CG_LAUNCH_SAMPLE(D, VV)                                                                                  \
@@ -782,7 +842,7 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) \
             return launch_status("apply_mask_sample (LDS attribute)");                                           \
         hipLaunchKernelGGL((k_sample<D, VV>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask, wpr, \
-                           temp, seed, step, K, use_stash, out_id, out_lp);                                      \
+                           temp, seed, step, K, use_stash, out_id, out_lp, adv);                                 \
     } while (0)
     if (dt == 0) {
         if (vec) CG_LAUNCH_SAMPLE(0, true);
@@ -792,7 +852,7 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
         else CG_LAUNCH_SAMPLE(1, false);
     }
 #undef CG_LAUNCH_SAMPLE
-    return launch_status("apply_mask_sample");
+    return launch_status(g ? "sample_advance" : "apply_mask_sample");
 }
 
 }  // namespace cg
