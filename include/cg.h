@@ -14,6 +14,8 @@
  *   cg_apply_mask_sample masked softmax + greedy / Gumbel-max pick (device)
  *   cg_advance           walk the chosen tokens, update rows (device)
  *   cg_sample_advance    the last two in one launch (device)
+ *   cg_force_bytes       engine-written bytes (an evaluated result) (device)
+ *   cg_eval_calc         evaluate a calc span (host)
  *   cg_try_input         where a candidate string is refused (host)
  *
  * Conventions
@@ -47,13 +49,16 @@ extern "C" {
 #define CG_E_LIMIT (-4)       /* automaton or vocabulary beyond a size limit */
 #define CG_E_VOCAB (-5)       /* malformed vocabulary (offsets) */
 #define CG_E_DEVICE (-6)      /* HIP runtime error (allocation, copy, launch) */
+#define CG_E_EVAL (-7)        /* calc span: division by zero, or a value outside int64 */
 
 /* ---- per-row status written by cg_advance --------------------------------- */
 #define CG_ROW_OK 0       /* token accepted, row continues */
 #define CG_ROW_DONE 1     /* token accepted, the row's bytes are now a complete member */
 #define CG_ROW_CAPPED 2   /* token accepted, row reached the generation cap */
 #define CG_ROW_REJECTED 3 /* token refused (illegal, out of range, or row finished); row unchanged */
-#define CG_ROW_NOOP 4     /* token id -1: nothing to do */
+#define CG_ROW_NOOP 4     /* token id -1 (or an empty forced string): nothing to do */
+#define CG_ROW_INJECT 5   /* token accepted; the row now sits in a region the engine writes
+                             (cg_force_bytes): its mask is empty until then */
 
 /* ---- row state flags (cg_state.flags) ------------------------------------- */
 #define CG_FLAG_DONE 1u
@@ -108,6 +113,14 @@ typedef struct {
  *       T := INT | "(" W E W ")", op one of + - * /, INT canonical decimal in
  *       [int_min, int_max] ("Evaluator aware decoding", "This is a grammar
  *       problem");
+ *   {"kind":"calc_text", "int_min":0, "int_max":999, "ws_max":2, "depth_cap":16}
+ *       text with evaluated spans: TEXT* (CALC RESULT TEXT*)* "<end>", TEXT =
+ *       LF or printable ASCII other than '<', CALC the span above, RESULT =
+ *       "<result>" "-"? digit{1,20} "</result>" or "<result_error>" MSG
+ *       "</result_error>" (MSG: printable ASCII other than '<') -- written by
+ *       the engine (cg_force_bytes), never sampled: rows inside it have an
+ *       empty mask ("Evaluator aware decoding", "A concrete prototype on
+ *       llama.cpp");
  *   {"kind":"json_schema", "schema":{...}, settings...}
  *       a JSON value of the schema ("Guided Decoding & Structured-Output
  *       Reliability", "Design 1 -- base schema, validators-first ordering");
@@ -155,7 +168,9 @@ size_t cg_fill_workspace_bytes(const cg_grammar *g, int32_t batch);
  * Packed token bitmask: bit (t & 63) of d_mask[r * words_per_row + (t >> 6)]
  * is 1 iff row r is not finished and the bytes of token t are a legal
  * continuation of the row's bytes (the row's bytes followed by token t can
- * still be completed to a member).  Pad bits past vocab_size are 0.
+ * still be completed to a member) without taking a byte the engine writes
+ * (a token may end where an engine-written region begins, not go into it;
+ * a row inside one gets an all-zero row).  Pad bits past vocab_size are 0.
  * words_per_row must be >= ceil(vocab_size / 64); words beyond that are
  * left untouched.  Depends only on the states, so it may run before the
  * logits exist ("Evaluator aware decoding", "Why isn't this in production
@@ -217,9 +232,10 @@ int cg_sample_advance(const cg_grammar *g, const void *d_logits, int32_t dtype, 
  * Walk d_token_ids[r] for every row: -1 is a no-op (CG_ROW_NOOP).  A token
  * whose bytes continue the row legally is committed: d_step[r] += 1, then
  * the row is DONE if its bytes form a complete member, CAPPED if
- * d_step[r] >= gen_cap.  Otherwise (illegal, id out of range, or the row is
- * already finished) the row is left unchanged and d_status[r] is
- * CG_ROW_REJECTED.  Ids may come from cg_apply_mask_sample or be forced by
+ * d_step[r] >= gen_cap, INJECT if it now sits where the engine writes (see
+ * cg_force_bytes).  Otherwise (illegal, a byte the engine writes, id out of
+ * range, or the row is already finished) the row is left unchanged and
+ * d_status[r] is CG_ROW_REJECTED.  Ids may come from cg_apply_mask_sample or be forced by
  * the caller: a forced token is a transition the model did not choose
  * ("Evaluator aware decoding", "A concrete prototype on llama.cpp").
  * d_step: in/out, tokens accepted so far (the caller zeroes it at start).
@@ -228,11 +244,42 @@ int cg_advance(const cg_grammar *g, cg_state *d_states, int32_t batch, const int
                int32_t *d_status, void *stream);
 
 /*
+ * Walk each row's forced byte string: row r takes
+ * d_bytes[d_offsets[r] .. d_offsets[r+1]) (device memory; d_offsets has
+ * batch+1 entries; an empty string is a no-op, CG_ROW_NOOP).  The engine
+ * writes text the model did not choose -- an evaluated result -- and the
+ * automaton follows: injection is a grammar transition the model did not
+ * choose ("Evaluator aware decoding", "A concrete prototype on llama.cpp").
+ * Engine-written bytes are legal here; text the model may write is too.
+ * All bytes legal: the row takes the walked configuration and d_status[r]
+ * is OK, DONE (a complete member), or INJECT (still inside a region the
+ * engine writes).  A refused byte, or a finished row: CG_ROW_REJECTED, row
+ * unchanged.  Forced bytes are not generation steps: the step counter and
+ * the cap are untouched.  Tokenizing the forced text for the model's own
+ * forward pass is the engine's business; the automaton walks bytes.
+ */
+int cg_force_bytes(const cg_grammar *g, cg_state *d_states, int32_t batch, const uint8_t *d_bytes,
+                   const uint32_t *d_offsets, int32_t *d_status, void *stream);
+
+/*
+ * Host-side evaluator of a calc span ("Evaluator aware decoding", "The core
+ * idea": the engine evaluates the span and writes the result back).  `span`
+ * is "<calc>...</calc>" or the bare expression: integers, + - * /,
+ * parentheses, whitespace; * and / before + and -, left to right, / truncating
+ * toward zero.  CG_OK with *value; CG_E_PARSE for a malformed span;
+ * CG_E_EVAL for division by zero or any literal or intermediate value
+ * outside int64, with cg_last_error() exactly "division by zero" or "out of
+ * range" (text an engine can inject as <result_error>).
+ */
+int cg_eval_calc(const uint8_t *span, size_t len, int64_t *value);
+
+/*
  * Host-side diagnostic: run `bytes` against the automaton from its start.
  * *refused_at = index of the first refused byte (len if none); *complete =
  * 1 iff all bytes were accepted and form a complete member ("Constrained
  * decoding", "Reading the grammar for a tool": try-input says where a
- * candidate would have been refused).
+ * candidate would have been refused).  The whole language is walked,
+ * engine-written regions included.
  */
 int cg_try_input(const cg_grammar *g, const uint8_t *bytes, size_t len, size_t *refused_at, int *complete);
 

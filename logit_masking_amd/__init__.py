@@ -12,8 +12,9 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcg.so")
 
-CG_OK, CG_E_ARG, CG_E_PARSE, CG_E_UNSUPPORTED, CG_E_LIMIT, CG_E_VOCAB, CG_E_DEVICE = 0, -1, -2, -3, -4, -5, -6
-ROW_OK, ROW_DONE, ROW_CAPPED, ROW_REJECTED, ROW_NOOP = 0, 1, 2, 3, 4
+CG_OK, CG_E_ARG, CG_E_PARSE, CG_E_UNSUPPORTED, CG_E_LIMIT, CG_E_VOCAB, CG_E_DEVICE, CG_E_EVAL = \
+    0, -1, -2, -3, -4, -5, -6, -7
+ROW_OK, ROW_DONE, ROW_CAPPED, ROW_REJECTED, ROW_NOOP, ROW_INJECT = 0, 1, 2, 3, 4, 5
 FLAG_DONE, FLAG_CAPPED = 1, 2
 HOST_ONLY = 1
 STATE_BYTES = 24
@@ -21,7 +22,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # Symbols the C ABI (include/cg.h) exports.
 EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
-           "cg_fill_bitmask", "cg_sample_advance",
+           "cg_fill_bitmask", "cg_sample_advance", "cg_force_bytes", "cg_eval_calc",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
 
 
@@ -66,10 +67,13 @@ def lib():
         L.cg_sample_workspace_bytes.restype = sz
         L.cg_apply_mask_sample.argtypes = [vp, i32, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.cg_advance.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.cg_force_bytes.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.cg_eval_calc.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_int64)]
         L.cg_sample_advance.argtypes = [vp, vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
         L.cg_last_error.restype = ctypes.c_char_p
         for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask", "cg_sample_advance",
+                     "cg_force_bytes", "cg_eval_calc",
                      "cg_apply_mask_sample", "cg_advance", "cg_try_input"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -216,6 +220,34 @@ class Grammar:
                 raise ValueError(f"{n} has fewer rows than states")
         _check(lib().cg_advance(self._h, _ptr(states), states.shape[0], _ptr(ids), _ptr(steps), _ptr(status),
                                 _stream(stream)))
+
+    def force_bytes(self, states, data, offsets, status, stream=None):
+        """cg_force_bytes: row r walks data[offsets[r]:offsets[r+1]] (uint8 /
+        int32 device tensors, offsets has B+1 entries)."""
+        import torch
+        _dev(states, torch.uint8, "states", 2)
+        B = states.shape[0]
+        _dev(data, torch.uint8, "data", 1)
+        _dev(offsets, torch.int32, "offsets", 1)
+        if offsets.shape[0] < B + 1:
+            raise ValueError("offsets needs B+1 entries")
+        _dev(status, torch.int32, "status", 1)
+        if status.shape[0] < B:
+            raise ValueError("status has fewer rows than states")
+        _check(lib().cg_force_bytes(self._h, _ptr(states), B, _ptr(data), _ptr(offsets), _ptr(status),
+                                    _stream(stream)))
+
+
+def eval_calc(span: bytes):
+    """cg_eval_calc: (CG_OK, value) or (error code, message)."""
+    if isinstance(span, str):
+        span = span.encode()
+    buf = ctypes.create_string_buffer(span, len(span)) if span else None
+    v = ctypes.c_int64()
+    rc = lib().cg_eval_calc(buf, len(span), ctypes.byref(v))
+    if rc != CG_OK:
+        return rc, lib().cg_last_error().decode(errors="replace")
+    return CG_OK, v.value
 
 
 def sample_workspace_bytes(B: int, V: int) -> int:

@@ -3,6 +3,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
+#include <string>
 #include <vector>
 
 #include "cg_internal.hpp"
@@ -12,6 +14,8 @@ const char *last_error();
 int launch_init(const cg_grammar *g, cg_state *states, int B, hipStream_t st);
 int launch_advance(const cg_grammar *g, cg_state *states, int B, const int32_t *ids, int32_t *steps,
                    int32_t *status, hipStream_t st);
+int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *bytes, const uint32_t *offsets,
+                 int32_t *status, hipStream_t st);
 int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws,
                 hipStream_t st);
 int fill_plan_stride(const cg_grammar *g);
@@ -49,6 +53,7 @@ void release(cg_grammar *g) {
         (void)hipFree(g->dev.tokw);
         (void)hipFree(g->dev.tokinfo);
         (void)hipFree(g->dev.legal);
+        (void)hipFree(g->dev.forced);
         (void)hipFree(g->dev.lex_idlen);
         (void)hipFree(g->dev.lex_jump);
         (void)hipFree(g->dev.lex_w);
@@ -249,7 +254,8 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
             upload(&g->dev.q_posch, f.q_posch.data(), f.q_posch.size()) ||
             upload(&g->dev.q_w, f.q_w.data(), f.q_w.size()) ||
             upload(&g->dev.q_tile, f.q_tile.data(), f.q_tile.size()) ||
-            upload(&g->dev.strbits, f.strbits.data(), f.strbits.size())) {
+            upload(&g->dev.strbits, f.strbits.data(), f.strbits.size()) ||
+            (g->has_forced && upload(&g->dev.forced, g->host_forced.data(), g->host_forced.size()))) {
             set_error("device upload failed: %s", hipGetErrorString(hipGetLastError()));
             release(g);
             return CG_E_DEVICE;
@@ -345,6 +351,87 @@ int cg_advance(const cg_grammar *g, cg_state *d_states, int32_t batch, const int
     return launch_advance(g, d_states, batch, d_token_ids, d_step, d_status, (hipStream_t)stream);
 }
 
+int cg_force_bytes(const cg_grammar *g, cg_state *d_states, int32_t batch, const uint8_t *d_bytes,
+                   const uint32_t *d_offsets, int32_t *d_status, void *stream) {
+    if (!on_device(g)) return arg_error("grammar has no device tables");
+    if (batch < 0 || (batch > 0 && (!d_states || !d_offsets || !d_status))) return arg_error("bad arguments");
+    return launch_force(g, d_states, batch, d_bytes, d_offsets, d_status, (hipStream_t)stream);
+}
+
+int cg_eval_calc(const uint8_t *span, size_t len, int64_t *value) {
+    if (!value || (len && !span)) return arg_error("NULL argument");
+    std::string s((const char *)span, len);
+    if (s.size() >= 13 && s.compare(0, 6, "<calc>") == 0 && s.compare(s.size() - 7, 7, "</calc>") == 0)
+        s = s.substr(6, s.size() - 13);
+    size_t i = 0;
+    auto skip = [&]() {
+        while (i < s.size() && (s[i] == ' ' || s[i] == '\t' || s[i] == '\n' || s[i] == '\r')) i++;
+    };
+    struct Fail {
+        int code;
+        const char *msg;
+    };
+    // E := P (('+' | '-') P)*, P := T (('*' | '/') T)*, T := int | '(' E ')'
+    std::function<int64_t()> expr;
+    auto term = [&]() -> int64_t {
+        skip();
+        if (i < s.size() && s[i] == '(') {
+            i++;
+            const int64_t v = expr();
+            skip();
+            if (i >= s.size() || s[i] != ')') throw Fail{CG_E_PARSE, "missing )"};
+            i++;
+            return v;
+        }
+        if (i >= s.size() || s[i] < '0' || s[i] > '9') throw Fail{CG_E_PARSE, "expected an integer or ("};
+        int64_t v = 0;
+        while (i < s.size() && s[i] >= '0' && s[i] <= '9') {
+            if (__builtin_mul_overflow(v, (int64_t)10, &v) || __builtin_add_overflow(v, (int64_t)(s[i] - '0'), &v))
+                throw Fail{CG_E_EVAL, "out of range"};
+            i++;
+        }
+        return v;
+    };
+    auto prod = [&]() -> int64_t {
+        int64_t v = term();
+        for (;;) {
+            skip();
+            if (i >= s.size() || (s[i] != '*' && s[i] != '/')) return v;
+            const char op = s[i++];
+            const int64_t r = term();
+            if (op == '*') {
+                if (__builtin_mul_overflow(v, r, &v)) throw Fail{CG_E_EVAL, "out of range"};
+            } else {
+                if (r == 0) throw Fail{CG_E_EVAL, "division by zero"};
+                if (v == INT64_MIN && r == -1) throw Fail{CG_E_EVAL, "out of range"};
+                v /= r;  // truncates toward zero
+            }
+        }
+    };
+    expr = [&]() -> int64_t {
+        int64_t v = prod();
+        for (;;) {
+            skip();
+            if (i >= s.size() || (s[i] != '+' && s[i] != '-')) return v;
+            const char op = s[i++];
+            const int64_t r = prod();
+            if (op == '+' ? __builtin_add_overflow(v, r, &v) : __builtin_sub_overflow(v, r, &v))
+                throw Fail{CG_E_EVAL, "out of range"};
+        }
+    };
+    try {
+        const int64_t v = expr();
+        skip();
+        if (i != s.size()) throw Fail{CG_E_PARSE, "trailing input"};
+        *value = v;
+        return CG_OK;
+    } catch (const Fail &f) {
+        if (f.code == CG_E_EVAL) set_error("%s", f.msg);
+        else set_error("calc span: %s at byte %zu", f.msg, i);
+        return f.code;
+    }
+}
+
 int cg_try_input(const cg_grammar *g, const uint8_t *bytes, size_t len, size_t *refused_at, int *complete) {
     if (!g || !refused_at || !complete || (len && !bytes)) return arg_error("NULL argument");
     Walker w;
@@ -356,7 +443,7 @@ int cg_try_input(const cg_grammar *g, const uint8_t *bytes, size_t len, size_t *
     w.stk = 0;
     size_t i = 0;
     for (; i < len; i++)
-        if (!step_byte(w, bytes[i], g->host_comb, g->k)) break;
+        if (!step_byte<true>(w, bytes[i], g->host_comb, g->k)) break;
     *refused_at = i;
     *complete = (i == len && w.q == g->k.accept) ? 1 : 0;
     return CG_OK;

@@ -8,7 +8,10 @@
 // classes, no per-state descriptor.
 //
 // Slot layout (little-endian u64):
-//   bits  0..15  owner   state id whose row this slot belongs to (0xFFFF: empty)
+//   bits  0..15  owner   state id whose row this slot belongs to (0xFFFF:
+//                        empty), plus 0x8000 when that state lies in a region
+//                        only the engine writes (kEngineOwner): a model token
+//                        may enter such a state but never leave it
 //   bits 16..31  next    next state (see ops)
 //   bits 32..35  op      what the byte does to the registers besides moving
 //   bits 36..63  arg     operand (28 bits)
@@ -21,6 +24,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <vector>
 
 #include "../../include/cg.h"
 
@@ -37,6 +42,7 @@ enum Op : uint32_t {
 };
 
 constexpr uint32_t kEmptyOwner = 0xFFFF;
+constexpr uint32_t kEngineOwner = 0x8000;  // owner tag of an engine-written state's slots
 constexpr uint32_t kMaxStateId = 0x3FFF;   // POP packs two state ids in 28 bits
 constexpr uint32_t kUncapped = 0x0FFFFFFF; // cnt of an uncapped string
 constexpr int kMaxTokenLen = 32;
@@ -80,11 +86,14 @@ __host__ __device__ inline void store_walker(cg_state &s, const Walker &w) {
 // unspecified but every state id in it stays < q_limit, so a dead lane may
 // keep indexing the table safely).  The common ops (move, whitespace, string
 // code point) are straight-line; string open/close and container push/pop
-// take the rare branch.
+// take the rare branch.  kEngine: the engine's own bytes, which may also
+// leave engine-written states (a model token's walk refuses those slots
+// because their owner carries the tag).
+template <bool kEngine = false>
 __host__ __device__ inline bool step_byte(Walker &w, uint32_t b, const uint64_t *comb, const WalkConsts &k) {
     const uint64_t e = comb[w.q + b];
     const uint32_t lo = (uint32_t)e, hi = (uint32_t)(e >> 32);
-    bool ok = (lo & 0xFFFFu) == w.q;
+    bool ok = (lo & (kEngine ? 0x7FFFu : 0xFFFFu)) == w.q;
     uint32_t nq = lo >> 16;
     const uint32_t op = hi & 0xFu;
     const uint32_t ws1 = (op == OP_WS) ? w.ws + 1 : 0;
@@ -137,11 +146,16 @@ __device__ inline void stage_table(uint64_t *dst, const uint64_t *__restrict__ s
 // Commit token `id` (its n bytes in words[], 4 per word) to a row: the
 // cg_advance rules.  -1 is a no-op; an id out of range, a finished row or a
 // refused byte leaves the row unchanged (REJECTED); otherwise the row takes
-// the walked configuration, step + 1, and DONE / CAPPED flags.  Returns the
-// status; `s` and `step` are updated only when the token is accepted.
+// the walked configuration, step + 1, and DONE / CAPPED flags, or INJECT
+// when it now sits in an engine-written region.  Returns the status; `s`
+// and `step` are updated only when the token is accepted.
+__host__ __device__ inline bool forced_state(const uint32_t *forced, uint32_t q) {
+    return forced && ((forced[q >> 5] >> (q & 31)) & 1u);
+}
+
 __host__ __device__ inline int commit_token(cg_state &s, int &step, int id, int V, uint32_t n,
                                             const uint32_t (&words)[kMaxTokenLen / 4], const uint64_t *comb,
-                                            const WalkConsts &k, uint32_t gen_cap) {
+                                            const WalkConsts &k, uint32_t gen_cap, const uint32_t *forced) {
     if (id < 0) return CG_ROW_NOOP;
     if (id >= V || (s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) || s.q >= k.q_limit || s.ret >= k.q_limit)
         return CG_ROW_REJECTED;
@@ -165,6 +179,7 @@ __host__ __device__ inline int commit_token(cg_state &s, int &step, int id, int 
         fl |= CG_FLAG_CAPPED;
         if (res == CG_ROW_OK) res = CG_ROW_CAPPED;
     }
+    if (res == CG_ROW_OK && forced_state(forced, w.q)) res = CG_ROW_INJECT;
     s.flags = fl;
     s.pad0 = 0;
     s.pad1 = 0;
@@ -207,6 +222,7 @@ struct DeviceTables {
     uint32_t *tokw = nullptr;     // [nw][V] token bytes, 4 per word, little-endian, zero padded
     uint32_t *tokinfo = nullptr;  // [V] length + string-body summary
     uint64_t *legal = nullptr;    // [q_limit][4] bytes with a transition out of state q (256-bit set)
+    uint32_t *forced = nullptr;   // [ceil(q_limit / 32)] bit q: engine-written state (null: none)
     // Fill candidates: the non-empty tokens in lexicographic order, padded
     // with empty entries (idlen 0) to whole 64-token tiles.
     uint32_t *lex_idlen = nullptr;   // [lex_tiles * 64] id | len << 24
@@ -241,6 +257,8 @@ struct cg_grammar {
     int32_t q_tiles = 0;     // and of the string-closing list
     double compile_ms = 0;
     uint64_t *host_comb = nullptr;
+    std::vector<uint32_t> host_forced;  // bit q: state q is inside an engine-written region
+    bool has_forced = false;
     cg::DeviceTables dev;
 };
 

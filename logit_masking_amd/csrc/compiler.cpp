@@ -356,6 +356,7 @@ struct BState {
     std::vector<Edge> e;
     bool string_state = false;
     bool trie_node = false;  // interior node made by trie()
+    bool forced = false;     // inside a region only the engine writes
 };
 
 struct Builder {
@@ -774,22 +775,61 @@ struct Builder {
     }
 
     // ---- whole grammars -----------------------------------------------
-    void calc() {
+    // "<calc>" W E W "</calc>" from state `from` to state `to`
+    void calc_span(int from, int to) {
         int ETt = add(), ETi = add(), ATt = add(), ATi = add();
         for (int q : {ETt, ETi, ATt, ATi}) ws_loop(q);
         for (int op : {'+', '-', '*', '/'}) {
             edge(ATt, op, op, OP_NONE, 0, ETt);
             edge(ATi, op, op, OP_NONE, 0, ETi);
         }
-        trie(ATt, {"</calc>"}, accept);
+        trie(ATt, {"</calc>"}, to);
         edge(ATi, ')', ')', OP_POP, 0, ATt, ATi, ATi);
         const uint32_t push = ((uint32_t)S.depth_cap << 1);
         edge(ETt, '(', '(', OP_PUSH, push, ETi);
         edge(ETi, '(', '(', OP_PUSH, push, ETi);
         magnitude(ETt, (u128)S.calc_min, (u128)S.calc_max, 19, ATt);
         magnitude(ETi, (u128)S.calc_min, (u128)S.calc_max, 19, ATi);
+        trie(from, {"<calc>"}, ETt);
+    }
+
+    void calc() {
         start = add();
-        trie(start, {"<calc>"}, ETt);
+        calc_span(start, accept);
+    }
+
+    // Text with evaluated spans: TEXT* ("<calc>" W E W "</calc>" RESULT
+    // TEXT*)* "<end>", TEXT = LF or printable ASCII other than '<'.  RESULT is
+    // written by the engine, never sampled, so its states are marked forced:
+    // "<result>" "-"? digit{1,20} "</result>" for a value, or
+    // "<result_error>" MSG "</result_error>" for a failed evaluation, MSG =
+    // printable ASCII other than '<'.
+    void calc_text() {
+        const int TX = start = add();
+        edge(TX, '\n', '\n', OP_NONE, 0, TX);
+        edge(TX, 0x20, '<' - 1, OP_NONE, 0, TX);
+        edge(TX, '<' + 1, 0x7E, OP_NONE, 0, TX);
+        const int R0 = add();
+        calc_span(TX, R0);
+        trie(TX, {"<end>"}, accept);
+        const int first_forced = (int)st.size();
+        const int RV = add(), RN = add(), RM = add();
+        int RD[21];
+        for (int d = 1; d <= 20; d++) RD[d] = add();
+        trie(R0, {"<result>"}, RV);
+        trie(R0, {"<result_error>"}, RM);
+        edge(RV, '-', '-', OP_NONE, 0, RN);
+        edge(RV, '0', '9', OP_NONE, 0, RD[1]);
+        edge(RN, '0', '9', OP_NONE, 0, RD[1]);
+        for (int d = 1; d <= 20; d++) {
+            if (d < 20) edge(RD[d], '0', '9', OP_NONE, 0, RD[d + 1]);
+            trie(RD[d], {"</result>"}, TX);
+        }
+        edge(RM, 0x20, '<' - 1, OP_NONE, 0, RM);
+        edge(RM, '<' + 1, 0x7E, OP_NONE, 0, RM);
+        trie(RM, {"</result_error>"}, TX);
+        st[R0].forced = true;
+        for (int q = first_forced; q < (int)st.size(); q++) st[q].forced = true;
     }
 };
 
@@ -904,12 +944,17 @@ void trim_and_pack(Builder &B, cg_grammar *g) {
             else next = (uint32_t)base[e.to];
             if (e.op == OP_POP) arg = (uint32_t)base[e.to_obj] | ((uint32_t)base[e.to_arr] << 14);
             for (int b = e.lo; b <= e.hi; b++) {
-                uint64_t lo32 = (uint64_t)(uint32_t)base[q] | ((uint64_t)next << 16);
+                const uint32_t owner = (uint32_t)base[q] | (B.st[q].forced ? kEngineOwner : 0u);
+                uint64_t lo32 = (uint64_t)owner | ((uint64_t)next << 16);
                 uint64_t hi32 = (uint64_t)e.op | ((uint64_t)arg << 4);
                 comb[base[q] + b] = lo32 | (hi32 << 32);
             }
         }
     }
+    g->host_forced.assign(((size_t)max_base + 1 + 31) / 32, 0u);
+    for (int q : order)
+        if (B.st[q].forced) g->host_forced[base[q] >> 5] |= 1u << (base[q] & 31);
+    g->has_forced = std::any_of(order.begin(), order.end(), [&](int q) { return B.st[q].forced; });
     g->host_comb = comb;
     g->comb_len = comb_len;
     g->n_states = (int)order.size();
@@ -947,7 +992,7 @@ int compile_spec(const char *spec, size_t len, cg_grammar *g) {
         R.S = S;
         int json_root = -1;
         std::vector<std::pair<std::string, int>> tools;
-        if (k == "calc") {
+        if (k == "calc" || k == "calc_text") {
             S.calc_min = setting(root, "int_min", 0, 0, 1000000000, false);
             S.calc_max = setting(root, "int_max", 999, 0, 1000000000, false);
             if (S.calc_min > S.calc_max) refuse("$", "empty integer range");
@@ -984,6 +1029,8 @@ int compile_spec(const char *spec, size_t len, cg_grammar *g) {
         B.accept = B.add();
         if (k == "calc") {
             B.calc();
+        } else if (k == "calc_text") {
+            B.calc_text();
         } else if (k == "json_schema") {
             B.start = B.value(json_root, B.accept, 0);
             if (B.start < 0) refuse("$", "grammar accepts no string");

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ co
                                                  const uint32_t *__restrict__ tokw, const uint32_t *__restrict__ tokinfo,
                                                  int nw, int V, cg_state *__restrict__ states, int B,
                                                  const int32_t *__restrict__ ids, int32_t *__restrict__ steps,
-                                                 int32_t *__restrict__ status, uint32_t gen_cap) {
+                                                 int32_t *__restrict__ status, uint32_t gen_cap,
+                                                 const uint32_t *__restrict__ forced) {
     extern __shared__ uint64_t lds_comb[];
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     const bool row = r < B;
@@ -72,11 +73,61 @@ __global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ co
     __syncthreads();
     if (!row) return;
     int st = st0;
-    const int res = commit_token(s, st, id, V, n, words, lds_comb, k, gen_cap);
+    const int res = commit_token(s, st, id, V, n, words, lds_comb, k, gen_cap, forced);
     if (res == CG_ROW_OK || res == CG_ROW_DONE || res == CG_ROW_CAPPED) {
         states[r] = s;
         steps[r] = st;
     }
+    status[r] = res;
+}
+
+// One lane per row: walk the row's forced byte string (the engine writing an
+// evaluated result into the text, "Evaluator aware decoding", "A concrete
+// prototype on llama.cpp").  One forced string counts as one step.
+__global__ __launch_bounds__(256) void k_force(const uint64_t *__restrict__ comb, uint32_t comb_len, WalkConsts k,
+                                               cg_state *__restrict__ states, int B, const uint8_t *__restrict__ bytes,
+                                               const uint32_t *__restrict__ offsets, int32_t *__restrict__ status,
+                                               const uint32_t *__restrict__ forced) {
+    extern __shared__ uint64_t lds_comb[];
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    const bool row = r < B;
+    cg_state s{};
+    uint32_t b0 = 0, b1 = 0;
+    if (row) {
+        s = states[r];
+        b0 = offsets[r];
+        b1 = offsets[r + 1];
+    }
+    stage_table(lds_comb, comb, comb_len);
+    __syncthreads();
+    if (!row) return;
+    if (b1 <= b0) {
+        status[r] = CG_ROW_NOOP;
+        return;
+    }
+    if ((s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) || s.q >= k.q_limit || s.ret >= k.q_limit) {
+        status[r] = CG_ROW_REJECTED;
+        return;
+    }
+    Walker w = load_walker(s);
+    bool ok = true;
+    for (uint32_t i = b0; ok && i < b1; i++) ok = step_byte<true>(w, bytes[i], lds_comb, k);
+    if (!ok) {
+        status[r] = CG_ROW_REJECTED;
+        return;
+    }
+    store_walker(s, w);
+    int res = CG_ROW_OK;
+    s.flags = 0;
+    if (w.q == k.accept) {
+        s.flags = CG_FLAG_DONE;
+        res = CG_ROW_DONE;
+    } else if (forced_state(forced, w.q)) {
+        res = CG_ROW_INJECT;
+    }
+    s.pad0 = 0;
+    s.pad1 = 0;
+    states[r] = s;
     status[r] = res;
 }
 
@@ -130,6 +181,7 @@ struct FillArgs {
     const cg_state *states;
     unsigned long long *mask;
     int words_per_row;
+    const uint32_t *forced;  // engine-written states: empty mask (null: none)
     uint32_t *plan;       // per row: [0] listed tiles, [1..] their indices
     int plan_stride;      // u32 per row
     int B;
@@ -257,7 +309,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_fill_plan(FillArgs a) {
     const cg_state s = a.states[r];
     uint32_t *plan = a.plan + (size_t)r * a.plan_stride;
     unsigned long long *out = a.mask + (size_t)r * a.words_per_row;
-    const bool live = row_live(s, k);
+    const bool live = row_live(s, k) && !forced_state(a.forced, s.q);
     const bool in_str = live && s.q == k.s_body;
     const int n_all = !live ? 0 : in_str ? a.q_tiles : a.lex_tiles;
     const uint2 *tkeys = in_str ? a.q_tile : a.lex_tile;
@@ -441,8 +493,18 @@ int launch_advance(const cg_grammar *g, cg_state *states, int B, const int32_t *
     if (B == 0) return CG_OK;
     const size_t lds = (size_t)g->comb_len * sizeof(uint64_t);
     hipLaunchKernelGGL(k_advance, dim3((B + 255) / 256), dim3(256), lds, st, g->dev.comb, g->comb_len, g->k,
-                       g->dev.tokw, g->dev.tokinfo, g->nw, g->V, states, B, ids, steps, status, g->gen_cap);
+                       g->dev.tokw, g->dev.tokinfo, g->nw, g->V, states, B, ids, steps, status, g->gen_cap,
+                       g->dev.forced);
     return launch_status("advance");
+}
+
+int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *bytes, const uint32_t *offsets,
+                 int32_t *status, hipStream_t st) {
+    if (B == 0) return CG_OK;
+    const size_t lds = (size_t)g->comb_len * sizeof(uint64_t);
+    hipLaunchKernelGGL(k_force, dim3((B + 255) / 256), dim3(256), lds, st, g->dev.comb, g->comb_len, g->k, states, B,
+                       bytes, offsets, status, g->dev.forced);
+    return launch_status("force_bytes");
 }
 
 // Plan of one row: listed-tile count + up to every tile of the longer list.
@@ -486,6 +548,7 @@ static int launch_fill_nw(const cg_grammar *g, const cg_state *states, int B, ui
     a.states = states;
     a.mask = (unsigned long long *)mask;
     a.words_per_row = wpr;
+    a.forced = g->dev.forced;
     a.plan = (uint32_t *)ws;
     a.plan_stride = fill_plan_stride(g);
     a.B = B;

@@ -468,6 +468,7 @@ struct AdvanceArgs {
     int32_t *steps;        // the same array as the sampler's step (read first, then bumped)
     int32_t *status;
     uint32_t gen_cap;
+    const uint32_t *forced;
 };
 
 // byte offset of the stash in dynamic LDS: after the chunk summaries, 16-byte aligned
@@ -775,7 +776,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             if (j < adv.nw) words[j] = adv.tokw[(size_t)j * adv.V + pick];
     }
     int stp1 = (int)stp;
-    const int res = commit_token(row_state, stp1, pick, adv.V, n, words, lds_comb, adv.k, adv.gen_cap);
+    const int res = commit_token(row_state, stp1, pick, adv.V, n, words, lds_comb, adv.k, adv.gen_cap, adv.forced);
     if (res == CG_ROW_OK || res == CG_ROW_DONE || res == CG_ROW_CAPPED) {
         adv.states[r] = row_state;
         adv.steps[r] = stp1;
@@ -833,6 +834,7 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
         adv.steps = steps_rw;
         adv.status = status;
         adv.gen_cap = g->gen_cap;
+        adv.forced = g->dev.forced;
     }
     const int es = dt == 0 ? 4 : 2;
     const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * es) % 16 == 0);

@@ -1,7 +1,7 @@
 """Seeded synthetic workloads for the constrained-decoding hot path.
 
 This module is shared by the tests, the benchmark and the smoke check.  It
-holds the five grammar specs, the vocabulary generators, per-row seeds and
+holds the six grammar specs, the vocabulary generators, per-row seeds and
 the logits recipe -- inputs only.  It performs none of the method's
 arithmetic (no automaton, no masking, no sampling).
 
@@ -19,6 +19,9 @@ The workloads restate the pages' settings:
     "The system boundary I am testing"), compact separators ("What the audit
     found"), greedy decoding ("The protocol was frozen before the cloud run").
   * a recursive-JSON stress grammar capped at 2048 tokens.
+  * text with evaluated calc spans ("Evaluator aware decoding", "A concrete
+    prototype on llama.cpp"): the model writes prose and <calc> spans, the
+    engine writes <result> / <result_error> blocks.
 
 Random numbers come from splitmix64 written in plain Python so that every
 vocabulary is byte-identical across numpy versions.
@@ -150,6 +153,7 @@ SPECS = {
         "schema": _obj([("reasoning", _strn(2000)), ("answer", {"type": "integer"})])},
     5: {"kind": "json_schema", "ws_max": 4, "open_string_cap": None, "depth_cap": 32,
         "schema": {"anyOf": [{"type": "object"}, {"type": "array"}]}},
+    6: {"kind": "calc_text", "int_min": 0, "int_max": 999, "ws_max": 2, "depth_cap": 16},
 }
 
 
@@ -172,6 +176,8 @@ CONFIGS = {
             T=0.0, steps=400, maxlen=24, mean=6.0, seed=0xC0F4),
     5: dict(name="stress-json", B=512, V=256000, dtype="bf16", logits="student_t3", sigma=1.0,
             T=1.0, steps=2048, maxlen=32, mean=7.0, seed=0xC0F5),
+    6: dict(name="calc-text", B=256, V=128256, dtype="bf16", logits="normal", sigma=3.0,
+            T=0.7, steps=256, maxlen=16, mean=5.0, seed=0xC0F6),
 }
 
 GEN_CAP = 2048  # engine cap on one constrained generation, in tokens
@@ -211,6 +217,12 @@ _FRAGS = {
         "-", "+", "0.5", "1e9", "-3", "1.25e-3"],
 }
 
+_TEXT_FRAGS = ["<calc>", "</calc>", "<result>", "</result>", "<result_error>", "</result_error>", "<end>",
+               "<", ">", "</", "calc", "result", " + ", " - ", " * ", " / ", "+", "-", "*", "/", "(", ")",
+               " (", ") ", " = ", "=", " is", " the", " answer", " total", ".", ",", "\n", " "]
+
+_CALC_BYTES = b"0123456789+-*/() "
+_TEXT_PUNCT = b".,;:!?'\"\n\t <>"
 _LETTERS = b"abcdefghijklmnopqrstuvwxyz"
 _UTF8_RANGES = [(0xA0, 0x24F), (0x370, 0x3FF), (0x400, 0x4FF), (0x4E00, 0x9FFF),
                 (0x1F300, 0x1F64F), (0xAC00, 0xD7A3)]
@@ -219,6 +231,33 @@ _UTF8_RANGES = [(0xA0, 0x24F), (0x370, 0x3FF), (0x400, 0x4FF), (0x4E00, 0x9FFF),
 def _utf8_piece(rng: SplitMix) -> bytes:
     lo, hi = _UTF8_RANGES[rng.below(len(_UTF8_RANGES))]
     return chr(lo + rng.below(hi - lo + 1)).encode("utf-8")
+
+
+def _gen_text_token(rng: SplitMix, L: int) -> bytes:
+    """One candidate token of exactly L bytes for text with calc spans."""
+    u = rng.uniform()
+    out = bytearray()
+    if u < 0.30:  # tags, operators and glue
+        while len(out) < L:
+            piece = rng.choice(_TEXT_FRAGS).encode()
+            if not out and len(piece) > 1 and rng.uniform() < 0.4:
+                piece = piece[rng.below(len(piece)):]
+            out += piece
+    elif u < 0.65:  # words, usually with a leading space
+        if rng.uniform() < 0.7:
+            out += b" "
+        while len(out) < L:
+            out.append(_LETTERS[rng.below(26)])
+    elif u < 0.85:  # digits, operators, spaces, parentheses
+        while len(out) < L:
+            out.append(_CALC_BYTES[rng.below(len(_CALC_BYTES))] if rng.uniform() < 0.7 else 0x30 + rng.below(10))
+    elif u < 0.95:  # punctuation and whitespace
+        while len(out) < L:
+            out.append(_TEXT_PUNCT[rng.below(len(_TEXT_PUNCT))])
+    else:  # raw bytes
+        while len(out) < L:
+            out.append(rng.below(256))
+    return bytes(out[:L])
 
 
 def _gen_token(rng: SplitMix, cfg: int, L: int) -> bytes:
@@ -281,6 +320,9 @@ def make_vocab(cfg: int, V: int | None = None):
             L = 2 + rng.below(5)
             t = bytes((_CALC_ALPHA[rng.below(len(_CALC_ALPHA))] if rng.uniform() < 0.8
                        else _PRINTABLE[rng.below(len(_PRINTABLE))]) for _ in range(L))
+        elif cfg == 6:
+            L = min(c["maxlen"], 2 + rng.poisson(c["mean"] - 2.0))
+            t = _gen_text_token(rng, L)
         else:
             L = min(c["maxlen"], 2 + rng.poisson(c["mean"] - 2.0))
             t = _gen_token(rng, cfg, L)
@@ -330,3 +372,61 @@ def make_logits(cfg: int, step: int, B: int, V: int, device, row_stride: int | N
         x = z / torch.sqrt((chi * chi).sum(0) / 3.0) * c["sigma"]
     dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
     return x.to(dt)
+
+
+# ---------------------------------------------------------------------------
+# Scripts for text with calc spans: what a row's model writes, segment by
+# segment.  Each segment but the last ends with a closed <calc> span (the
+# engine writes the result after it); the last ends with "<end>".  Inputs
+# only: nothing here evaluates a span.
+# ---------------------------------------------------------------------------
+_PROSE_WORDS = [b"the", b"total", b"is", b"so", b"we", b"get", b"then", b"each", b"and", b"of", b"price",
+                b"items", b"sum", b"answer", b"left", b"per", b"box"]
+
+
+def calc_expr(rng: SplitMix, spec, depth: int = 0, budget: int = 6) -> bytes:
+    """A random expression of the calc span grammar of `spec` (ints within
+    [int_min, int_max], + - * /, parentheses under depth_cap, whitespace
+    runs within ws_max).  Sometimes divides by zero or multiplies large
+    numbers so that evaluation fails."""
+    lo, hi = spec.get("int_min", 0), spec.get("int_max", 999)
+    wsm, dcap = spec.get("ws_max", 4), spec.get("depth_cap", 16)
+
+    def ws():
+        return b" " * rng.below(wsm + 1) if wsm else b""
+
+    def term(d, budget):
+        if d < dcap and budget > 1 and rng.uniform() < 0.2:
+            return b"(" + ws() + expr(d + 1, budget - 1) + ws() + b")"
+        r = rng.uniform()
+        v = lo if r < 0.08 else hi if r < 0.2 else lo + rng.below(hi - lo + 1)
+        return str(v).encode()
+
+    def expr(d, budget):
+        out = term(d, budget)
+        n = rng.below(max(1, min(4, budget)))
+        for _ in range(n):
+            out += ws() + bytes([b"+-*/"[rng.below(4)]]) + ws() + term(d, budget - n)
+        return out
+
+    return expr(depth, budget)
+
+
+def calc_text_script(rng: SplitMix, spec, n_spans: int) -> list:
+    """Model segments of one row: prose, then "<calc>" EXPR "</calc>", n_spans
+    times, then prose and "<end>"."""
+    def prose():
+        words = [rng.choice(_PROSE_WORDS) for _ in range(rng.below(6))]
+        text = b" ".join(words)
+        if text and rng.uniform() < 0.3:
+            text += b"\n"
+        return text + (b" " if text else b"")
+
+    segs = []
+    for _ in range(n_spans):
+        w = spec.get("ws_max", 4)
+        lead = b" " * rng.below(w + 1) if w else b""
+        tail = b" " * rng.below(w + 1) if w else b""
+        segs.append(prose() + b"<calc>" + lead + calc_expr(rng, spec) + tail + b"</calc>")
+    segs.append(prose() + b"<end>")
+    return segs

@@ -90,6 +90,10 @@ def lib():
             L.oc_start.argtypes = [vp, vp]
             L.oc_feed.argtypes = [vp, vp, vp, i32]
             L.oc_feed.restype = ctypes.c_int
+            L.oc_feed_model.argtypes = [vp, vp, vp, i32]
+            L.oc_feed_model.restype = ctypes.c_int
+            L.oc_in_engine.argtypes = [vp, vp]
+            L.oc_in_engine.restype = ctypes.c_int
             L.oc_complete.argtypes = [vp, vp]
             L.oc_complete.restype = ctypes.c_int
             L.oc_mask.argtypes = [vp, vp, vp, vp, i32, vp]
@@ -107,7 +111,7 @@ def lib():
 # Spec reading
 # ---------------------------------------------------------------------------
 K_OBJ, K_ARR, K_STR, K_INT, K_NUM, K_BOOL, K_NULL, K_ENUM, K_ANYOF, K_ANY = range(1, 11)
-G_CALC, G_JSON, G_TOOL = 1, 2, 3
+G_CALC, G_JSON, G_TOOL, G_TEXT = 1, 2, 3, 4
 AK_ALL = 31
 
 # Defaults of a spec that leaves a setting out.
@@ -324,8 +328,8 @@ class Grammar:
         og = OG()
         og.ws_max, og.depth_cap, og.open_cap = s["ws_max"], s["depth_cap"], s["open_cap"]
         og.root, og.tools_first, og.tools_count = -1, 0, 0
-        if kind == "calc":
-            og.gkind = G_CALC
+        if kind in ("calc", "calc_text"):
+            og.gkind = G_CALC if kind == "calc" else G_TEXT
             og.calc_min = _setting(spec, "int_min", 0, 10**9)
             og.calc_max = _setting(spec, "int_max", 0, 10**9)
             if og.calc_min > og.calc_max:
@@ -393,12 +397,19 @@ class Grammar:
         ctypes.memmove(c, conf, len(conf))
         return c
 
-    def feed(self, conf, data: bytes) -> int:
-        """Feed bytes; returns how many were accepted (len(data) if all)."""
+    def feed(self, conf, data: bytes, model: bool = False) -> int:
+        """Feed bytes; returns how many were accepted (len(data) if all).
+        model=True: the bytes are the model's, refused where the engine
+        writes (the result region of calc_text)."""
         if not data:
             return 0
         buf = (ctypes.c_uint8 * len(data)).from_buffer_copy(data)
-        return self._L.oc_feed(ctypes.byref(self._og), conf, buf, len(data))
+        fn = self._L.oc_feed_model if model else self._L.oc_feed
+        return fn(ctypes.byref(self._og), conf, buf, len(data))
+
+    def in_engine(self, conf) -> bool:
+        """Is the next byte one the engine writes?"""
+        return bool(self._L.oc_in_engine(ctypes.byref(self._og), conf))
 
     def complete(self, conf) -> bool:
         return bool(self._L.oc_complete(ctypes.byref(self._og), conf))
@@ -466,7 +477,7 @@ def load_spec(spec) -> Grammar:
 # ---------------------------------------------------------------------------
 # Rows: state + step counter + the engine cap.
 # ---------------------------------------------------------------------------
-ROW_OK, ROW_DONE, ROW_CAPPED, ROW_REJECTED, ROW_NOOP = 0, 1, 2, 3, 4
+ROW_OK, ROW_DONE, ROW_CAPPED, ROW_REJECTED, ROW_NOOP, ROW_INJECT = 0, 1, 2, 3, 4, 5
 
 
 class Row:
@@ -488,23 +499,41 @@ class Row:
         return self.complete or self.capped
 
     def advance(self, tok: bytes | None) -> int:
+        """A token the model chose (or a forced token id): every byte must be
+        the model's to write."""
         if tok is None:
             return ROW_NOOP
-        if self.done:
+        return self._take(tok, model=True)
+
+    def force(self, data: bytes) -> int:
+        """Bytes the engine writes -- an evaluated result injected into the
+        stream, a transition the model did not choose (page "Evaluator aware
+        decoding", section "A concrete prototype on llama.cpp").  Not a
+        generation step: the step count and the cap are untouched.  Empty is
+        a no-op."""
+        if not data:
+            return ROW_NOOP
+        return self._take(data, model=False)
+
+    def _take(self, data: bytes, model: bool) -> int:
+        if self.done or not data:
             return ROW_REJECTED
         c = self.g.clone(self.conf)
-        if self.g.feed(c, tok) != len(tok) or not tok:
+        if self.g.feed(c, data, model=model) != len(data):
             return ROW_REJECTED
         self.conf = c
-        self.text += tok
-        self.step += 1
+        self.text += data
         self.complete = self.g.complete(c)
-        if self.step >= self.gen_cap:
-            self.capped = True
+        if model:
+            self.step += 1
+            if self.step >= self.gen_cap:
+                self.capped = True
         if self.complete:
             return ROW_DONE
         if self.capped:
             return ROW_CAPPED
+        if self.g.in_engine(c):
+            return ROW_INJECT
         return ROW_OK
 
 
@@ -624,16 +653,29 @@ def unpack_mask(words, V):
 
 # ---------------------------------------------------------------------------
 # Calc-span evaluator: exact integers, * and / before + and -, left to
-# right, / truncating toward zero, division by zero an error.
+# right, / truncating toward zero, division by zero an error (page "Evaluator
+# aware decoding", sections "The core idea" and "A concrete prototype on
+# llama.cpp": a small local parser evaluates the closed span).  bound=(lo,
+# hi): also an error when a literal or any intermediate result leaves
+# [lo, hi] -- a fixed-width engine's range.
 # ---------------------------------------------------------------------------
 class CalcError(ValueError):
     pass
 
 
-def eval_calc(span: bytes) -> int:
+INT64_RANGE = (-(1 << 63), (1 << 63) - 1)
+
+
+def eval_calc(span: bytes, bound=None) -> int:
     s = span.decode("ascii")
     if not (s.startswith("<calc>") and s.endswith("</calc>")):
         raise CalcError("not a calc span")
+
+    def within(v):
+        if bound is not None and not bound[0] <= v <= bound[1]:
+            raise CalcError("out of range")
+        return v
+
     toks = []
     body = s[6:-7]
     i = 0
@@ -668,7 +710,7 @@ def eval_calc(span: bytes) -> int:
             pos += 1
             return v
         if isinstance(t, int):
-            return Fraction(t)
+            return within(t)
         raise CalcError("expected a term")
 
     def prod():
@@ -683,8 +725,9 @@ def eval_calc(span: bytes) -> int:
             else:
                 if r == 0:
                     raise CalcError("division by zero")
-                q = abs(v.numerator * r.denominator) // abs(v.denominator * r.numerator)
-                v = Fraction(q if (v >= 0) == (r >= 0) else -q)
+                q = abs(v) // abs(r)
+                v = q if (v >= 0) == (r >= 0) else -q
+            within(v)
         return v
 
     def expr():
@@ -695,9 +738,10 @@ def eval_calc(span: bytes) -> int:
             pos += 1
             r = prod()
             v = v + r if op == "+" else v - r
+            within(v)
         return v
 
     v = expr()
     if pos != len(toks):
         raise CalcError("trailing input")
-    return int(v)
+    return v

@@ -41,7 +41,7 @@ typedef __int128 i128;
 
 /* ---- schema description, filled in by oracle.py ---------------------- */
 enum { K_OBJ = 1, K_ARR, K_STR, K_INT, K_NUM, K_BOOL, K_NULL, K_ENUM, K_ANYOF, K_ANY };
-enum { G_CALC = 1, G_JSON = 2, G_TOOL = 3 };
+enum { G_CALC = 1, G_JSON = 2, G_TOOL = 3, G_TEXT = 4 };
 /* K_ANY kinds that may start a value */
 enum { AK_OBJ = 1, AK_ARR = 2, AK_STR = 4, AK_NUM = 8, AK_LIT = 16 };
 
@@ -76,7 +76,7 @@ typedef struct {
 } og;
 
 /* ---- configuration ---------------------------------------------------- */
-enum { F_ROOT = 1, F_OBJ, F_ARR, F_STR, F_INT, F_NUM, F_LIT, F_ENUM, F_CALC };
+enum { F_ROOT = 1, F_OBJ, F_ARR, F_STR, F_INT, F_NUM, F_LIT, F_ENUM, F_CALC, F_TEXT };
 #define MAXF 48
 
 typedef struct {
@@ -265,6 +265,8 @@ enum { N_MINUS = 0, N_ZERO, N_INT, N_DOT, N_FRAC, N_E, N_ESIGN, N_EXP };
 enum { C_OPEN = 0, C_ET, C_INT, C_AT, C_CLOSE, C_DONE };
 /* root phases */
 enum { RT_NAME = 0, RT_VALUE, RT_INVAL, RT_CLOSE, RT_DONE };
+/* text phases; inside X_RES the engine writes every byte */
+enum { X_TEXT = 0, X_LT, X_END, X_CALC, X_RES, X_DONE };
 
 /*
  * Can a value of schema `node` be completed when `depth` containers are
@@ -612,11 +614,101 @@ static int step_calc(const og *g, ofr *f, int ch) {
             return R_DEAD;
         case C_CLOSE:
             if (ch != CALC_CLOSE[f->b]) return R_DEAD;
-            if (++f->b == 7) f->phase = C_DONE;
+            if (++f->b == 7) {
+                if (g->gkind == G_TEXT) return R_DONE_TOOK; /* a span inside text */
+                f->phase = C_DONE;
+            }
             return R_OK;
         default:
             return R_DEAD;
         }
+    }
+}
+
+/* text with evaluated spans (page "Evaluator aware decoding", "A concrete
+ * prototype on llama.cpp": the model writes a span, the engine evaluates it
+ * and writes the result, or an error the model can recover from, back):
+ *   X* ("<calc>" ... "</calc>" RESULT X*)* "<end>",
+ *   X = LF or printable ASCII other than '<',
+ *   RESULT = "<result>" "-"? digit{1,20} "</result>"
+ *          | "<result_error>" M* "</result_error>",  M = printable ASCII but '<'.
+ * In X_RES, a = position in RESULT: 0 "<result" (b bytes matched), 1 value
+ * start, 2 after '-', 3 digits (aux of them), 4 "</result>" (b matched),
+ * 5 "_error>" (b matched), 6 message, 7 "</result_error>" (b matched). */
+static const char END_TAG[] = "<end>";
+static const char RES_OPEN[] = "<result";
+static const char RES_CLOSE[] = "</result>";
+static const char ERR_OPEN[] = "_error>";
+static const char ERR_CLOSE[] = "</result_error>";
+
+static int printable(int ch) { return ch >= 0x20 && ch <= 0x7E; }
+
+static int step_text(oconf *c, ofr *f, int ch) {
+    switch (f->phase) {
+    case X_TEXT:
+        if (ch == '<') { f->phase = X_LT; return R_OK; }
+        return (ch == '\n' || printable(ch)) ? R_OK : R_DEAD;
+    case X_LT:
+        if (ch == 'e') { f->phase = X_END; f->b = 2; return R_OK; }
+        if (ch == 'c') {
+            ofr *k = push(c, F_CALC, -1);
+            k->phase = C_OPEN;
+            k->b = 2; /* "<c" matched */
+            f->phase = X_CALC;
+            return R_OK;
+        }
+        return R_DEAD;
+    case X_END:
+        if (ch != END_TAG[f->b]) return R_DEAD;
+        if (++f->b == 5) f->phase = X_DONE;
+        return R_OK;
+    case X_RES:
+        switch (f->a) {
+        case 0:
+            if (f->b < 7) {
+                if (ch != RES_OPEN[f->b]) return R_DEAD;
+                f->b++;
+                return R_OK;
+            }
+            if (ch == '>') { f->a = 1; return R_OK; }
+            if (ch == '_') { f->a = 5; f->b = 1; return R_OK; }
+            return R_DEAD;
+        case 1:
+        case 2:
+            if (f->a == 1 && ch == '-') { f->a = 2; return R_OK; }
+            if (!is_digit(ch)) return R_DEAD;
+            f->a = 3;
+            f->aux = 1;
+            return R_OK;
+        case 3:
+            if (is_digit(ch)) {
+                if (f->aux >= 20) return R_DEAD;
+                f->aux++;
+                return R_OK;
+            }
+            if (ch != '<') return R_DEAD;
+            f->a = 4;
+            f->b = 1;
+            return R_OK;
+        case 4:
+            if (ch != RES_CLOSE[f->b]) return R_DEAD;
+            if (++f->b == 9) f->phase = X_TEXT;
+            return R_OK;
+        case 5:
+            if (ch != ERR_OPEN[f->b]) return R_DEAD;
+            if (++f->b == 7) f->a = 6;
+            return R_OK;
+        case 6:
+            if (ch == '<') { f->a = 7; f->b = 1; return R_OK; }
+            return printable(ch) ? R_OK : R_DEAD;
+        case 7:
+            if (ch != ERR_CLOSE[f->b]) return R_DEAD;
+            if (++f->b == 15) f->phase = X_TEXT;
+            return R_OK;
+        }
+        return R_DEAD;
+    default:
+        return R_DEAD;
     }
 }
 
@@ -765,6 +857,11 @@ static void child_done(const og *g, ofr *p) {
         p->phase = A_AFTER;
         p->ws = 0;
         break;
+    case F_TEXT: /* a calc span closed: the engine's result comes next */
+        p->phase = X_RES;
+        p->a = 0;
+        p->b = 0;
+        break;
     default:
         abort();
     }
@@ -781,6 +878,7 @@ static int step_frame(const og *g, oconf *c, ofr *f, int ch) {
     case F_LIT: return step_lit(f, ch);
     case F_ENUM: return step_enum(g, f, ch);
     case F_CALC: return step_calc(g, f, ch);
+    case F_TEXT: return step_text(c, f, ch);
     }
     return R_DEAD;
 }
@@ -794,6 +892,10 @@ void oc_start(const og *g, oconf *c) {
     memset(c, 0, sizeof *c);
     if (g->gkind == G_CALC) {
         push(c, F_CALC, -1);
+        return;
+    }
+    if (g->gkind == G_TEXT) {
+        push(c, F_TEXT, -1);
         return;
     }
     ofr *r = push(c, F_ROOT, -1);
@@ -822,11 +924,25 @@ static int feed1(const og *g, oconf *c, int ch) {
     }
 }
 
-/* Feed n bytes; returns how many were accepted before the first refusal
- * (n if all were).  After a refusal the configuration is unspecified. */
+/* Is the next byte one the engine writes (not the model)? */
+int oc_in_engine(const og *g, const oconf *c) {
+    return g->gkind == G_TEXT && c->n == 1 && c->f[0].phase == X_RES;
+}
+
+/* Feed n bytes of the language (engine-written ones included); returns how
+ * many were accepted before the first refusal (n if all were).  After a
+ * refusal the configuration is unspecified. */
 int oc_feed(const og *g, oconf *c, const uint8_t *s, int n) {
     for (int i = 0; i < n; i++)
         if (!feed1(g, c, s[i])) return i;
+    return n;
+}
+
+/* The same for bytes the model writes: a byte where the engine writes is
+ * refused (a model token may end where the engine's region begins). */
+int oc_feed_model(const og *g, oconf *c, const uint8_t *s, int n) {
+    for (int i = 0; i < n; i++)
+        if (oc_in_engine(g, c) || !feed1(g, c, s[i])) return i;
     return n;
 }
 
@@ -834,6 +950,7 @@ int oc_feed(const og *g, oconf *c, const uint8_t *s, int n) {
 int oc_complete(const og *g, const oconf *c) {
     const ofr *f = &c->f[0];
     if (g->gkind == G_CALC) return f->phase == C_DONE;
+    if (g->gkind == G_TEXT) return c->n == 1 && f->phase == X_DONE;
     return c->n == 1 && f->phase == RT_DONE;
 }
 
@@ -844,7 +961,8 @@ static void copy_conf(oconf *dst, const oconf *src) {
 
 /*
  * Token mask for one configuration: bit t is set iff every byte of token t
- * is accepted from the configuration, i.e. p.b(t) is a viable prefix.
+ * is accepted from the configuration as a byte the model writes, i.e.
+ * p.b(t) is a viable prefix reached without writing into the engine's part.
  * Bit t&63 of word t>>6.  Returns the number of bytes walked.
  */
 int64_t oc_mask(const og *g, const oconf *c, const uint8_t *blob, const uint32_t *off, int V,
@@ -857,7 +975,7 @@ int64_t oc_mask(const og *g, const oconf *c, const uint8_t *blob, const uint32_t
         uint32_t a = off[tok], b = off[tok + 1];
         if (b == a) continue; /* empty tokens are never allowed */
         copy_conf(&t, c);
-        int k = oc_feed(g, &t, blob + a, (int)(b - a));
+        int k = oc_feed_model(g, &t, blob + a, (int)(b - a));
         walked += (k < (int)(b - a)) ? k + 1 : k;
         if (k == (int)(b - a)) words[tok >> 6] |= 1ull << (tok & 63);
     }
@@ -916,6 +1034,6 @@ void oc_next_bytes(const og *g, const oconf *c, uint64_t *set4) {
     for (int b = 0; b < 256; b++) {
         copy_conf(&t, c);
         uint8_t s = (uint8_t)b;
-        if (oc_feed(g, &t, &s, 1) == 1) set4[b >> 6] |= 1ull << (b & 63);
+        if (oc_feed_model(g, &t, &s, 1) == 1) set4[b >> 6] |= 1ull << (b & 63);
     }
 }

@@ -30,7 +30,7 @@ def random_walk(og: O.Grammar, toks, n_tokens, rng: W.SplitMix, multi=0.6, gen_c
             for _ in range(64):
                 t = 256 + rng.below(V - 256)
                 c = og.clone(row.conf)
-                if og.feed(c, toks[t]) == len(toks[t]):
+                if og.feed(c, toks[t], model=True) == len(toks[t]):
                     pick = t
                     break
         if pick is None:

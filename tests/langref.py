@@ -332,11 +332,45 @@ def _calc_member(spec, s):
     return i == len(body)
 
 
+_RESULT_RE = re.compile(rb"<result>-?[0-9]{1,20}</result>|<result_error>[\x20-\x3b\x3d-\x7e]*</result_error>")
+_TEXT_RE = re.compile(rb"[\n\x20-\x3b\x3d-\x7e]*")
+
+
+def calc_text_parts(spec, data: bytes):
+    """Split a complete calc_text member into (who, bytes) pieces, who =
+    "model" or "engine"; None if `data` is not a member.  Reads the text
+    left to right with regular expressions and the calc-span validator."""
+    parts = []
+    i = 0
+    while True:
+        m = _TEXT_RE.match(data, i)
+        if m.end() > i:
+            parts.append(("model", data[i:m.end()]))
+        i = m.end()
+        if data[i:] == b"<end>":
+            parts.append(("model", b"<end>"))
+            return parts
+        if not data.startswith(b"<calc>", i):
+            return None
+        j = data.find(b"</calc>", i)
+        if j < 0 or not _calc_member(spec, data[i:j + 7]):
+            return None
+        parts.append(("model", data[i:j + 7]))
+        i = j + 7
+        r = _RESULT_RE.match(data, i)
+        if not r:
+            return None
+        parts.append(("engine", r.group(0)))
+        i = r.end()
+
+
 def member(spec, data: bytes) -> bool:
     """Is `data` (complete) in the language of `spec`?"""
     kind = spec["kind"]
     if kind == "calc":
         return _calc_member(spec, data)
+    if kind == "calc_text":
+        return calc_text_parts(spec, data) is not None
     p = _P(spec, data)
     try:
         if kind == "json_schema":
