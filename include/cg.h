@@ -245,8 +245,10 @@ int cg_advance(const cg_grammar *g, cg_state *d_states, int32_t batch, const int
 
 /*
  * Walk each row's forced byte string: row r takes
- * d_bytes[d_offsets[r] .. d_offsets[r+1]) (device memory; d_offsets has
- * batch+1 entries; an empty string is a no-op, CG_ROW_NOOP).  The engine
+ * d_bytes[d_offsets[r] .. d_offsets[r+1]) (device memory, caller-owned;
+ * d_offsets has batch+1 non-decreasing entries, the last at most the size of
+ * d_bytes -- the kernel does not check them; an empty string is a no-op,
+ * CG_ROW_NOOP).  The engine
  * writes text the model did not choose -- an evaluated result -- and the
  * automaton follows: injection is a grammar transition the model did not
  * choose ("Evaluator aware decoding", "A concrete prototype on llama.cpp").

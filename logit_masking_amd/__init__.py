@@ -234,6 +234,10 @@ class Grammar:
         _dev(status, torch.int32, "status", 1)
         if status.shape[0] < B:
             raise ValueError("status has fewer rows than states")
+        # the kernel trusts the offsets: check them here (one host sync)
+        o = offsets[:B + 1].to(torch.int64)
+        if B and bool(((o[1:] < o[:-1]).any() | (o[0] < 0) | (o[B] > data.numel())).item()):
+            raise ValueError("offsets must be non-decreasing and within data")
         _check(lib().cg_force_bytes(self._h, _ptr(states), B, _ptr(data), _ptr(offsets), _ptr(status),
                                     _stream(stream)))
 

@@ -143,6 +143,9 @@ __device__ inline void stage_table(uint64_t *dst, const uint64_t *__restrict__ s
     }
 }
 
+// Did commit_token take the token (the row and its step count changed)?
+__host__ __device__ inline bool token_taken(int res) { return res != CG_ROW_NOOP && res != CG_ROW_REJECTED; }
+
 // Commit token `id` (its n bytes in words[], 4 per word) to a row: the
 // cg_advance rules.  -1 is a no-op; an id out of range, a finished row or a
 // refused byte leaves the row unchanged (REJECTED); otherwise the row takes

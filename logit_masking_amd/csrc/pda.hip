@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ co
     if (!row) return;
     int st = st0;
     const int res = commit_token(s, st, id, V, n, words, lds_comb, k, gen_cap, forced);
-    if (res == CG_ROW_OK || res == CG_ROW_DONE || res == CG_ROW_CAPPED) {
+    if (token_taken(res)) {
         states[r] = s;
         steps[r] = st;
     }
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ co
 
 // One lane per row: walk the row's forced byte string (the engine writing an
 // evaluated result into the text, "Evaluator aware decoding", "A concrete
-// prototype on llama.cpp").  One forced string counts as one step.
+// prototype on llama.cpp").  Not a generation step: the step count stays.
 __global__ __launch_bounds__(256) void k_force(const uint64_t *__restrict__ comb, uint32_t comb_len, WalkConsts k,
                                                cg_state *__restrict__ states, int B, const uint8_t *__restrict__ bytes,
                                                const uint32_t *__restrict__ offsets, int32_t *__restrict__ status,

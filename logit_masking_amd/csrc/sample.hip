@@ -777,7 +777,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     }
     int stp1 = (int)stp;
     const int res = commit_token(row_state, stp1, pick, adv.V, n, words, lds_comb, adv.k, adv.gen_cap, adv.forced);
-    if (res == CG_ROW_OK || res == CG_ROW_DONE || res == CG_ROW_CAPPED) {
+    if (token_taken(res)) {
         adv.states[r] = row_state;
         adv.steps[r] = stp1;
     }

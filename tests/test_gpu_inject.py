@@ -1,0 +1,350 @@
+"""Engine-written results on the device, against the oracle (page
+"Evaluator aware decoding", "A concrete prototype on llama.cpp": after a
+closed <calc> span the engine evaluates it and injects the result, which the
+grammar follows as a transition the model did not choose; the model itself
+may not write the result block).
+
+* masks of rows parked anywhere in text with calc spans -- inside spans,
+  right at an injection point, part way through a forced result -- are
+  bit-exact against the oracle, and rows waiting for an injection get empty
+  masks;
+* cg_force_bytes statuses and edge cases (empty, refused, finished rows);
+* the whole decode loop: fill -> sample (+ advance) -> on CG_ROW_INJECT the
+  host evaluates the span with cg_eval_calc and forces the result, in lockstep
+  with the oracle (which evaluates with its own evaluator).
+"""
+import numpy as np
+import pytest
+
+import logit_masking_amd as cg
+from logit_masking_amd import workloads as W
+from oracle import oracle as O
+from tests.gpu_util import NTHREADS, say
+
+pytestmark = pytest.mark.gpu
+
+CFG = 6
+SPEC = W.SPECS[CFG]
+
+
+def _setup(V=4096, gen_cap=W.GEN_CAP):
+    blob, off = W.make_vocab(CFG, V)
+    toks = [blob[off[i]:off[i + 1]] for i in range(len(off) - 1)]
+    g = cg.Grammar(W.spec_json(CFG), blob, off, gen_cap=gen_cap)
+    og = O.load_spec(W.spec_json(CFG))
+    return g, og, blob, off, toks
+
+
+def _oracle_result(span: bytes) -> bytes:
+    try:
+        return b"<result>%d</result>" % O.eval_calc(span, O.INT64_RANGE)
+    except O.CalcError as e:
+        return b"<result_error>" + str(e).encode() + b"</result_error>"
+
+
+def _device_result(span: bytes) -> bytes:
+    rc, v = cg.eval_calc(span)
+    if rc == cg.CG_OK:
+        return b"<result>%d</result>" % v
+    assert rc == cg.CG_E_EVAL, (span, v)
+    return b"<result_error>" + v.encode() + b"</result_error>"
+
+
+def _last_span(text: bytes) -> bytes:
+    return text[text.rindex(b"<calc>"):]
+
+
+class _Prefix:
+    """Longest vocabulary token that is a prefix of a byte string."""
+
+    def __init__(self, toks):
+        self.by = {t: i for i, t in enumerate(toks)}
+        self.maxlen = max(len(t) for t in toks)
+
+    def longest(self, rest: bytes, rng=None):
+        cands = [self.by[rest[:k]] for k in range(1, min(len(rest), self.maxlen) + 1) if rest[:k] in self.by]
+        if rng is not None and len(cands) > 1 and rng.uniform() < 0.3:
+            return cands[rng.below(len(cands))]
+        return cands[-1]
+
+
+def _events(og, toks, pre, rng, n_events, split_results=True, stop_at_inject=False):
+    """A row's events, following a script: ("tok", id) for what the model
+    writes, ("force", bytes) for what the engine writes after a closed span
+    (sometimes in two pieces).  The oracle row is advanced alongside.
+    stop_at_inject: end at the first event after which the engine must
+    write (a closed span, or a result forced only in part)."""
+    row = O.Row(og, W.GEN_CAP)
+    segs = W.calc_text_script(rng, SPEC, (1 if stop_at_inject else 0) + rng.below(4))
+    ev = []
+    for seg in segs:
+        pos = 0
+        while pos < len(seg) and len(ev) < n_events:
+            t = pre.longest(seg[pos:], rng)
+            ev.append(("tok", t, row.advance(toks[t])))
+            pos += len(toks[t])
+        if len(ev) >= n_events or row.done:
+            break
+        if stop_at_inject and (rng.uniform() < 0.5 or seg is segs[-2]):
+            if rng.uniform() < 0.5:
+                res = _oracle_result(_last_span(bytes(row.text)))
+                part = res[:1 + rng.below(len(res) - 1)]
+                ev.append(("force", part, row.force(part)))
+            break
+        res = _oracle_result(_last_span(bytes(row.text)))
+        pieces = [res]
+        if split_results and rng.uniform() < 0.4:
+            k = 1 + rng.below(len(res) - 1)
+            pieces = [res[:k], res[k:]]
+        for p in pieces:
+            if len(ev) >= n_events:
+                break
+            ev.append(("force", p, row.force(p)))
+    return ev, row
+
+
+def _replay(g, B, events):
+    """Replay per-row events on the device: at index k every row takes its
+    k-th event, a token through cg_advance and engine bytes through
+    cg_force_bytes (the other call sees -1 / an empty string).  Checks each
+    status against the oracle's; returns (states, steps)."""
+    import torch
+    st = g.new_states(B)
+    g.init_state(st)
+    steps = torch.zeros(B, dtype=torch.int32, device="cuda")
+    status = torch.empty(B, dtype=torch.int32, device="cuda")
+    fstatus = torch.empty(B, dtype=torch.int32, device="cuda")
+    L = max((len(e) for e in events), default=0)
+    for k in range(L):
+        ids = np.full(B, -1, dtype=np.int32)
+        data, offs = bytearray(), [0]
+        for r in range(B):
+            e = events[r][k] if k < len(events[r]) else None
+            if e is not None and e[0] == "tok":
+                ids[r] = e[1]
+            elif e is not None:
+                data += e[1]
+            offs.append(len(data))
+        g.advance(st, torch.from_numpy(ids).cuda(), steps, status)
+        d = torch.frombuffer(bytearray(data) or bytearray(1), dtype=torch.uint8).cuda()
+        g.force_bytes(st, d, torch.tensor(offs, dtype=torch.int32).cuda(), fstatus)
+        s_adv, s_frc = status.cpu().numpy(), fstatus.cpu().numpy()
+        for r in range(B):
+            e = events[r][k] if k < len(events[r]) else None
+            want_adv = e[2] if e is not None and e[0] == "tok" else O.ROW_NOOP
+            want_frc = e[2] if e is not None and e[0] == "force" else O.ROW_NOOP
+            assert s_adv[r] == want_adv, ("advance", k, r, s_adv[r], want_adv, e)
+            assert s_frc[r] == want_frc, ("force", k, r, s_frc[r], want_frc, e)
+    return st, steps
+
+
+def _masks(g, st):
+    import torch
+    mask = torch.full((st.shape[0], g.W), 0x5A5A5A5A5A5A5A5A, dtype=torch.int64, device="cuda")
+    g.fill_bitmask(st, mask)
+    return mask.cpu().numpy().view(np.uint64)
+
+
+@pytest.mark.parametrize("V", [4096, 32000])
+def test_mask_parity_at_injection_points(V):
+    say("inject masks", V)
+    g, og, blob, off, toks = _setup(V)
+    pre = _Prefix(toks)
+    rng = W.SplitMix(0x1A1 + V)
+    B = 96
+    events, rows = [], []
+    for r in range(B):
+        ev, row = _events(og, toks, pre, rng, 1 + rng.below(60), stop_at_inject=r % 4 == 0)
+        events.append(ev)
+        rows.append(row)
+    st, steps = _replay(g, B, events)
+    got = _masks(g, st)
+    want, _ = og.mask_rows([r.conf for r in rows], [r.done for r in rows], blob, off, NTHREADS)
+    n_inject = 0
+    for r in range(B):
+        assert np.array_equal(got[r], want[r]), (r, bytes(rows[r].text))
+        if og.in_engine(rows[r].conf):
+            n_inject += 1
+            assert not got[r].any()
+    assert n_inject >= 5
+    sc = steps.cpu().numpy()
+    assert all(sc[r] == rows[r].step for r in range(B))
+
+
+def test_force_bytes_edge_cases():
+    import torch
+    say("force edge cases")
+    g, og, blob, off, toks = _setup()
+    pre = _Prefix(toks)
+    scripts = [
+        [b"<calc>1+2</calc>"],                 # waits for the engine
+        [b"<calc>1+2</calc>"],
+        [b"ab"],
+        [b"ab <end>"],                         # finished
+        [b"<calc>(4</calc>"[:8]],              # inside a span
+        [b"<calc>9/0</calc>"],
+    ]
+    forced = [b"<result>3</result>", b"<result>3", b"<result>", b"x", b"", b"<result_error>division by zero</result_error>"]
+    B = len(scripts)
+    rows = [O.Row(og, W.GEN_CAP) for _ in range(B)]
+    events = []
+    for r in range(B):
+        ev = []
+        for seg in scripts[r]:
+            pos = 0
+            while pos < len(seg):
+                t = pre.longest(seg[pos:])
+                ev.append(("tok", t, rows[r].advance(toks[t])))
+                pos += len(toks[t])
+        events.append(ev)
+    st, steps = _replay(g, B, events)
+    before = st.clone()
+    data = b"".join(forced)
+    offs = np.cumsum([0] + [len(f) for f in forced]).astype(np.int32)
+    status = torch.empty(B, dtype=torch.int32, device="cuda")
+    g.force_bytes(st, torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda(), torch.from_numpy(offs).cuda(),
+                  status)
+    got = status.cpu().numpy()
+    want = [rows[r].force(forced[r]) for r in range(B)]
+    assert list(got) == want, (list(got), want)
+    assert want == [O.ROW_OK, O.ROW_INJECT, O.ROW_REJECTED, O.ROW_REJECTED, O.ROW_NOOP, O.ROW_OK]
+    # refused and no-op rows are unchanged, byte for byte
+    b0, b1 = before.cpu().numpy(), st.cpu().numpy()
+    for r in range(B):
+        if want[r] in (O.ROW_REJECTED, O.ROW_NOOP):
+            assert np.array_equal(b0[r], b1[r]), r
+    m = _masks(g, st)
+    w, _ = og.mask_rows([x.conf for x in rows], [x.done for x in rows], blob, off, NTHREADS)
+    assert np.array_equal(m, w)
+    assert not m[1].any()  # part way through the result: still the engine's
+
+
+def _bias_toward_script(logits, targets, bonus=40.0):
+    import torch
+    add = torch.zeros(logits.shape, dtype=torch.float32)
+    for r, t in enumerate(targets):
+        if t is not None:
+            add[r, t] = bonus
+    return (logits.float() + add.to(logits.device)).to(logits.dtype)
+
+
+@pytest.mark.parametrize("fused,T", [(True, 0.7), (False, 0.7), (True, 0.0)])
+def test_decode_loop_with_injection(fused, T):
+    """fill -> sample -> advance; rows that report CG_ROW_INJECT get their
+    span evaluated on the host (cg_eval_calc) and the result forced
+    (cg_force_bytes).  The oracle runs the same loop with its own masks,
+    sampler, rows and evaluator; logits lean toward each row's script."""
+    import torch
+    say("inject loop", fused, T)
+    V = 4096
+    g, og, blob, off, toks = _setup(V)
+    pre = _Prefix(toks)
+    B = 12
+    rng = W.SplitMix(0x1A5 + int(fused) + int(T * 10))
+    scripts = [W.calc_text_script(rng, SPEC, 1 + rng.below(3)) for _ in range(B)]
+    st = g.new_states(B)
+    g.init_state(st)
+    stepc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+    fstatus = torch.zeros(B, dtype=torch.int32, device="cuda")
+    mask = torch.empty((B, g.W), dtype=torch.int64, device="cuda")
+    temp = torch.full((B,), float(T), dtype=torch.float32, device="cuda")
+    seeds = np.array(W.row_seeds(CFG, B), dtype=np.uint64)
+    seed_t = torch.from_numpy(seeds.view(np.int64)).cuda()
+    ws = cg.new_workspace(B, V)
+    ids = torch.empty(B, dtype=torch.int32, device="cuda")
+    lp = torch.empty(B, dtype=torch.float32, device="cuda")
+    orows = [O.Row(og, W.GEN_CAP) for _ in range(B)]
+    dev_text = [bytearray() for _ in range(B)]
+    seg_i = [0] * B          # script segment each row is writing
+    seg_start = [0] * B      # where that segment starts in the row's text
+    injections = ties = 0
+    for s in range(160):
+        targets = []
+        for r in range(B):
+            row = orows[r]
+            written = bytes(row.text[seg_start[r]:])
+            seg = scripts[r][min(seg_i[r], len(scripts[r]) - 1)]
+            targets.append(pre.longest(seg[len(written):]) if not row.done and seg.startswith(written)
+                           and len(written) < len(seg) else None)
+        logits = _bias_toward_script(W.make_logits(CFG, s, B, V, "cuda"), targets)
+        g.fill_bitmask(st, mask)
+        if fused:
+            g.sample_advance(logits, mask, temp, seed_t, stepc, ws, ids, lp, st, status)
+        else:
+            cg.apply_mask_sample(logits, mask, temp, seed_t, stepc, ws, ids, lp)
+            g.advance(st, ids, stepc, status)
+        m_dev = mask.cpu().numpy().view(np.uint64)
+        ids_dev, lp_dev, stat = ids.cpu().numpy(), lp.cpu().numpy(), status.cpu().numpy()
+        x = logits.float().cpu().numpy().astype(np.float64)
+        words, _ = og.mask_rows([r.conf for r in orows], [r.done for r in orows], blob, off, NTHREADS)
+        for r in range(B):
+            assert np.array_equal(m_dev[r], words[r]), (s, r, bytes(orows[r].text))
+            bits = O.unpack_mask(words[r], V)
+            i, l, info = O.sample_row(x[r], bits, T, int(seeds[r]), orows[r].step)
+            if i >= 0 and T > 0 and min(info["margin_chunk"], info["margin_token"]) < 1e-6:
+                ties += 1
+                assert bits[ids_dev[r]]
+            else:
+                assert ids_dev[r] == i, (s, r, ids_dev[r], i)
+                if i >= 0:
+                    assert abs(lp_dev[r] - l) < 1e-5
+            tok = None if ids_dev[r] < 0 else toks[ids_dev[r]]
+            want = orows[r].advance(tok)
+            assert stat[r] == want, (s, r, stat[r], want)
+            if tok is not None and want != O.ROW_REJECTED:
+                dev_text[r] += tok
+        # the engine's half of the loop: evaluate closed spans, inject
+        inj = [r for r in range(B) if stat[r] == cg.ROW_INJECT]
+        if inj:
+            data, offs = bytearray(), [0]
+            for r in range(B):
+                if r in inj:
+                    res = _device_result(_last_span(bytes(dev_text[r])))
+                    assert res == _oracle_result(_last_span(bytes(orows[r].text)))
+                    data += res
+                    dev_text[r] += res
+                offs.append(len(data))
+            g.force_bytes(st, torch.frombuffer(data, dtype=torch.uint8).cuda(),
+                          torch.tensor(offs, dtype=torch.int32).cuda(), fstatus)
+            fst = fstatus.cpu().numpy()
+            for r in range(B):
+                if r in inj:
+                    res = bytes(data[offs[r]:offs[r + 1]])
+                    assert fst[r] == orows[r].force(res) == O.ROW_OK
+                    injections += 1
+                    seg_i[r] += 1
+                    seg_start[r] = len(orows[r].text)
+                else:
+                    assert fst[r] == O.ROW_NOOP
+        if all(r.done for r in orows):
+            break
+    assert stepc.cpu().numpy().tolist() == [r.step for r in orows]
+    assert [bytes(t) for t in dev_text] == [bytes(r.text) for r in orows]
+    assert injections >= B // 2, injections
+    assert ties <= 2
+    say("inject loop", fused, T, "injections", injections, "done", sum(r.done for r in orows))
+
+
+def test_full_vocab_sampled_rows():
+    """Config 6 at its full vocabulary (128,256 tokens, 256 rows): the mask
+    of every row checked against the oracle on a sample of rows."""
+    say("inject full vocab")
+    g, og, blob, off, toks = _setup(None)
+    pre = _Prefix(toks)
+    rng = W.SplitMix(0x1A9)
+    B = 256
+    events, rows = [], []
+    for r in range(B):
+        ev, row = _events(og, toks, pre, rng, 1 + rng.below(40), stop_at_inject=r % 4 == 0)
+        events.append(ev)
+        rows.append(row)
+    st, _ = _replay(g, B, events)
+    got = _masks(g, st)
+    chk = list(range(0, B, 8))
+    want, _ = og.mask_rows([rows[r].conf for r in chk], [rows[r].done for r in chk], blob, off, NTHREADS)
+    for k, r in enumerate(chk):
+        assert np.array_equal(got[r], want[k]), r
+    for r in range(B):
+        if og.in_engine(rows[r].conf):
+            assert not got[r].any()
