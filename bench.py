@@ -104,6 +104,165 @@ def cpu_baseline(ids_hist, B, V, blob, off, budget_s):
     }
 
 
+def inject_bench(args):
+    """--inject: the decode loop of text with calc spans (vocab 128,256, batch
+    256, bf16, T = 0.7), the logits leaning toward each row's script so that
+    rows write spans.  After every step the host reads the statuses; rows at
+    CG_ROW_INJECT get their span evaluated (cg_eval_calc) and the result
+    forced (cg_force_bytes) before the next step ("Evaluator aware decoding",
+    "A concrete prototype on llama.cpp": injected-token counts and the
+    latency of each injection).  Prints one JSON line."""
+    import torch
+    import logit_masking_amd as cg
+    from logit_masking_amd import workloads as W
+    cfg = 6
+    c = W.CONFIGS[cfg]
+    B, T = c["B"], c["T"]
+    blob, off = W.make_vocab(cfg)
+    V = len(off) - 1
+    toks = [blob[off[i]:off[i + 1]] for i in range(V)]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    g = cg.Grammar(W.spec_json(cfg), blob, off, gen_cap=W.GEN_CAP)
+    pre = W.ScriptTokens(toks)
+    rng = W.SplitMix(c["seed"])
+    scripts = [W.calc_text_script(rng, W.SPECS[cfg], 2 + rng.below(4)) for _ in range(B)]
+    npool = max(1, min(args.pool, args.steps))
+    pool = [W.make_logits(cfg, s, B, V, dev) for s in range(npool)]
+    st = g.new_states(B, dev)
+    g.init_state(st)
+    steps = torch.zeros(B, dtype=torch.int32, device=dev)
+    status = torch.zeros(B, dtype=torch.int32, device=dev)
+    fstatus = torch.zeros(B, dtype=torch.int32, device=dev)
+    mask = torch.empty((B, g.W), dtype=torch.int64, device=dev)
+    temp = torch.full((B,), T, dtype=torch.float32, device=dev)
+    seed = torch.from_numpy(np.array(W.row_seeds(cfg, B), dtype=np.uint64).view(np.int64)).to(dev)
+    ws = cg.new_workspace(B, V, dev)
+    fws = g.new_fill_workspace(B, dev)
+    ids = torch.empty(B, dtype=torch.int32, device=dev)
+    lp = torch.empty(B, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    texts = [bytearray() for _ in range(B)]
+    seg_i, seg_start = [0] * B, [0] * B
+    done = [False] * B
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    dev_step_ms, inj_wall, inj_eval, inj_kernel, inj_rows, inj_bytes, inj_toks = [], [], [], [], [], [], []
+    # load every kernel and the evaluator once before anything is timed
+    g.force_bytes(st, torch.zeros(1, dtype=torch.uint8, device=dev), torch.zeros(B + 1, dtype=torch.int32, device=dev),
+                  fstatus, stream)
+    cg.eval_calc(b"<calc>1</calc>")
+    torch.cuda.synchronize()
+    n_err = 0
+    for s in range(args.warmup + args.steps):
+        # untimed: lean each row's logits toward the next token of its script
+        ri, ti = [], []
+        for r in range(B):
+            if done[r]:
+                continue
+            seg = scripts[r][min(seg_i[r], len(scripts[r]) - 1)]
+            written = bytes(texts[r][seg_start[r]:])
+            if seg.startswith(written) and len(written) < len(seg):
+                ri.append(r)
+                ti.append(pre.longest(seg[len(written):]))
+        x = pool[s % npool].clone()
+        if ri:
+            ri_t, ti_t = torch.tensor(ri, device=dev), torch.tensor(ti, device=dev)
+            x[ri_t, ti_t] = x[ri_t, ti_t] + 40.0
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        g.fill_bitmask(st, mask, fws, stream)
+        g.sample_advance(x, mask, temp, seed, steps, ws, ids, lp, st, status, stream)
+        ev[1].record(stream)
+        ids_h = ids.cpu().numpy()          # the engine reads the picks back anyway
+        stat_h = status.cpu().numpy()
+        dev_step_ms.append(ev[0].elapsed_time(ev[1]))
+        for r in range(B):
+            if ids_h[r] >= 0 and stat_h[r] not in (cg.ROW_REJECTED, cg.ROW_NOOP):
+                texts[r] += toks[ids_h[r]]
+            if stat_h[r] in (cg.ROW_DONE, cg.ROW_CAPPED):
+                done[r] = True
+        inj = [r for r in range(B) if stat_h[r] == cg.ROW_INJECT]
+        if not inj:
+            if all(done):
+                break
+            continue
+        # the injection: evaluate the closed spans on the host, force the results
+        t0 = time.perf_counter()
+        data, offs = bytearray(), [0]
+        k = 0
+        for r in range(B):
+            if k < len(inj) and inj[k] == r:
+                rc, v = cg.eval_calc(bytes(texts[r][texts[r].rindex(b"<calc>"):]))
+                if rc == cg.CG_OK:
+                    res = b"<result>%d</result>" % v
+                else:
+                    res = b"<result_error>" + v.encode() + b"</result_error>"
+                    n_err += 1
+                data += res
+                texts[r] += res
+                k += 1
+            offs.append(len(data))
+        t1 = time.perf_counter()
+        h_data = torch.frombuffer(data, dtype=torch.uint8).pin_memory()
+        h_offs = torch.tensor(offs, dtype=torch.int32).pin_memory()
+        d_data = h_data.to(dev, non_blocking=True)
+        d_offs = h_offs.to(dev, non_blocking=True)
+        ev[2].record(stream)
+        g.force_bytes(st, d_data, d_offs, fstatus, stream)
+        ev[3].record(stream)
+        fst = fstatus.cpu().numpy()
+        t2 = time.perf_counter()
+        for r in inj:
+            if fst[r] != cg.ROW_OK:
+                raise RuntimeError(f"forced result refused on row {r}: status {fst[r]}")
+            seg_i[r] += 1
+            seg_start[r] = len(texts[r])
+        if s >= args.warmup:
+            inj_wall.append(t2 - t0)
+            inj_eval.append(t1 - t0)
+            inj_kernel.append(ev[2].elapsed_time(ev[3]))
+            inj_rows.append(len(inj))
+            for r in inj:
+                res = bytes(data[offs[r]:offs[r + 1]])
+                inj_bytes.append(len(res))
+                inj_toks.append(pre.count(res))
+    n_inj = int(sum(inj_rows))
+    wall = np.array(inj_wall) * 1e6
+    ev_us = np.array(inj_eval) * 1e6 / np.maximum(1, np.array(inj_rows))
+    out = {
+        "metric": "injection latency per decode step with injections (host evaluation + forced-byte walk), "
+                  "median us",
+        "value": round(pct(wall, 50), 2) if len(wall) else None,
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": len(dev_step_ms) - args.warmup,
+        "warmup": args.warmup,
+        "higher_is_better": False,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "text with calc spans, vocab 128256, batch 256, bf16 N(0,9) logits leaning +40 "
+                               "toward each row's script, T=0.7, engine cap 2048", "batch": B, "vocab": V},
+        "injection_steps": len(wall),
+        "injected_rows": n_inj,
+        "error_results": n_err,
+        "us_per_injection_step": {"mean": round(float(wall.mean()), 2), "p50": round(pct(wall, 50), 2),
+                                  "p99": round(pct(wall, 99), 2)} if len(wall) else None,
+        "injected_rows_per_step": round(float(np.mean(inj_rows)), 2) if inj_rows else None,
+        "us_host_eval_per_span": {"p50": round(pct(ev_us, 50), 2), "p99": round(pct(ev_us, 99), 2)} if len(ev_us) else None,
+        "us_force_kernel": {"p50": round(1e3 * pct(inj_kernel, 50), 2), "p99": round(1e3 * pct(inj_kernel, 99), 2)}
+        if inj_kernel else None,
+        "injected_bytes_mean": round(float(np.mean(inj_bytes)), 2) if inj_bytes else None,
+        "injected_tokens_mean": round(float(np.mean(inj_toks)), 2) if inj_toks else None,
+        "us_device_step": {"p50": round(1e3 * pct(dev_step_ms[args.warmup:], 50), 2),
+                           "mean": round(1e3 * float(np.mean(dev_step_ms[args.warmup:])), 2)},
+        "note": "latency = from the step's statuses on the host to the forced statuses back on the host: "
+                "span evaluation for every row at CG_ROW_INJECT, the results' bytes to the device, "
+                "cg_force_bytes, and the statuses read back",
+        "rows_done": int(sum(done)),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,11 +275,17 @@ def main():
                     help="cg_apply_mask_sample and cg_advance as two launches instead of cg_sample_advance")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 64 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--inject", action="store_true",
+                    help="measure result injection on text with calc spans instead (its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: rows shard across GPUs with no exchange, and multi-GPU runs are not "
               "part of this build", file=sys.stderr)
         sys.exit(2)
+
+    if args.inject:
+        inject_bench(args)
+        return
 
     import torch
     import logit_masking_amd as cg

@@ -101,6 +101,9 @@ typedef struct {
     int32_t table_entries;  /* packed transition slots (8 bytes each) */
     int32_t table_bytes;    /* bytes of the transition table staged per workgroup */
     double compile_ms;      /* host time of parse + build + pack */
+    int32_t state_masks;    /* states whose plain-configuration mask was computed once at
+                               compile time (0: none, or the table would exceed 64 MiB) */
+    int32_t pad;
 } cg_info;
 
 /*
@@ -246,9 +249,9 @@ int cg_advance(const cg_grammar *g, cg_state *d_states, int32_t batch, const int
 /*
  * Walk each row's forced byte string: row r takes
  * d_bytes[d_offsets[r] .. d_offsets[r+1]) (device memory, caller-owned;
- * d_offsets has batch+1 non-decreasing entries, the last at most the size of
- * d_bytes -- the kernel does not check them; an empty string is a no-op,
- * CG_ROW_NOOP).  The engine
+ * d_bytes holds n_bytes bytes, d_offsets batch+1 entries).  An empty string
+ * is a no-op (CG_ROW_NOOP); offsets out of order or past n_bytes give
+ * CG_ROW_REJECTED with nothing read.  The engine
  * writes text the model did not choose -- an evaluated result -- and the
  * automaton follows: injection is a grammar transition the model did not
  * choose ("Evaluator aware decoding", "A concrete prototype on llama.cpp").
@@ -260,7 +263,7 @@ int cg_advance(const cg_grammar *g, cg_state *d_states, int32_t batch, const int
  * the cap are untouched.  Tokenizing the forced text for the model's own
  * forward pass is the engine's business; the automaton walks bytes.
  */
-int cg_force_bytes(const cg_grammar *g, cg_state *d_states, int32_t batch, const uint8_t *d_bytes,
+int cg_force_bytes(const cg_grammar *g, cg_state *d_states, int32_t batch, const uint8_t *d_bytes, size_t n_bytes,
                    const uint32_t *d_offsets, int32_t *d_status, void *stream);
 
 /*

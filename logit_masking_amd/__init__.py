@@ -40,7 +40,7 @@ class Info(ctypes.Structure):
     _fields_ = [("vocab_size", ctypes.c_int32), ("words_per_row", ctypes.c_int32),
                 ("max_token_len", ctypes.c_int32), ("n_states", ctypes.c_int32),
                 ("table_entries", ctypes.c_int32), ("table_bytes", ctypes.c_int32),
-                ("compile_ms", ctypes.c_double)]
+                ("compile_ms", ctypes.c_double), ("state_masks", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,7 +67,7 @@ def lib():
         L.cg_sample_workspace_bytes.restype = sz
         L.cg_apply_mask_sample.argtypes = [vp, i32, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.cg_advance.argtypes = [vp, vp, i32, vp, vp, vp, vp]
-        L.cg_force_bytes.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+        L.cg_force_bytes.argtypes = [vp, vp, i32, vp, sz, vp, vp, vp]
         L.cg_eval_calc.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_int64)]
         L.cg_sample_advance.argtypes = [vp, vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
@@ -234,12 +234,8 @@ class Grammar:
         _dev(status, torch.int32, "status", 1)
         if status.shape[0] < B:
             raise ValueError("status has fewer rows than states")
-        # the kernel trusts the offsets: check them here (one host sync)
-        o = offsets[:B + 1].to(torch.int64)
-        if B and bool(((o[1:] < o[:-1]).any() | (o[0] < 0) | (o[B] > data.numel())).item()):
-            raise ValueError("offsets must be non-decreasing and within data")
-        _check(lib().cg_force_bytes(self._h, _ptr(states), B, _ptr(data), _ptr(offsets), _ptr(status),
-                                    _stream(stream)))
+        _check(lib().cg_force_bytes(self._h, _ptr(states), B, _ptr(data), data.numel(), _ptr(offsets),
+                                    _ptr(status), _stream(stream)))
 
 
 def eval_calc(span: bytes):

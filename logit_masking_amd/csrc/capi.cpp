@@ -14,8 +14,8 @@ const char *last_error();
 int launch_init(const cg_grammar *g, cg_state *states, int B, hipStream_t st);
 int launch_advance(const cg_grammar *g, cg_state *states, int B, const int32_t *ids, int32_t *steps,
                    int32_t *status, hipStream_t st);
-int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *bytes, const uint32_t *offsets,
-                 int32_t *status, hipStream_t st);
+int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *bytes, uint64_t n_bytes,
+                 const uint32_t *offsets, int32_t *status, hipStream_t st);
 int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws,
                 hipStream_t st);
 int fill_plan_stride(const cg_grammar *g);
@@ -54,6 +54,11 @@ void release(cg_grammar *g) {
         (void)hipFree(g->dev.tokinfo);
         (void)hipFree(g->dev.legal);
         (void)hipFree(g->dev.forced);
+        (void)hipFree(g->dev.state_mask);
+        (void)hipFree(g->dev.closebits);
+        (void)hipFree(g->dev.retmask);
+        (void)hipFree(g->dev.rq_idx);
+        (void)hipFree(g->dev.smask_idx);
         (void)hipFree(g->dev.lex_idlen);
         (void)hipFree(g->dev.lex_jump);
         (void)hipFree(g->dev.lex_w);
@@ -90,8 +95,11 @@ uint32_t string_summary(const cg_grammar *g, const uint8_t *s, uint32_t n) {
 // Candidate tables of the fill kernel (see DeviceTables).  In lexicographic
 // order, tokens sharing their first bytes sit in the same 64-token tiles: a
 // row then visits only tiles holding a key it can accept.
+constexpr size_t kCloseMaskBudget = 64ull << 20;  // bytes of per-resume-state closing masks
+
 struct FillHost {
-    std::vector<uint64_t> legal, strbits;
+    std::vector<uint64_t> legal, strbits, closebits, retmask;
+    std::vector<int32_t> rq_idx;
     std::vector<uint32_t> lex_idlen, lex_jump, lex_w, q_idlen, q_posch, q_w;
     std::vector<uint2> lex_tile, q_tile;
 };
@@ -173,9 +181,100 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
         for (uint32_t c = tok_chars(tokinfo[t]); c < (uint32_t)kStrBitsets; c++)
             f.strbits[(size_t)c * Wv + (t >> 6)] |= 1ull << (t & 63);
     }
+    // Tokens that close the string: the content before the quote fits a
+    // budget of c code points (closebits[c]), and the bytes after the quote
+    // are accepted from resume state R with no open container (retmask[R]).
+    // A row inside a string with no open container then needs no walk:
+    // strbits[c] | (closebits[c] & retmask[ret]).
+    f.closebits.assign((size_t)kStrBitsets * Wv, 0ull);
+    f.rq_idx.assign(g->k.q_limit, -1);
+    if (g->k.s_body >= g->k.q_limit) return;
+    std::vector<uint32_t> closers;
+    for (uint32_t t : q)
+        if (t != kPad) closers.push_back(t);
+    for (uint32_t t : closers)
+        for (uint32_t c = tok_chars(tokinfo[t]); c < (uint32_t)kStrBitsets; c++)
+            f.closebits[(size_t)c * Wv + (t >> 6)] |= 1ull << (t & 63);
+    std::vector<uint32_t> resume;
+    for (uint32_t i = 0; i < g->comb_len; i++) {
+        const uint64_t e = g->host_comb[i];
+        const uint32_t owner = (uint32_t)e & 0xFFFFu, op = (uint32_t)(e >> 32) & 0xFu;
+        if (owner < g->k.q_limit && op == OP_STR_OPEN) resume.push_back(((uint32_t)e >> 16) & 0xFFFFu);
+    }
+    std::sort(resume.begin(), resume.end());
+    resume.erase(std::unique(resume.begin(), resume.end()), resume.end());
+    if (resume.size() * Wv * 8 > kCloseMaskBudget) return;
+    f.retmask.assign(resume.size() * Wv, 0ull);
+    for (size_t j = 0; j < resume.size(); j++) {
+        f.rq_idx[resume[j]] = (int32_t)j;
+        for (uint32_t t : closers) {
+            Walker w;
+            w.q = resume[j];
+            w.ret = g->k.start;
+            w.cnt = 0;
+            w.ws = 0;
+            w.depth = 0;
+            w.stk = 0;
+            bool ok = true;
+            for (uint32_t i = tok_pos(tokinfo[t]) + 1; ok && i < len(t); i++)
+                ok = step_byte(w, bytes(t)[i], g->host_comb, g->k);
+            if (ok) f.retmask[j * Wv + (t >> 6)] |= 1ull << (t & 63);
+        }
+    }
 }
 
 }  // namespace
+
+// Masks of the plain configurations (a live state outside strings, no
+// whitespace run, no open container), computed once with the fill kernels
+// themselves; the fill then copies such a row's mask instead of walking
+// tokens.  A state's registers other than the whitespace run and the
+// container stack are only read inside strings, so the mask of a plain
+// configuration depends on the state alone.  Skipped (no table) when it
+// would exceed kStateMaskBudget bytes.
+constexpr size_t kStateMaskBudget = 64ull << 20;
+
+int build_state_masks(cg_grammar *g) {
+    const size_t Wv = ((size_t)g->V + 63) / 64, n = g->plain_q.size();
+    if (n == 0 || n * Wv * 8 > kStateMaskBudget) return CG_OK;
+    std::vector<cg_state> st(n);
+    for (size_t i = 0; i < n; i++) {
+        cg_state &c = st[i];
+        memset(&c, 0, sizeof c);
+        c.q = (uint16_t)g->plain_q[i];
+        c.ret = (uint16_t)g->k.start;
+    }
+    std::vector<int32_t> idx(g->k.q_limit, -1);
+    for (size_t i = 0; i < n; i++) idx[g->plain_q[i]] = (int32_t)i;
+    cg_state *d_st = nullptr;
+    void *d_ws = nullptr;
+    uint64_t *d_mask = nullptr;
+    int rc = CG_OK;
+    const size_t ws_bytes = (size_t)fill_plan_stride(g) * 4 * n;
+    if (upload(&d_st, st.data(), n) != CG_OK || hipMalloc(&d_ws, ws_bytes) != hipSuccess ||
+        hipMalloc((void **)&d_mask, n * Wv * 8) != hipSuccess) {
+        set_error("state masks: allocation failed: %s", hipGetErrorString(hipGetLastError()));
+        rc = CG_E_DEVICE;
+    }
+    if (rc == CG_OK) rc = launch_fill(g, d_st, (int)n, d_mask, (int)Wv, d_ws, nullptr);
+    if (rc == CG_OK && hipStreamSynchronize(nullptr) != hipSuccess) {
+        set_error("state masks: %s", hipGetErrorString(hipGetLastError()));
+        rc = CG_E_DEVICE;
+    }
+    if (rc == CG_OK && upload(&g->dev.smask_idx, idx.data(), idx.size()) != CG_OK) {
+        set_error("state masks: upload failed");
+        rc = CG_E_DEVICE;
+    }
+    (void)hipFree(d_st);
+    (void)hipFree(d_ws);
+    if (rc != CG_OK) {
+        (void)hipFree(d_mask);
+        return rc;
+    }
+    g->dev.state_mask = d_mask;
+    g->n_smask = (int32_t)n;
+    return CG_OK;
+}
 
 extern "C" {
 
@@ -255,10 +354,18 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
             upload(&g->dev.q_w, f.q_w.data(), f.q_w.size()) ||
             upload(&g->dev.q_tile, f.q_tile.data(), f.q_tile.size()) ||
             upload(&g->dev.strbits, f.strbits.data(), f.strbits.size()) ||
+            upload(&g->dev.closebits, f.closebits.data(), f.closebits.size()) ||
+            (!f.retmask.empty() && (upload(&g->dev.retmask, f.retmask.data(), f.retmask.size()) ||
+                                    upload(&g->dev.rq_idx, f.rq_idx.data(), f.rq_idx.size()))) ||
             (g->has_forced && upload(&g->dev.forced, g->host_forced.data(), g->host_forced.size()))) {
             set_error("device upload failed: %s", hipGetErrorString(hipGetLastError()));
             release(g);
             return CG_E_DEVICE;
+        }
+        rc = build_state_masks(g);
+        if (rc != CG_OK) {
+            release(g);
+            return rc;
         }
     }
     *out = g;
@@ -276,6 +383,8 @@ int cg_grammar_info(const cg_grammar *g, cg_info *info) {
     info->table_entries = (int32_t)g->comb_len;
     info->table_bytes = (int32_t)(g->comb_len * sizeof(uint64_t));
     info->compile_ms = g->compile_ms;
+    info->state_masks = g->n_smask;
+    info->pad = 0;
     return CG_OK;
 }
 
@@ -351,11 +460,12 @@ int cg_advance(const cg_grammar *g, cg_state *d_states, int32_t batch, const int
     return launch_advance(g, d_states, batch, d_token_ids, d_step, d_status, (hipStream_t)stream);
 }
 
-int cg_force_bytes(const cg_grammar *g, cg_state *d_states, int32_t batch, const uint8_t *d_bytes,
+int cg_force_bytes(const cg_grammar *g, cg_state *d_states, int32_t batch, const uint8_t *d_bytes, size_t n_bytes,
                    const uint32_t *d_offsets, int32_t *d_status, void *stream) {
     if (!on_device(g)) return arg_error("grammar has no device tables");
-    if (batch < 0 || (batch > 0 && (!d_states || !d_offsets || !d_status))) return arg_error("bad arguments");
-    return launch_force(g, d_states, batch, d_bytes, d_offsets, d_status, (hipStream_t)stream);
+    if (batch < 0 || (batch > 0 && (!d_states || !d_offsets || !d_status)) || (n_bytes > 0 && !d_bytes))
+        return arg_error("bad arguments");
+    return launch_force(g, d_states, batch, d_bytes, (uint64_t)n_bytes, d_offsets, d_status, (hipStream_t)stream);
 }
 
 int cg_eval_calc(const uint8_t *span, size_t len, int64_t *value) {

@@ -226,6 +226,18 @@ struct DeviceTables {
     uint32_t *tokinfo = nullptr;  // [V] length + string-body summary
     uint64_t *legal = nullptr;    // [q_limit][4] bytes with a transition out of state q (256-bit set)
     uint32_t *forced = nullptr;   // [ceil(q_limit / 32)] bit q: engine-written state (null: none)
+    // Masks of plain configurations, computed once: state_mask[smask_idx[q]]
+    // is the mask of (q, no whitespace run, no open container) for a state
+    // q outside strings; smask_idx[q] < 0 where there is none (null: no table).
+    uint64_t *state_mask = nullptr;  // [n_smask][Wv]
+    int32_t *smask_idx = nullptr;    // [q_limit]
+    // Tokens that close a string: closebits[c] = the content before the
+    // quote fits a budget of c code points; retmask[rq_idx[R]] = the bytes
+    // after the quote are accepted from resume state R with no open
+    // container (rq_idx null: no table).
+    uint64_t *closebits = nullptr;   // [kStrBitsets][Wv]
+    uint64_t *retmask = nullptr;     // [n_resume][Wv]
+    int32_t *rq_idx = nullptr;       // [q_limit]
     // Fill candidates: the non-empty tokens in lexicographic order, padded
     // with empty entries (idlen 0) to whole 64-token tiles.
     uint32_t *lex_idlen = nullptr;   // [lex_tiles * 64] id | len << 24
@@ -262,6 +274,8 @@ struct cg_grammar {
     uint64_t *host_comb = nullptr;
     std::vector<uint32_t> host_forced;  // bit q: state q is inside an engine-written region
     bool has_forced = false;
+    std::vector<uint32_t> plain_q;  // live states outside strings (candidates of the state-mask table)
+    int32_t n_smask = 0;            // rows of dev.state_mask
     cg::DeviceTables dev;
 };
 

@@ -955,6 +955,10 @@ void trim_and_pack(Builder &B, cg_grammar *g) {
     for (int q : order)
         if (B.st[q].forced) g->host_forced[base[q] >> 5] |= 1u << (base[q] & 31);
     g->has_forced = std::any_of(order.begin(), order.end(), [&](int q) { return B.st[q].forced; });
+    g->plain_q.clear();
+    for (int q : order)
+        if (!B.st[q].string_state && !B.st[q].forced && q != B.accept) g->plain_q.push_back((uint32_t)base[q]);
+    std::sort(g->plain_q.begin(), g->plain_q.end());
     g->host_comb = comb;
     g->comb_len = comb_len;
     g->n_states = (int)order.size();

@@ -86,8 +86,8 @@ __global__ __launch_bounds__(256) void k_advance(const uint64_t *__restrict__ co
 // prototype on llama.cpp").  Not a generation step: the step count stays.
 __global__ __launch_bounds__(256) void k_force(const uint64_t *__restrict__ comb, uint32_t comb_len, WalkConsts k,
                                                cg_state *__restrict__ states, int B, const uint8_t *__restrict__ bytes,
-                                               const uint32_t *__restrict__ offsets, int32_t *__restrict__ status,
-                                               const uint32_t *__restrict__ forced) {
+                                               uint64_t n_bytes, const uint32_t *__restrict__ offsets,
+                                               int32_t *__restrict__ status, const uint32_t *__restrict__ forced) {
     extern __shared__ uint64_t lds_comb[];
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     const bool row = r < B;
@@ -101,11 +101,13 @@ __global__ __launch_bounds__(256) void k_force(const uint64_t *__restrict__ comb
     stage_table(lds_comb, comb, comb_len);
     __syncthreads();
     if (!row) return;
-    if (b1 <= b0) {
+    if (b1 == b0) {
         status[r] = CG_ROW_NOOP;
         return;
     }
-    if ((s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) || s.q >= k.q_limit || s.ret >= k.q_limit) {
+    // offsets out of order or past the bytes: refused, nothing read
+    if (b1 < b0 || b1 > n_bytes || (s.flags & (CG_FLAG_DONE | CG_FLAG_CAPPED)) || s.q >= k.q_limit ||
+        s.ret >= k.q_limit) {
         status[r] = CG_ROW_REJECTED;
         return;
     }
@@ -182,6 +184,10 @@ struct FillArgs {
     unsigned long long *mask;
     int words_per_row;
     const uint32_t *forced;  // engine-written states: empty mask (null: none)
+    const uint64_t *state_mask;  // precomputed masks of plain configurations (null: none)
+    const int32_t *smask_idx;
+    const uint64_t *closebits, *retmask;  // string rows with no open container (rq_idx null: none)
+    const int32_t *rq_idx;
     uint32_t *plan;       // per row: [0] listed tiles, [1..] their indices
     int plan_stride;      // u32 per row
     int B;
@@ -319,10 +325,23 @@ __global__ __launch_bounds__(kPlanThreads) void k_fill_plan(FillArgs a) {
         const int t = tid + i * kPlanThreads;
         kk[i] = t < n_all ? tkeys[t] : make_uint2(1, 0);
     }
-    // base words
-    const uint64_t *base = in_str ? a.strbits + (size_t)min(s.cnt, (uint32_t)kStrBitsets - 1u) * a.Wv : nullptr;
-    for (int i = tid; i < a.Wv; i += kPlanThreads) out[i] = base ? base[i] : 0ull;
-    if (!live) {
+    // base words: zero; inside a string, the tokens that stay inside within
+    // the budget, and with no open container also the tokens that close the
+    // string and go on legally (then nothing is walked); in a plain
+    // configuration (no whitespace run, no open container, outside
+    // strings), the state's whole precomputed mask
+    const bool plain = live && s.depth == 0 && s.stk == 0;
+    const int sidx = (plain && !in_str && a.smask_idx && s.ws == 0) ? a.smask_idx[s.q] : -1;
+    const int ridx = (plain && in_str && a.rq_idx) ? a.rq_idx[s.ret] : -1;
+    const size_t c_off = (size_t)min(s.cnt, (uint32_t)kStrBitsets - 1u) * a.Wv;
+    const uint64_t *base = in_str ? a.strbits + c_off : sidx >= 0 ? a.state_mask + (size_t)sidx * a.Wv : nullptr;
+    if (ridx >= 0) {
+        const uint64_t *cb = a.closebits + c_off, *rm = a.retmask + (size_t)ridx * a.Wv;
+        for (int i = tid; i < a.Wv; i += kPlanThreads) out[i] = base[i] | (cb[i] & rm[i]);
+    } else {
+        for (int i = tid; i < a.Wv; i += kPlanThreads) out[i] = base ? base[i] : 0ull;
+    }
+    if (!live || sidx >= 0 || ridx >= 0) {
         if (tid == 0) plan[0] = 0;
         return;
     }
@@ -498,12 +517,12 @@ int launch_advance(const cg_grammar *g, cg_state *states, int B, const int32_t *
     return launch_status("advance");
 }
 
-int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *bytes, const uint32_t *offsets,
-                 int32_t *status, hipStream_t st) {
+int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *bytes, uint64_t n_bytes,
+                 const uint32_t *offsets, int32_t *status, hipStream_t st) {
     if (B == 0) return CG_OK;
     const size_t lds = (size_t)g->comb_len * sizeof(uint64_t);
     hipLaunchKernelGGL(k_force, dim3((B + 255) / 256), dim3(256), lds, st, g->dev.comb, g->comb_len, g->k, states, B,
-                       bytes, offsets, status, g->dev.forced);
+                       bytes, n_bytes, offsets, status, g->dev.forced);
     return launch_status("force_bytes");
 }
 
@@ -549,6 +568,11 @@ static int launch_fill_nw(const cg_grammar *g, const cg_state *states, int B, ui
     a.mask = (unsigned long long *)mask;
     a.words_per_row = wpr;
     a.forced = g->dev.forced;
+    a.state_mask = g->dev.state_mask;
+    a.smask_idx = g->dev.state_mask ? g->dev.smask_idx : nullptr;
+    a.closebits = g->dev.closebits;
+    a.retmask = g->dev.retmask;
+    a.rq_idx = g->dev.retmask ? g->dev.rq_idx : nullptr;
     a.plan = (uint32_t *)ws;
     a.plan_stride = fill_plan_stride(g);
     a.B = B;

@@ -430,3 +430,34 @@ def calc_text_script(rng: SplitMix, spec, n_spans: int) -> list:
         segs.append(prose() + b"<calc>" + lead + calc_expr(rng, spec) + tail + b"</calc>")
     segs.append(prose() + b"<end>")
     return segs
+
+
+class ScriptTokens:
+    """The vocabulary token that spells the next bytes of a script: the
+    longest token that is a prefix of the remaining bytes (how the scripted
+    runs lean the logits toward a row's script; an input recipe, not a
+    tokenizer of the method)."""
+
+    def __init__(self, toks):
+        self.by = {t: i for i, t in enumerate(toks)}
+        self.maxlen = max(len(t) for t in toks)
+
+    def longest(self, rest: bytes, rng: SplitMix | None = None) -> int:
+        cands = [self.by[rest[:k]] for k in range(1, min(len(rest), self.maxlen) + 1) if rest[:k] in self.by]
+        if rng is not None and len(cands) > 1 and rng.uniform() < 0.3:
+            return cands[rng.below(len(cands))]
+        return cands[-1]
+
+    def count(self, data: bytes) -> int:
+        """Tokens of a greedy longest-match spelling of `data`."""
+        n = pos = 0
+        while pos < len(data):
+            pos += len(self.longest_bytes(data[pos:]))
+            n += 1
+        return n
+
+    def longest_bytes(self, rest: bytes) -> bytes:
+        for k in range(min(len(rest), self.maxlen), 0, -1):
+            if rest[:k] in self.by:
+                return rest[:k]
+        raise ValueError("byte not in the vocabulary")

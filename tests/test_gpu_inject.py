@@ -54,20 +54,6 @@ def _last_span(text: bytes) -> bytes:
     return text[text.rindex(b"<calc>"):]
 
 
-class _Prefix:
-    """Longest vocabulary token that is a prefix of a byte string."""
-
-    def __init__(self, toks):
-        self.by = {t: i for i, t in enumerate(toks)}
-        self.maxlen = max(len(t) for t in toks)
-
-    def longest(self, rest: bytes, rng=None):
-        cands = [self.by[rest[:k]] for k in range(1, min(len(rest), self.maxlen) + 1) if rest[:k] in self.by]
-        if rng is not None and len(cands) > 1 and rng.uniform() < 0.3:
-            return cands[rng.below(len(cands))]
-        return cands[-1]
-
-
 def _events(og, toks, pre, rng, n_events, split_results=True, stop_at_inject=False):
     """A row's events, following a script: ("tok", id) for what the model
     writes, ("force", bytes) for what the engine writes after a closed span
@@ -149,7 +135,7 @@ def _masks(g, st):
 def test_mask_parity_at_injection_points(V):
     say("inject masks", V)
     g, og, blob, off, toks = _setup(V)
-    pre = _Prefix(toks)
+    pre = W.ScriptTokens(toks)
     rng = W.SplitMix(0x1A1 + V)
     B = 96
     events, rows = [], []
@@ -175,7 +161,7 @@ def test_force_bytes_edge_cases():
     import torch
     say("force edge cases")
     g, og, blob, off, toks = _setup()
-    pre = _Prefix(toks)
+    pre = W.ScriptTokens(toks)
     scripts = [
         [b"<calc>1+2</calc>"],                 # waits for the engine
         [b"<calc>1+2</calc>"],
@@ -217,6 +203,14 @@ def test_force_bytes_edge_cases():
     w, _ = og.mask_rows([x.conf for x in rows], [x.done for x in rows], blob, off, NTHREADS)
     assert np.array_equal(m, w)
     assert not m[1].any()  # part way through the result: still the engine's
+    # offsets out of order or past the bytes: refused, rows unchanged
+    before = st.clone()
+    bad = torch.tensor([0, 4, 2, 2, 40, 3, 3], dtype=torch.int32, device="cuda")
+    g.force_bytes(st, torch.frombuffer(bytearray(b"text" * 3), dtype=torch.uint8).cuda(), bad, status)
+    got = status.cpu().numpy().tolist()
+    assert got[1] == O.ROW_REJECTED and got[3] == O.ROW_REJECTED and got[4] == O.ROW_REJECTED
+    assert got[2] == O.ROW_NOOP and got[5] == O.ROW_NOOP
+    assert np.array_equal(before.cpu().numpy()[1:], st.cpu().numpy()[1:])
 
 
 def _bias_toward_script(logits, targets, bonus=40.0):
@@ -238,7 +232,7 @@ def test_decode_loop_with_injection(fused, T):
     say("inject loop", fused, T)
     V = 4096
     g, og, blob, off, toks = _setup(V)
-    pre = _Prefix(toks)
+    pre = W.ScriptTokens(toks)
     B = 12
     rng = W.SplitMix(0x1A5 + int(fused) + int(T * 10))
     scripts = [W.calc_text_script(rng, SPEC, 1 + rng.below(3)) for _ in range(B)]
@@ -331,7 +325,7 @@ def test_full_vocab_sampled_rows():
     of every row checked against the oracle on a sample of rows."""
     say("inject full vocab")
     g, og, blob, off, toks = _setup(None)
-    pre = _Prefix(toks)
+    pre = W.ScriptTokens(toks)
     rng = W.SplitMix(0x1A9)
     B = 256
     events, rows = [], []

@@ -86,6 +86,35 @@ def test_mask_parity(torch_dev, cfg, B, V, max_len):
             assert got[r].any()
 
 
+def _plain(states_np, g_start_is_string=False):
+    """Rows in a plain configuration: no whitespace run, no open container
+    (the fill copies such a row's precomputed state mask)."""
+    ws = states_np[:, 17]
+    depth = states_np[:, 16]
+    stk = states_np[:, 8:16].copy().view(np.uint64)[:, 0]
+    return (ws == 0) & (depth == 0) & (stk == 0) & (states_np[:, 18] == 0)
+
+
+@pytest.mark.parametrize("cfg,V", [(2, None), (3, 20000), (4, 20000), (6, 20000), (5, 5000)])
+def test_state_mask_table(torch_dev, cfg, V):
+    """Masks of rows in plain configurations come from the table computed at
+    compile time; they must equal the oracle's like every other row, and
+    the table must be there (and be used by a fair share of the rows)."""
+    say("state masks", cfg, V)
+    g, og, blob, off, toks = _setup(cfg, V)
+    info = g.info()
+    assert info["state_masks"] > 0
+    seqs, rows = _walks(og, toks, 96, seed=cfg * 31 + 5, max_len=60)
+    st, steps, status = device_rows(g, seqs)
+    got = gpu_masks(g, st)
+    want, _ = oracle_masks(og, rows, blob, off)
+    _compare_masks(got, want, len(toks), f"config {cfg} state masks")
+    plain = _plain(st.cpu().numpy())
+    say("state masks", cfg, "plain rows", int(plain.sum()), "of", len(rows), "table rows", info["state_masks"])
+    if cfg != 5:
+        assert plain.sum() >= 5
+
+
 STRING_PREFIXES = {
     2: [b'{"eligibility":{"criteria_met":true,"reason_code":"eligible"},"action":"decline","appointment":{"date":"',
         b'{"eligibility":{"criteria_met":true,"reason_code":"eligible"},"action":"decline","appointment":null,'
