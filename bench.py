@@ -263,6 +263,91 @@ def inject_bench(args):
     print(json.dumps(out))
 
 
+def draft_bench(args):
+    """--draft K: masks along K-token drafts at the tool-call workload (vocab
+    128,256, batch 256).  The drafts are the trajectory's own next K tokens
+    (all legal), taken from the states of a recorded 256-step run.  One
+    cg_fill_draft call (the path walk + one fill over B (K+1) configurations)
+    is timed against the same masks made one position at a time (K + 1
+    fills and K advances).  Prints one JSON line."""
+    import torch
+    import logit_masking_amd as cg
+    from logit_masking_amd import workloads as W
+    c = W.CONFIGS[CONFIG]
+    B, T, K = c["B"], c["T"], args.draft
+    blob, off = W.make_vocab(CONFIG)
+    V = len(off) - 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    g = cg.Grammar(W.spec_json(CONFIG), blob, off, gen_cap=W.GEN_CAP)
+    n = 96
+    st = g.new_states(B, dev)
+    g.init_state(st)
+    steps = torch.zeros(B, dtype=torch.int32, device=dev)
+    status = torch.zeros(B, dtype=torch.int32, device=dev)
+    mask = torch.empty((B, g.W), dtype=torch.int64, device=dev)
+    temp = torch.full((B,), T, dtype=torch.float32, device=dev)
+    seed = torch.from_numpy(np.array(W.row_seeds(CONFIG, B), dtype=np.uint64).view(np.int64)).to(dev)
+    ws = cg.new_workspace(B, V, dev)
+    fws = g.new_fill_workspace(B, dev)
+    ids_hist = torch.full((n + K, B), -1, dtype=torch.int32, device=dev)
+    lp = torch.empty(B, dtype=torch.float32, device=dev)
+    hist_st, hist_steps = [], []
+    for s in range(n + K):
+        hist_st.append(st.clone())
+        hist_steps.append(steps.clone())
+        logits = W.make_logits(CONFIG, s % 64, B, V, dev)
+        g.fill_bitmask(st, mask, fws)
+        g.sample_advance(logits, mask, temp, seed, steps, ws, ids_hist[s], lp, st, status)
+    torch.cuda.synchronize()
+    path = torch.empty((B, K + 1, cg.STATE_BYTES), dtype=torch.uint8, device=dev)
+    masks = torch.empty((B, K + 1, g.W), dtype=torch.int64, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    dws = torch.empty(max(2, (g.draft_workspace_bytes(B, K) + 15) // 16 * 2), dtype=torch.int64, device=dev)
+    drafts = [ids_hist[s:s + K].t().contiguous() for s in range(n)]
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    acc_sum = 0
+    st2 = g.new_states(B, dev)
+    steps2 = torch.zeros(B, dtype=torch.int32, device=dev)
+    for rep in range(2):  # the first pass loads the kernels
+        for s in range(n):
+            ev[s][0].record(stream)
+            g.fill_draft(hist_st[s], hist_steps[s], drafts[s], path, masks, acc, dws, stream)
+            ev[s][1].record(stream)
+            if rep == 1:
+                acc_sum += int(acc.sum().item())
+            # the same positions one at a time
+            st2.copy_(hist_st[s])
+            steps2.copy_(hist_steps[s])
+            evs[s][0].record(stream)
+            for j in range(K + 1):
+                g.fill_bitmask(st2, mask, fws, stream)
+                if j < K:
+                    g.advance(st2, drafts[s][:, j].contiguous(), steps2, status, stream)
+            evs[s][1].record(stream)
+        torch.cuda.synchronize()
+    t_draft = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    t_seq = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    out = {
+        "metric": f"masks along {K}-token drafts: us per cg_fill_draft call (batch {B})",
+        "value": round(pct(t_draft, 50), 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "higher_is_better": False,
+        "dtype": "int (automaton)",
+        "data": "synthetic",
+        "config": {"workload": f"tool-call grammar (8 tools), vocab {V}, batch {B}, drafts = the next {K} tokens "
+                               f"of a recorded T=0.7 trajectory, {n} draft positions", "batch": B, "vocab": V, "k": K},
+        "us_fill_draft": {"p50": round(pct(t_draft, 50), 2), "mean": round(float(t_draft.mean()), 2)},
+        "us_one_position_at_a_time": {"p50": round(pct(t_seq, 50), 2), "mean": round(float(t_seq.mean()), 2)},
+        "token_checks_per_s": round(B * (K + 1) * V / (pct(t_draft, 50) * 1e-6), 1),
+        "draft_tokens_legal_mean": round(acc_sum / (n * B), 3),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,6 +360,8 @@ def main():
                     help="cg_apply_mask_sample and cg_advance as two launches instead of cg_sample_advance")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 64 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--draft", type=int, default=0,
+                    help="measure masks along K-token drafts instead (its own JSON line)")
     ap.add_argument("--inject", action="store_true",
                     help="measure result injection on text with calc spans instead (its own JSON line)")
     args = ap.parse_args()
@@ -285,6 +372,9 @@ def main():
 
     if args.inject:
         inject_bench(args)
+        return
+    if args.draft:
+        draft_bench(args)
         return
 
     import torch

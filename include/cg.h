@@ -14,6 +14,7 @@
  *   cg_apply_mask_sample masked softmax + greedy / Gumbel-max pick (device)
  *   cg_advance           walk the chosen tokens, update rows (device)
  *   cg_sample_advance    the last two in one launch (device)
+ *   cg_fill_draft        masks along each row's k-token draft (device)
  *   cg_force_bytes       engine-written bytes (an evaluated result) (device)
  *   cg_eval_calc         evaluate a calc span (host)
  *   cg_try_input         where a candidate string is refused (host)
@@ -185,6 +186,33 @@ size_t cg_fill_workspace_bytes(const cg_grammar *g, int32_t batch);
  */
 int cg_fill_bitmask(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
                     int32_t words_per_row, void *d_workspace, void *stream);
+
+/* Longest draft cg_fill_draft takes. */
+#define CG_MAX_DRAFT 64
+
+/* Bytes of the workspace cg_fill_draft needs (0 if batch < 1 or k out of range). */
+size_t cg_draft_workspace_bytes(const cg_grammar *g, int32_t batch, int32_t k);
+
+/*
+ * Masks along a draft, for speculative decoding: row r has k draft tokens
+ * d_draft[r * k + j] (-1 pads a shorter draft).  The draft is walked from
+ * the row (cg_advance's rules, with d_step for the cap; d_step may be NULL
+ * for steps of 0) and position j = 0..k gets the row's configuration after
+ * the first j draft tokens, in d_path_states[r * (k + 1) + j], and its mask,
+ * in d_masks[(r * (k + 1) + j) * words_per_row ...] (cg_fill_bitmask's
+ * layout).  d_accept_len[r] = how many draft tokens in a row are legal; the
+ * positions after them get empty masks (the configuration is marked
+ * finished).  The target model's logits at position j are masked with mask j
+ * and a verifier keeps a prefix of at most d_accept_len[r] tokens; the row
+ * then takes d_path_states at the kept length (and d_step += that length).
+ * The rows themselves are not changed.  "Constrained decoding", "The
+ * guarantee": every position is masked by the automaton's state there.
+ * k <= CG_MAX_DRAFT; d_workspace: cg_draft_workspace_bytes(g, batch, k)
+ * bytes, 16-byte aligned, scratch.
+ */
+int cg_fill_draft(const cg_grammar *g, const cg_state *d_states, const int32_t *d_step, int32_t batch,
+                  const int32_t *d_draft, int32_t k, cg_state *d_path_states, uint64_t *d_masks,
+                  int32_t words_per_row, int32_t *d_accept_len, void *d_workspace, void *stream);
 
 /* Bytes of the workspace cg_apply_mask_sample needs for (batch, vocab) (0 if batch or vocab < 1). */
 size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab);

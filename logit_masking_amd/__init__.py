@@ -22,7 +22,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # Symbols the C ABI (include/cg.h) exports.
 EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
-           "cg_fill_bitmask", "cg_sample_advance", "cg_force_bytes", "cg_eval_calc",
+           "cg_fill_bitmask", "cg_sample_advance", "cg_force_bytes", "cg_eval_calc", "cg_draft_workspace_bytes",
+           "cg_fill_draft",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
 
 
@@ -68,12 +69,15 @@ def lib():
         L.cg_apply_mask_sample.argtypes = [vp, i32, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.cg_advance.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.cg_force_bytes.argtypes = [vp, vp, i32, vp, sz, vp, vp, vp]
+        L.cg_draft_workspace_bytes.argtypes = [vp, i32, i32]
+        L.cg_draft_workspace_bytes.restype = sz
+        L.cg_fill_draft.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]
         L.cg_eval_calc.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_int64)]
         L.cg_sample_advance.argtypes = [vp, vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
         L.cg_last_error.restype = ctypes.c_char_p
         for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask", "cg_sample_advance",
-                     "cg_force_bytes", "cg_eval_calc",
+                     "cg_force_bytes", "cg_eval_calc", "cg_fill_draft",
                      "cg_apply_mask_sample", "cg_advance", "cg_try_input"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -220,6 +224,35 @@ class Grammar:
                 raise ValueError(f"{n} has fewer rows than states")
         _check(lib().cg_advance(self._h, _ptr(states), states.shape[0], _ptr(ids), _ptr(steps), _ptr(status),
                                 _stream(stream)))
+
+    def draft_workspace_bytes(self, B: int, k: int) -> int:
+        return int(lib().cg_draft_workspace_bytes(self._h, B, k))
+
+    def fill_draft(self, states, steps, draft, path_states, masks, accept_len, workspace=None, stream=None):
+        """cg_fill_draft: draft [B, k] int32 (-1 pads); path_states [B, k+1, 24]
+        uint8; masks [B, k+1, W] int64; accept_len [B] int32; steps [B] int32
+        or None."""
+        import torch
+        _dev(states, torch.uint8, "states", 2)
+        B = states.shape[0]
+        _dev(draft, torch.int32, "draft", 2)
+        k = draft.shape[1]
+        if draft.shape[0] < B:
+            raise ValueError("draft has fewer rows than states")
+        _dev(path_states, torch.uint8, "path_states", 3)
+        _dev(masks, torch.int64, "masks", 3)
+        _dev(accept_len, torch.int32, "accept_len", 1)
+        if steps is not None:
+            _dev(steps, torch.int32, "steps", 1)
+        if path_states.shape[0] < B or path_states.shape[1] != k + 1 or masks.shape[0] < B or masks.shape[1] != k + 1:
+            raise ValueError("path_states / masks must be [B, k+1, ...]")
+        if workspace is None:
+            n = self.draft_workspace_bytes(B, k)
+            workspace = torch.empty(max(2, (n + 15) // 16 * 2), dtype=torch.int64, device=states.device)
+        if workspace.numel() * workspace.element_size() < self.draft_workspace_bytes(B, k):
+            raise ValueError("draft workspace too small")
+        _check(lib().cg_fill_draft(self._h, _ptr(states), _ptr(steps), B, _ptr(draft), k, _ptr(path_states),
+                                   _ptr(masks), masks.shape[2], _ptr(accept_len), _ptr(workspace), _stream(stream)))
 
     def force_bytes(self, states, data, offsets, status, stream=None):
         """cg_force_bytes: row r walks data[offsets[r]:offsets[r+1]] (uint8 /

@@ -18,6 +18,8 @@ int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *by
                  const uint32_t *offsets, int32_t *status, hipStream_t st);
 int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws,
                 hipStream_t st);
+int launch_draft(const cg_grammar *g, const cg_state *states, const int32_t *steps, int B, const int32_t *draft,
+                 int kd, cg_state *path, int32_t *accept_len, hipStream_t st);
 int fill_plan_stride(const cg_grammar *g);
 size_t sample_workspace_bytes(int B, int V);
 size_t fill_lds_bytes(const cg_grammar *g, int items_per_row);
@@ -407,6 +409,28 @@ int cg_fill_bitmask(const cg_grammar *g, const cg_state *d_states, int32_t batch
     if (batch > 0 && (!d_workspace || (uintptr_t)d_workspace % 16))
         return arg_error("workspace must be a 16-byte aligned device buffer of cg_fill_workspace_bytes bytes");
     return launch_fill(g, d_states, batch, d_mask, words_per_row, d_workspace, (hipStream_t)stream);
+}
+
+size_t cg_draft_workspace_bytes(const cg_grammar *g, int32_t batch, int32_t k) {
+    if (!on_device(g) || batch < 1 || k < 0 || k > CG_MAX_DRAFT) return 0;
+    return cg_fill_workspace_bytes(g, batch * (k + 1));
+}
+
+int cg_fill_draft(const cg_grammar *g, const cg_state *d_states, const int32_t *d_step, int32_t batch,
+                  const int32_t *d_draft, int32_t k, cg_state *d_path_states, uint64_t *d_masks,
+                  int32_t words_per_row, int32_t *d_accept_len, void *d_workspace, void *stream) {
+    if (!on_device(g)) return arg_error("grammar has no device tables");
+    if (k < 0 || k > CG_MAX_DRAFT) return arg_error("k out of range");
+    if (batch < 0 || (size_t)batch * (size_t)(k + 1) > (size_t)INT32_MAX) return arg_error("bad batch");
+    if (batch > 0 && (!d_states || !d_path_states || !d_masks || !d_accept_len || (k > 0 && !d_draft)))
+        return arg_error("bad arguments");
+    if (words_per_row < (g->V + 63) / 64) return arg_error("words_per_row < ceil(vocab_size / 64)");
+    if (batch > 0 && (!d_workspace || (uintptr_t)d_workspace % 16))
+        return arg_error("workspace must be a 16-byte aligned device buffer of cg_draft_workspace_bytes bytes");
+    hipStream_t st = (hipStream_t)stream;
+    int rc = launch_draft(g, d_states, d_step, batch, d_draft, k, d_path_states, d_accept_len, st);
+    if (rc != CG_OK) return rc;
+    return launch_fill(g, d_path_states, batch * (k + 1), d_masks, words_per_row, d_workspace, st);
 }
 
 size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab) {

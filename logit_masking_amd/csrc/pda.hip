@@ -133,6 +133,66 @@ __global__ __launch_bounds__(256) void k_force(const uint64_t *__restrict__ comb
     status[r] = res;
 }
 
+// One lane per row: walk the row's k draft tokens and write the states
+// along the path (position 0 = the row as it is).  The walk follows the
+// cg_advance rules, caps included, from a private copy of the row and step;
+// it stops at the first token that is not taken, and every later position
+// gets that state marked finished, so its mask is empty.  The row itself is
+// not changed.
+__global__ __launch_bounds__(256) void k_draft(const uint64_t *__restrict__ comb, uint32_t comb_len, WalkConsts k,
+                                               const uint32_t *__restrict__ tokw, const uint32_t *__restrict__ tokinfo,
+                                               int nw, int V, const cg_state *__restrict__ states,
+                                               const int32_t *__restrict__ steps, int B,
+                                               const int32_t *__restrict__ draft, int kd,
+                                               cg_state *__restrict__ path, int32_t *__restrict__ accept_len,
+                                               uint32_t gen_cap, const uint32_t *__restrict__ forced) {
+    extern __shared__ uint64_t lds_comb[];
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    const bool row = r < B;
+    cg_state s{};
+    int st = 0;
+    if (row) {
+        s = states[r];
+        st = steps ? steps[r] : 0;
+    }
+    stage_table(lds_comb, comb, comb_len);
+    __syncthreads();
+    if (!row) return;
+    cg_state *out = path + (size_t)r * (kd + 1);
+    out[0] = s;
+    int acc = 0;
+    bool alive = true;
+    for (int j = 0; j < kd; j++) {
+        if (alive) {
+            const int id = draft[(size_t)r * kd + j];
+            const bool valid = id >= 0 && id < V;
+            uint32_t n = 0;
+            uint32_t words[kMaxTokenLen / 4];
+#pragma unroll
+            for (int w = 0; w < kMaxTokenLen / 4; w++) words[w] = 0;
+            if (valid) {
+                n = tok_len(tokinfo[id]);
+#pragma unroll
+                for (int w = 0; w < kMaxTokenLen / 4; w++)
+                    if (w < nw) words[w] = tokw[(size_t)w * V + id];
+            }
+            cg_state t = s;
+            int st1 = st;
+            const int res = commit_token(t, st1, id, V, n, words, lds_comb, k, gen_cap, forced);
+            if (token_taken(res)) {
+                s = t;
+                st = st1;
+                acc++;
+            } else {
+                alive = false;
+                s.flags |= CG_FLAG_DONE;  // past the draft's legal prefix: empty masks
+            }
+        }
+        out[j + 1] = s;
+    }
+    accept_len[r] = acc;
+}
+
 // ---------------------------------------------------------------------------
 // fill_bitmask
 // ---------------------------------------------------------------------------
@@ -515,6 +575,16 @@ int launch_advance(const cg_grammar *g, cg_state *states, int B, const int32_t *
                        g->dev.tokw, g->dev.tokinfo, g->nw, g->V, states, B, ids, steps, status, g->gen_cap,
                        g->dev.forced);
     return launch_status("advance");
+}
+
+int launch_draft(const cg_grammar *g, const cg_state *states, const int32_t *steps, int B, const int32_t *draft,
+                 int kd, cg_state *path, int32_t *accept_len, hipStream_t st) {
+    if (B == 0) return CG_OK;
+    const size_t lds = (size_t)g->comb_len * sizeof(uint64_t);
+    hipLaunchKernelGGL(k_draft, dim3((B + 255) / 256), dim3(256), lds, st, g->dev.comb, g->comb_len, g->k,
+                       g->dev.tokw, g->dev.tokinfo, g->nw, g->V, states, steps, B, draft, kd, path, accept_len,
+                       g->gen_cap, g->dev.forced);
+    return launch_status("fill_draft (path)");
 }
 
 int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *bytes, uint64_t n_bytes,
