@@ -17,6 +17,8 @@
  *   cg_fill_draft        masks along each row's k-token draft (device)
  *   cg_force_bytes       engine-written bytes (an evaluated result) (device)
  *   cg_eval_calc         evaluate a calc span (host)
+ *   cg_contract_model_spec  integer-string contract: the model-facing spec (host)
+ *   cg_contract_reverse  the exact inverse, then validation (host)
  *   cg_try_input         where a candidate string is refused (host)
  *
  * Conventions
@@ -51,6 +53,7 @@ extern "C" {
 #define CG_E_VOCAB (-5)       /* malformed vocabulary (offsets) */
 #define CG_E_DEVICE (-6)      /* HIP runtime error (allocation, copy, launch) */
 #define CG_E_EVAL (-7)        /* calc span: division by zero, or a value outside int64 */
+#define CG_E_INVALID (-8)     /* contract: the generated text does not map onto the original schema */
 
 /* ---- per-row status written by cg_advance --------------------------------- */
 #define CG_ROW_OK 0       /* token accepted, row continues */
@@ -305,6 +308,36 @@ int cg_force_bytes(const cg_grammar *g, cg_state *d_states, int32_t batch, const
  * range" (text an engine can inject as <result_error>).
  */
 int cg_eval_calc(const uint8_t *span, size_t len, int64_t *value);
+
+/*
+ * The integer-string contract ("Constrained Decoding Under Matched
+ * Conditions", "The system boundary I am testing"): the caller's schema asks
+ * for canonical signed-integer strings ({"type": "string", "pattern":
+ * "^-?(0|[1-9][0-9]*)$"}), the model writes native JSON integers, and an
+ * exact inverse maps them back before the result is checked against the
+ * caller's schema.  Host only; off the per-step path.
+ *
+ * cg_contract_model_spec: ext_spec is a json_schema spec (cg_compile_grammar's
+ * format); writes the model-facing spec -- every such string replaced by
+ * {"type": "integer"} -- as compact JSON with a terminating zero into
+ * out[cap] (*out_len = its length; CG_E_LIMIT and the needed length if cap is
+ * too small) and the number of replaced fields into *n_fields.  The
+ * model-facing spec is compiled once as a check (CG_E_UNSUPPORTED with the
+ * path when it does not compile, e.g. an integer string beside another
+ * numeric alternative of an anyOf).
+ *
+ * cg_contract_reverse: text is one generation under the model-facing spec.
+ * Each integer where the original schema has an integer string becomes a
+ * string holding the integer's text, digit for digit (no parsing: any
+ * length); everything else is kept.  The object is written compactly to
+ * out[cap] and validated against ext_spec: CG_OK, or CG_E_INVALID when a
+ * field is not an integer, the text is not JSON, or the original schema
+ * refuses the result (the output is still written when it fits).
+ */
+int cg_contract_model_spec(const char *ext_spec, size_t len, char *out, size_t cap, size_t *out_len,
+                           int32_t *n_fields);
+int cg_contract_reverse(const char *ext_spec, size_t len, const uint8_t *text, size_t text_len, char *out,
+                        size_t cap, size_t *out_len);
 
 /*
  * Host-side diagnostic: run `bytes` against the automaton from its start.

@@ -12,8 +12,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcg.so")
 
-CG_OK, CG_E_ARG, CG_E_PARSE, CG_E_UNSUPPORTED, CG_E_LIMIT, CG_E_VOCAB, CG_E_DEVICE, CG_E_EVAL = \
-    0, -1, -2, -3, -4, -5, -6, -7
+CG_OK, CG_E_ARG, CG_E_PARSE, CG_E_UNSUPPORTED, CG_E_LIMIT, CG_E_VOCAB, CG_E_DEVICE, CG_E_EVAL, CG_E_INVALID = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
 ROW_OK, ROW_DONE, ROW_CAPPED, ROW_REJECTED, ROW_NOOP, ROW_INJECT = 0, 1, 2, 3, 4, 5
 FLAG_DONE, FLAG_CAPPED = 1, 2
 HOST_ONLY = 1
@@ -23,7 +23,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 # Symbols the C ABI (include/cg.h) exports.
 EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
            "cg_fill_bitmask", "cg_sample_advance", "cg_force_bytes", "cg_eval_calc", "cg_draft_workspace_bytes",
-           "cg_fill_draft",
+           "cg_fill_draft", "cg_contract_model_spec", "cg_contract_reverse",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
 
 
@@ -69,6 +69,9 @@ def lib():
         L.cg_apply_mask_sample.argtypes = [vp, i32, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.cg_advance.argtypes = [vp, vp, i32, vp, vp, vp, vp]
         L.cg_force_bytes.argtypes = [vp, vp, i32, vp, sz, vp, vp, vp]
+        L.cg_contract_model_spec.argtypes = [ctypes.c_char_p, sz, vp, sz, ctypes.POINTER(sz),
+                                             ctypes.POINTER(ctypes.c_int32)]
+        L.cg_contract_reverse.argtypes = [ctypes.c_char_p, sz, vp, sz, vp, sz, ctypes.POINTER(sz)]
         L.cg_draft_workspace_bytes.argtypes = [vp, i32, i32]
         L.cg_draft_workspace_bytes.restype = sz
         L.cg_fill_draft.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]
@@ -77,7 +80,8 @@ def lib():
         L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
         L.cg_last_error.restype = ctypes.c_char_p
         for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask", "cg_sample_advance",
-                     "cg_force_bytes", "cg_eval_calc", "cg_fill_draft",
+                     "cg_force_bytes", "cg_eval_calc", "cg_fill_draft", "cg_contract_model_spec",
+                     "cg_contract_reverse",
                      "cg_apply_mask_sample", "cg_advance", "cg_try_input"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -281,6 +285,43 @@ def eval_calc(span: bytes):
     if rc != CG_OK:
         return rc, lib().cg_last_error().decode(errors="replace")
     return CG_OK, v.value
+
+
+def _sized_call(fn, *args):
+    """Call an output-buffer function, growing the buffer once if needed."""
+    cap = 1 << 16
+    for _ in range(2):
+        buf = ctypes.create_string_buffer(cap)
+        n = ctypes.c_size_t()
+        rc = fn(*args, buf, cap, ctypes.byref(n))
+        if rc != CG_E_LIMIT:
+            return rc, buf.raw[:n.value]
+        cap = n.value + 1
+    return rc, b""
+
+
+def contract_model_spec(ext_spec):
+    """cg_contract_model_spec: (model-facing spec bytes, replaced fields)."""
+    if isinstance(ext_spec, str):
+        ext_spec = ext_spec.encode()
+    nf = ctypes.c_int32()
+    rc, out = _sized_call(lambda b, c, n: lib().cg_contract_model_spec(ext_spec, len(ext_spec), b, c, n,
+                                                                       ctypes.byref(nf)))
+    _check(rc)
+    return out, nf.value
+
+
+def contract_reverse(ext_spec, text: bytes):
+    """cg_contract_reverse: (rc, output bytes, message); rc is CG_OK or
+    CG_E_INVALID (other codes raise)."""
+    if isinstance(ext_spec, str):
+        ext_spec = ext_spec.encode()
+    tb = ctypes.create_string_buffer(text, len(text)) if text else None
+    rc, out = _sized_call(lambda b, c, n: lib().cg_contract_reverse(ext_spec, len(ext_spec), tb, len(text), b, c, n))
+    if rc not in (CG_OK, CG_E_INVALID):
+        _check(rc)
+    msg = "" if rc == CG_OK else lib().cg_last_error().decode(errors="replace")
+    return rc, out, msg
 
 
 def sample_workspace_bytes(B: int, V: int) -> int:

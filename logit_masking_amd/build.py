@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libcg.so")
 ARCH = os.environ.get("CG_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["compiler.cpp", "capi.cpp", "pda.hip", "sample.hip"]
+SOURCES = ["compiler.cpp", "capi.cpp", "contract.cpp", "pda.hip", "sample.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "--offload-arch=" + ARCH,
          # keep hipcc from emitting packed fp32 instructions
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

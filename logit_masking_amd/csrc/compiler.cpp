@@ -34,6 +34,13 @@
 
 namespace cg {
 
+// The one string pattern accepted: a canonical signed decimal integer (the
+// external side of the integer-string contract, "Constrained Decoding Under
+// Matched Conditions", "The system boundary I am testing").  Any other
+// pattern is refused.
+extern const char *const kIntStringPattern;
+const char *const kIntStringPattern = "^-?(0|[1-9][0-9]*)$";
+
 static thread_local std::string g_err;
 
 void set_error(const char *fmt, ...) {
@@ -64,7 +71,9 @@ using i128 = __int128;
 // ---------------------------------------------------------------------------
 // Spec reading -> IR
 // ---------------------------------------------------------------------------
-enum Kind { K_OBJ, K_ARR, K_STR, K_INT, K_NUM, K_BOOL, K_NULL, K_ENUM, K_ANYOF, K_ANY };
+enum Kind { K_OBJ, K_ARR, K_STR, K_INT, K_NUM, K_BOOL, K_NULL, K_ENUM, K_ANYOF, K_ANY, K_INTSTR };
+
+
 enum { AK_OBJ = 1, AK_ARR = 2, AK_STR = 4, AK_NUM = 8, AK_LIT = 16, AK_ALL = 31, AK_SCALAR = 28 };
 
 struct Node {
@@ -276,6 +285,18 @@ struct Reader {
             return add(n);
         }
         if (t == "string") {
+            const Json *pat = sch->get("pattern");
+            if (pat) {
+                std::string extra = keylist(*sch, {"type", "pattern"});
+                if (!extra.empty()) refuse(path, "unsupported keywords " + extra);
+                if (pat->t != Json::STR || pat->s != kIntStringPattern)
+                    refuse(path, "the only pattern supported is the canonical signed integer " +
+                                     std::string(kIntStringPattern));
+                n.kind = K_INTSTR;
+                n.first = FC_STR;
+                n.maxdigits = S.open_int_digits;
+                return add(n);
+            }
             std::string extra = keylist(*sch, {"type", "maxLength"});
             if (!extra.empty()) refuse(path, "unsupported keywords " + extra);
             n.kind = K_STR;
@@ -462,6 +483,23 @@ struct Builder {
         case K_BOOL: trie(s, {"true", "false"}, C); break;
         case K_NULL: trie(s, {"null"}, C); break;
         case K_INT: integer(s, x, C); break;
+        case K_INTSTR: {
+            // '"' -?(0|[1-9][0-9]*) '"' with at most maxdigits digits (the
+            // pattern itself admits "-0")
+            const int I = add(), M = add(), Z = add();
+            edge(s, '"', '"', OP_NONE, 0, I);
+            edge(I, '-', '-', OP_NONE, 0, M);
+            std::vector<int> D(x.maxdigits + 1);
+            for (int k = 1; k <= x.maxdigits; k++) D[k] = add();
+            for (int from : {I, M}) {
+                edge(from, '0', '0', OP_NONE, 0, Z);
+                edge(from, '1', '9', OP_NONE, 0, D[1]);
+            }
+            for (int k = 1; k < x.maxdigits; k++) edge(D[k], '0', '9', OP_NONE, 0, D[k + 1]);
+            edge(Z, '"', '"', OP_NONE, 0, C);
+            for (int k = 1; k <= x.maxdigits; k++) edge(D[k], '"', '"', OP_NONE, 0, C);
+            break;
+        }
         case K_NUM: number(s, C); break;
         case K_ANYOF:
             for (int k : x.kids) {

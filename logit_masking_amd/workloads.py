@@ -121,6 +121,32 @@ DECISION_SCHEMA = _obj([
     ("response_text", _strn(700)),
 ])
 
+# Designs 2-5 of the same page ("Designs 2-4 -- making the schema show its
+# working", "Design 5 -- the pipeline"): fields ahead of the decision, or an
+# extraction schema with no decision at all.  "..." on the page is read as
+# the rest of design 1's object.
+_DECISION_PROPS = list(DECISION_SCHEMA["properties"].items())
+DESIGN_SCHEMAS = {
+    2: _obj([("calculation", _strn(400)),
+             ("within_limit_banding", _enum("within_limit", "reduced_scope_band", "over_limit"))] + _DECISION_PROPS),
+    3: _obj([("exceeds_value_limit", BOOL),
+             ("over_limit_tier", {"anyOf": [_enum("reduced_scope", "hard_decline"), {"type": "null"}]})]
+            + _DECISION_PROPS),
+    4: _obj([("customer_age", {"type": "integer"}), ("age_within_18_to_70", BOOL),
+             ("total_requested_value", {"type": "number"}), ("total_at_most_10000", BOOL),
+             ("total_at_most_12000", BOOL)] + _DECISION_PROPS),
+    5: _obj([("customer_age", {"anyOf": [{"type": "integer"}, {"type": "null"}]}),
+             ("price_components", {"type": "array", "items": {"type": "number"}, "maxItems": 10}),
+             ("requested_date", {"anyOf": [_strn(20), {"type": "null"}]}),
+             ("requested_time", {"anyOf": [_strn(10), {"type": "null"}]})]),
+}
+
+
+def design_spec_json(design: int) -> bytes:
+    return json.dumps({"kind": "json_schema", "ws_max": 4, "open_string_cap": 256, "depth_cap": 32,
+                       "schema": DESIGN_SCHEMAS[design]}, separators=(",", ":")).encode()
+
+
 # Eight tools with 1-5 typed arguments; ``?`` marks an optional argument.
 TOOLS = [
     ("calculate", [("expression", STR)]),

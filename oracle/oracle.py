@@ -110,7 +110,11 @@ def lib():
 # ---------------------------------------------------------------------------
 # Spec reading
 # ---------------------------------------------------------------------------
-K_OBJ, K_ARR, K_STR, K_INT, K_NUM, K_BOOL, K_NULL, K_ENUM, K_ANYOF, K_ANY = range(1, 11)
+K_OBJ, K_ARR, K_STR, K_INT, K_NUM, K_BOOL, K_NULL, K_ENUM, K_ANYOF, K_ANY, K_INTSTR = range(1, 12)
+# The one string pattern read: a canonical signed decimal integer (the external
+# side of the integer-string contract, page "Constrained Decoding Under Matched
+# Conditions", section "The system boundary I am testing").
+INT_STRING_PATTERN = "^-?(0|[1-9][0-9]*)$"
 G_CALC, G_JSON, G_TOOL, G_TEXT = 1, 2, 3, 4
 AK_ALL = 31
 
@@ -157,7 +161,7 @@ def _first_classes(node, nodes, props):
         return {"{"}
     if k == K_ARR:
         return {"["}
-    if k in (K_STR, K_ENUM):
+    if k in (K_STR, K_ENUM, K_INTSTR):
         return {'"'}
     if k in (K_INT, K_NUM):
         return {"num"}
@@ -272,6 +276,12 @@ class _Builder:
                 item = self.schema(sch["items"], f"{path}/items", depth + 1)
                 return self.add(kind=K_ARR, item=item, cap=mi)
             return self.add(kind=K_ARR, open=1, cap=mi)
+        if t == "string" and "pattern" in sch:
+            if not keys <= {"type", "pattern"}:
+                raise Unsupported(path, f"unsupported keywords {sorted(keys - {'type', 'pattern'})}")
+            if sch["pattern"] != INT_STRING_PATTERN:
+                raise Unsupported(path, "the only pattern supported is the canonical signed integer")
+            return self.add(kind=K_INTSTR, maxdigits=self.s["open_int_digits"])
         if t == "string":
             if not keys <= {"type", "maxLength"}:
                 raise Unsupported(path, f"unsupported keywords {sorted(keys - {'type', 'maxLength'})}")
@@ -745,3 +755,124 @@ def eval_calc(span: bytes, bound=None) -> int:
     if pos != len(toks):
         raise CalcError("trailing input")
     return v
+
+
+# ---------------------------------------------------------------------------
+# The integer-string contract (page "Constrained Decoding Under Matched
+# Conditions", section "The system boundary I am testing"): external
+# canonical signed-integer strings become native JSON integers for the
+# model; after one generation each such integer goes back to a string of its
+# own base-10 text, and the result is validated against the external schema.
+# ---------------------------------------------------------------------------
+class _RawNum(str):
+    """A JSON number kept as its source text."""
+
+
+class ContractError(ValueError):
+    pass
+
+
+def _is_int_string(sch):
+    return isinstance(sch, dict) and sch.get("type") == "string" and sch.get("pattern") == INT_STRING_PATTERN
+
+
+def contract_model_spec(spec: dict) -> tuple:
+    """(model-facing spec, number of replaced fields)."""
+    n = 0
+
+    def conv(s):
+        nonlocal n
+        if _is_int_string(s):
+            n += 1
+            return {"type": "integer"}
+        if not isinstance(s, dict):
+            return s
+        out = {}
+        for k, v in s.items():
+            if k == "properties" and isinstance(v, dict):
+                out[k] = {pk: conv(pv) for pk, pv in v.items()}
+            elif k == "items":
+                out[k] = conv(v)
+            elif k == "anyOf" and isinstance(v, list):
+                out[k] = [conv(a) for a in v]
+            else:
+                out[k] = v
+        return out
+
+    model = dict(spec)
+    model["schema"] = conv(spec["schema"])
+    return model, n
+
+
+def _dump(v) -> str:
+    if v is None:
+        return "null"
+    if v is True:
+        return "true"
+    if v is False:
+        return "false"
+    if isinstance(v, _RawNum):
+        return str.__str__(v)
+    if isinstance(v, str):
+        return json.dumps(v, ensure_ascii=False)
+    if isinstance(v, list):
+        return "[" + ",".join(_dump(x) for x in v) + "]"
+    return "{" + ",".join(json.dumps(k, ensure_ascii=False) + ":" + _dump(x) for k, x in v.items()) + "}"
+
+
+def _integer_text(v):
+    return isinstance(v, _RawNum) and all(c in "-0123456789" for c in v)
+
+
+def _fits(sch, v):
+    if _is_int_string(sch):
+        return _integer_text(v)
+    t = sch.get("type") if isinstance(sch, dict) else None
+    if not isinstance(t, str):
+        return True
+    if v is None:
+        return t == "null"
+    if isinstance(v, bool):
+        return t == "boolean"
+    if isinstance(v, _RawNum):
+        return t == "number" or (t == "integer" and _integer_text(v))
+    if isinstance(v, str):
+        return t == "string"
+    if isinstance(v, list):
+        return t == "array"
+    return t == "object"
+
+
+def contract_reverse(spec: dict, text: bytes):
+    """(ok, output text or None, message).  ok: the output maps onto the
+    external schema and the external grammar accepts it in full."""
+    try:
+        v = json.loads(text.decode("utf-8"), parse_int=_RawNum, parse_float=_RawNum,
+                       parse_constant=_RawNum)
+    except (ValueError, UnicodeDecodeError) as e:
+        return False, None, f"generated text: {e}"
+
+    def rev(sch, v):
+        if _is_int_string(sch):
+            if not _integer_text(v):
+                raise ContractError("expected an integer")
+            return str(str.__str__(v))
+        if not isinstance(sch, dict):
+            return v
+        if "anyOf" in sch:
+            for alt in sch["anyOf"]:
+                if _fits(alt, v):
+                    return rev(alt, v)
+            return v
+        if isinstance(v, dict) and isinstance(sch.get("properties"), dict):
+            return {k: (rev(sch["properties"][k], x) if k in sch["properties"] else x) for k, x in v.items()}
+        if isinstance(v, list) and "items" in sch:
+            return [rev(sch["items"], x) for x in v]
+        return v
+
+    try:
+        out = _dump(rev(spec["schema"], v)).encode("utf-8")
+    except ContractError as e:
+        return False, None, str(e)
+    k, complete = Grammar(spec).try_input(out)
+    return complete, out, "" if complete else f"refused at byte {k}"

@@ -40,7 +40,7 @@
 typedef __int128 i128;
 
 /* ---- schema description, filled in by oracle.py ---------------------- */
-enum { K_OBJ = 1, K_ARR, K_STR, K_INT, K_NUM, K_BOOL, K_NULL, K_ENUM, K_ANYOF, K_ANY };
+enum { K_OBJ = 1, K_ARR, K_STR, K_INT, K_NUM, K_BOOL, K_NULL, K_ENUM, K_ANYOF, K_ANY, K_INTSTR };
 enum { G_CALC = 1, G_JSON = 2, G_TOOL = 3, G_TEXT = 4 };
 /* K_ANY kinds that may start a value */
 enum { AK_OBJ = 1, AK_ARR = 2, AK_STR = 4, AK_NUM = 8, AK_LIT = 16 };
@@ -473,7 +473,9 @@ static int step_str(ofr *f, int ch) {
 }
 
 /* integer frame: aux = minus seen, a = digits so far, digits kept in v as a
- * little base-16 stack of decimal digits (max 21) -> decode for checks */
+ * little base-16 stack of decimal digits (max 21) -> decode for checks.
+ * phase 1: the content of a string with the signed-integer pattern; it ends
+ * by taking the closing quote. */
 static void int_digits(const ofr *f, char *d) {
     for (int i = 0; i < f->a; i++) d[i] = (char)('0' + (int)((f->v >> (4 * i)) & 0xF));
 }
@@ -484,6 +486,19 @@ static int step_int(const og *g, ofr *f, int ch) {
     int_bounds(g, f->node, &lo, &hi, &maxd);
     char d[40];
     int_digits(f, d);
+    if (f->phase == 1) {
+        /* the pattern -?(0|[1-9][0-9]*), at most maxd digits ("-0" matches it) */
+        if (ch == '"') return f->a > 0 ? R_DONE_TOOK : R_DEAD;
+        if (ch == '-') {
+            if (f->a > 0 || f->aux) return R_DEAD;
+            f->aux = 1;
+            return R_OK;
+        }
+        if (!is_digit(ch) || f->a >= maxd || (f->a > 0 && d[0] == '0')) return R_DEAD;
+        f->v |= (i128)(ch - '0') << (4 * f->a);
+        f->a++;
+        return R_OK;
+    }
     if (is_digit(ch)) {
         d[f->a] = (char)ch;
         if (!int_viable(f->aux, d, f->a + 1, lo, hi, maxd)) return R_DEAD;
@@ -762,6 +777,12 @@ static int start_value(const og *g, oconf *c, int node, int kinds, int ch) {
             }
             if (!is_digit(ch)) return 0;
             return step_int(g, f, ch) == R_OK;
+        }
+        case K_INTSTR: {
+            if (ch != '"') return 0;
+            ofr *f = push(c, F_INT, node);
+            f->phase = 1;
+            return 1;
         }
         case K_NUM: {
             if (ch != '-' && !is_digit(ch)) return 0;

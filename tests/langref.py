@@ -141,6 +141,15 @@ class _P:
             return self.obj(sch)
         if t == "array":
             return self.arr(sch)
+        if t == "string" and "pattern" in sch:
+            # the canonical signed-integer string: Python's regex engine on the
+            # string's raw content (no escapes spell a digit)
+            start = self.i
+            self.string(-1)
+            content = self.s[start + 1:self.i - 1].decode("utf-8")
+            if not re.fullmatch(sch["pattern"], content) or len(content.lstrip("-")) > self.digits:
+                raise _Fail
+            return
         if t == "string":
             return self.string(sch.get("maxLength", self.cap if self.cap is not None else -1))
         if t == "integer":

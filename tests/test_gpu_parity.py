@@ -368,3 +368,50 @@ def test_fill_workspace_reuse_and_size(torch_dev):
     small = torch.empty(max(1, g.fill_workspace_bytes(7) // 8 - 1), dtype=torch.int64, device="cuda")
     with pytest.raises(ValueError):
         g.fill_bitmask(st[:8].contiguous(), torch.empty((8, g.W), dtype=torch.int64, device="cuda"), small)
+
+
+@pytest.mark.parametrize("design", sorted(W.DESIGN_SCHEMAS))
+def test_design_mask_parity(torch_dev, design):
+    """Decision designs 2-5 (vocab of config 2): masks of rows at random
+    legal prefixes, bit-exact, and a sampled lock-step trajectory."""
+    say("design", design)
+    blob, off = W.make_vocab(2)
+    toks = [blob[off[i]:off[i + 1]] for i in range(len(off) - 1)]
+    spec = W.design_spec_json(design)
+    g = cg.Grammar(spec, blob, off)
+    og = O.load_spec(spec)
+    seqs, rows = _walks(og, toks, 32, seed=0xD0 + design, max_len=120)
+    st, steps, status = device_rows(g, seqs)
+    got = gpu_masks(g, st)
+    want, _ = oracle_masks(og, rows, blob, off)
+    _compare_masks(got, want, len(toks), f"design {design}")
+    # a few sampled steps from these rows
+    import torch
+    B, V = len(rows), len(toks)
+    mask = torch.empty((B, g.W), dtype=torch.int64, device="cuda")
+    temp = torch.full((B,), 0.7, dtype=torch.float32, device="cuda")
+    seeds = np.array(W.row_seeds(2, B), dtype=np.uint64)
+    seed_t = torch.from_numpy(seeds.view(np.int64)).cuda()
+    ws = cg.new_workspace(B, V)
+    ids = torch.empty(B, dtype=torch.int32, device="cuda")
+    lp = torch.empty(B, dtype=torch.float32, device="cuda")
+    ties = 0
+    for s in range(12):
+        logits = W.make_logits(2, 100 + s, B, V, "cuda")
+        g.fill_bitmask(st, mask)
+        g.sample_advance(logits, mask, temp, seed_t, steps, ws, ids, lp, st, status)
+        m_dev = mask.cpu().numpy().view(np.uint64)
+        ids_dev, lp_dev, stat = ids.cpu().numpy(), lp.cpu().numpy(), status.cpu().numpy()
+        x = logits.float().cpu().numpy().astype(np.float64)
+        words, _ = oracle_masks(og, rows, blob, off)
+        for r in range(B):
+            assert np.array_equal(m_dev[r], words[r]), (design, s, r)
+            bits = O.unpack_mask(words[r], V)
+            i, l, info = O.sample_row(x[r], bits, 0.7, int(seeds[r]), rows[r].step)
+            if i >= 0 and min(info["margin_chunk"], info["margin_token"]) < NEAR_TIE:
+                ties += 1
+                assert bits[ids_dev[r]]
+            else:
+                assert ids_dev[r] == i and (i < 0 or abs(lp_dev[r] - l) < LOGPROB_TOL)
+            assert stat[r] == rows[r].advance(None if ids_dev[r] < 0 else toks[ids_dev[r]])
+    assert ties <= 2
