@@ -24,6 +24,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E
 CONFIG = 3
+WORKLOADS = {
+    1: "calc span grammar, vocab 512, batch 4, fp32 N(0,1) logits, greedy",
+    2: "decision schema, vocab 32000, batch 64, fp32 N(0,4) logits, T=0.7 Philox two-level Gumbel",
+    3: "tool-call grammar (8 tools), vocab 128256, batch 256, bf16 N(0,9) logits, T=0.7 Philox two-level Gumbel",
+    4: "integer-answer contract, vocab 151936, batch 1024, bf16 N(0,1) logits, greedy",
+    5: "recursive JSON, vocab 256000, batch 512, bf16 Student-t(3) logits, T=1.0 Philox two-level Gumbel",
+    6: "text with calc spans, vocab 128256, batch 256, bf16 N(0,9) logits, T=0.7 Philox two-level Gumbel",
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_sample_hbm_traffic_toolcall_v128k_b256.md")
 KERNEL_SRC = os.path.join(ROOT, "logit_masking_amd", "csrc", "sample.hip")
 
@@ -57,20 +65,20 @@ def pct(a, q):
     return float(np.percentile(np.asarray(a), q))
 
 
-def cpu_baseline(ids_hist, B, V, blob, off, budget_s):
+def cpu_baseline(ids_hist, B, V, blob, off, budget_s, cfg=CONFIG):
     """The oracle as it stands, on a bounded sample of the same workload:
     the first rows of the measured trajectory replayed on the host; at every
     step each row still generating gets a full-vocabulary mask and a
     float64 two-level sample, until the time budget is spent."""
     import logit_masking_amd.workloads as W
     from oracle import oracle as O
-    og = O.load_spec(W.spec_json(CONFIG))
+    og = O.load_spec(W.spec_json(cfg))
     toks = [blob[off[i]:off[i + 1]] for i in range(V)]
     threads = min(16, os.cpu_count() or 1)
     nrows = threads
     rows = [O.Row(og, W.GEN_CAP) for _ in range(nrows)]
-    seeds = W.row_seeds(CONFIG, B)
-    T = W.CONFIGS[CONFIG]["T"]
+    seeds = W.row_seeds(cfg, B)
+    T = W.CONFIGS[cfg]["T"]
     checks = walked = row_steps = 0
     t_cpu = 0.0
     last = 0
@@ -78,7 +86,7 @@ def cpu_baseline(ids_hist, B, V, blob, off, budget_s):
         live = [r for r in range(nrows) if not rows[r].done]
         if not live or t_cpu >= budget_s:
             break
-        logits = W.make_logits(CONFIG, s, nrows, V, "cpu")
+        logits = W.make_logits(cfg, s, nrows, V, "cpu")
         x = logits.float().numpy().astype(np.float64)
         t0 = time.perf_counter()
         words, w = og.mask_rows([rows[r].conf for r in live], [False] * len(live), blob, off, threads)
@@ -360,6 +368,8 @@ def main():
                     help="cg_apply_mask_sample and cg_advance as two launches instead of cg_sample_advance")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 64 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--config", type=int, default=CONFIG,
+                    help="workload (1-6); the headline line is config 3, the others are for reference")
     ap.add_argument("--draft", type=int, default=0,
                     help="measure masks along K-token drafts instead (its own JSON line)")
     ap.add_argument("--inject", action="store_true",
@@ -381,24 +391,27 @@ def main():
     import logit_masking_amd as cg
     from logit_masking_amd import workloads as W
 
-    c = W.CONFIGS[CONFIG]
+    cfg = args.config
+    c = W.CONFIGS[cfg]
     B, T = c["B"], c["T"]
-    blob, off = W.make_vocab(CONFIG)
+    blob, off = W.make_vocab(cfg)
     V = len(off) - 1
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    g = cg.Grammar(W.spec_json(CONFIG), blob, off, gen_cap=W.GEN_CAP)
+    g = cg.Grammar(W.spec_json(cfg), blob, off, gen_cap=W.GEN_CAP)
     info = g.info()
     total = args.warmup + args.steps
-    npool = max(1, min(args.pool, total))
-    pool = [W.make_logits(CONFIG, s, B, V, dev) for s in range(npool)]
+    es = 2 if c["dtype"] == "bf16" else 4
+    # the pool of logits buffers stays within 16 GB of HBM
+    npool = max(1, min(args.pool, total, (16 << 30) // (B * V * es)))
+    pool = [W.make_logits(cfg, s, B, V, dev) for s in range(npool)]
     st = g.new_states(B, dev)
     g.init_state(st)
     steps = torch.zeros(B, dtype=torch.int32, device=dev)
     status = torch.zeros(B, dtype=torch.int32, device=dev)
     mask = torch.empty((B, g.W), dtype=torch.int64, device=dev)
     temp = torch.full((B,), T, dtype=torch.float32, device=dev)
-    seed = torch.from_numpy(np.array(W.row_seeds(CONFIG, B), dtype=np.uint64).view(np.int64)).to(dev)
+    seed = torch.from_numpy(np.array(W.row_seeds(cfg, B), dtype=np.uint64).view(np.int64)).to(dev)
     ws = cg.new_workspace(B, V, dev)
     fws = g.new_fill_workspace(B, dev)
     ids_hist = torch.full((total, B), -1, dtype=torch.int32, device=dev)
@@ -461,7 +474,7 @@ def main():
 
     # masked sample: every logit (bf16) and mask word read once, id + logprob
     # written; fused, also each row's state, step and status
-    sample_bytes = B * V * 2 + B * g.W * 8 + B * 8
+    sample_bytes = B * V * es + B * g.W * 8 + B * 8
     if not args.separate:
         sample_bytes += B * (2 * 24 + 2 * 4 + 4)
     sample_gbps = sample_bytes / (samp_ms.mean() * 1e-3) / 1e9
@@ -474,7 +487,7 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(sample_gbps / HBM_PEAK_GBPS, 4),
-        "traffic": recorded_traffic(),
+        "traffic": recorded_traffic() if cfg == CONFIG else None,
     }
     out = {
         "metric": "token-checks/s (fill_bitmask) + masked-sample GB/s vs HBM peak; µs/step",
@@ -487,10 +500,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": c["dtype"],
         "data": "synthetic",
-        "config": {"workload": "tool-call grammar (8 tools), vocab 128256, batch 256, bf16 N(0,9) logits, "
-                               "T=0.7 Philox two-level Gumbel, 256-step trajectory, engine cap 2048",
+        "config": {"workload": WORKLOADS[cfg] + f", {args.steps}-step trajectory, engine cap 2048",
                    "batch": B, "vocab": V, "logits_pool": npool},
         "fill_token_checks_per_s": round(fill_checks, 1),
         "masked_sample_GBps": round(sample_gbps, 1),
@@ -519,7 +531,7 @@ def main():
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = src.numel() * 2
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(ids_hist.cpu().numpy(), B, V, blob, off, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(ids_hist.cpu().numpy(), B, V, blob, off, args.cpu_budget, cfg)
     print(json.dumps(out))
 
 

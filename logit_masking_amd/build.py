@@ -42,7 +42,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=3) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -21,6 +21,7 @@ int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *ma
 int launch_draft(const cg_grammar *g, const cg_state *states, const int32_t *steps, int B, const int32_t *draft,
                  int kd, cg_state *path, int32_t *accept_len, hipStream_t st);
 int fill_plan_stride(const cg_grammar *g);
+int launch_mask_and(uint64_t *rows, const uint8_t *need, const uint64_t *m, int n, int Wv, hipStream_t st);
 size_t sample_workspace_bytes(int B, int V);
 size_t fill_lds_bytes(const cg_grammar *g, int items_per_row);
 int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, const uint64_t *mask, int wpr,
@@ -58,6 +59,15 @@ void release(cg_grammar *g) {
         (void)hipFree(g->dev.forced);
         (void)hipFree(g->dev.state_mask);
         (void)hipFree(g->dev.closebits);
+        (void)hipFree(g->dev.c_idlen);
+        (void)hipFree(g->dev.c_jump);
+        (void)hipFree(g->dev.c_w);
+        (void)hipFree(g->dev.c_tile);
+        (void)hipFree(g->dev.retmask2);
+        (void)hipFree(g->dev.qc_idlen);
+        (void)hipFree(g->dev.qc_posch);
+        (void)hipFree(g->dev.qc_w);
+        (void)hipFree(g->dev.qc_tile);
         (void)hipFree(g->dev.retmask);
         (void)hipFree(g->dev.rq_idx);
         (void)hipFree(g->dev.smask_idx);
@@ -102,9 +112,46 @@ constexpr size_t kCloseMaskBudget = 64ull << 20;  // bytes of per-resume-state c
 struct FillHost {
     std::vector<uint64_t> legal, strbits, closebits, retmask;
     std::vector<int32_t> rq_idx;
+    std::vector<uint64_t> s0;  // tokens that stay inside the container a row is in (bit per id)
+    std::vector<uint64_t> retmask2;  // [resume][kind of the open container][Wv]
+    std::vector<uint32_t> qc_idlen, qc_posch, qc_w;
+    std::vector<uint2> qc_tile;
+    std::vector<uint32_t> c_idlen, c_jump, c_w;
+    std::vector<uint2> c_tile;
     std::vector<uint32_t> lex_idlen, lex_jump, lex_w, q_idlen, q_posch, q_w;
     std::vector<uint2> lex_tile, q_tile;
 };
+
+// Brackets of a token read from outside a string: R = the deepest level at
+// or below the start that a closing bracket lands on (-1: none), H = the
+// highest level an opening bracket opens from (-1: none).  Brackets inside
+// JSON strings are content when the grammar has strings.  The automaton's
+// pushes and pops happen only on these bytes, so R and H never under-count
+// what a walk of the token does.
+void bracket_profile(const uint8_t *b, uint32_t n, bool json_strings, int &R, int &H) {
+    int lvl = 0;
+    bool in_str = false, esc = false;
+    R = -1;
+    H = -1;
+    for (uint32_t i = 0; i < n; i++) {
+        const uint8_t c = b[i];
+        if (in_str) {
+            if (esc) esc = false;
+            else if (c == '\\') esc = true;
+            else if (c == '"') in_str = false;
+            continue;
+        }
+        if (json_strings && c == '"') {
+            in_str = true;
+        } else if (c == '{' || c == '[' || c == '(') {
+            H = std::max(H, lvl);
+            lvl++;
+        } else if (c == '}' || c == ']' || c == ')') {
+            lvl--;
+            if (lvl <= 0) R = std::max(R, -lvl);
+        }
+    }
+}
 
 void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint32_t *tok_offsets,
                        const std::vector<uint32_t> &tokinfo, FillHost &f) {
@@ -163,16 +210,36 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
     spans(q, [&](uint32_t t) { return qoff(t) == len(t) ? 0u : bytes(t)[qoff(t)] + 1u; }, f.q_tile);
     // the jump: where the token's first quote is, and how the bytes after it
     // read as string content
-    f.lex_jump.assign(std::max<size_t>(lex.size(), 1), kNoQuote);
-    for (size_t i = 0; i < lex.size(); i++) {
-        const uint32_t t = lex[i];
-        if (t == kPad || g->k.s_body >= g->k.q_limit) continue;
-        const uint8_t *b = bytes(t);
-        const uint8_t *qp = (const uint8_t *)memchr(b, '"', len(t));
-        if (!qp) continue;
-        const uint32_t at = (uint32_t)(qp - b);
-        f.lex_jump[i] = at | string_summary(g, b + at + 1, len(t) - at - 1);
+    auto jumps = [&](const std::vector<uint32_t> &order, std::vector<uint32_t> &jump) {
+        jump.assign(std::max<size_t>(order.size(), 1), kNoQuote);
+        for (size_t i = 0; i < order.size(); i++) {
+            const uint32_t t = order[i];
+            if (t == kPad || g->k.s_body >= g->k.q_limit) continue;
+            const uint8_t *b = bytes(t);
+            const uint8_t *qp = (const uint8_t *)memchr(b, '"', len(t));
+            if (!qp) continue;
+            const uint32_t at = (uint32_t)(qp - b);
+            jump[i] = at | string_summary(g, b + at + 1, len(t) - at - 1);
+        }
+    };
+    jumps(lex, f.lex_jump);
+    // tokens that stay inside the container a row is in (s0) and the rest,
+    // kept as a lexicographic tile list of their own
+    f.s0.assign(Wv, 0ull);
+    std::vector<uint32_t> cl;
+    const bool json_strings = g->k.s_body < g->k.q_limit;
+    for (uint32_t t = 0; t < V; t++) {
+        if (len(t) == 0) continue;
+        int R, H;
+        bracket_profile(bytes(t), len(t), json_strings, R, H);
+        if (R <= 0 && H <= kPushLimit) f.s0[t >> 6] |= 1ull << (t & 63);
+        else cl.push_back(t);
     }
+    std::sort(cl.begin(), cl.end(), [&](uint32_t a, uint32_t b) { return less_from(a, 0, b, 0); });
+    pad(cl);
+    pack(cl, f.c_idlen, f.c_w);
+    spans(cl, [&](uint32_t t) { return lead_key(bytes(t)[0], len(t) > 1 ? bytes(t)[1] : 0u, len(t)); }, f.c_tile);
+    jumps(cl, f.c_jump);
     f.q_posch.assign(std::max<size_t>(q.size(), 1), 0u);
     for (size_t i = 0; i < q.size(); i++)
         if (q[i] != kPad) f.q_posch[i] = tok_pos(tokinfo[q[i]]) | tok_chars(tokinfo[q[i]]) << 8;
@@ -223,42 +290,156 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
             if (ok) f.retmask[j * Wv + (t >> 6)] |= 1ull << (t & 63);
         }
     }
+    // The same inside an open container (depth 1, container kind b), for the
+    // closing tokens whose bytes after the quote stay inside it and open at
+    // most kPushLimit more; the other closing tokens form a list of their
+    // own, in the string-closing order, walked for such rows.
+    std::vector<uint32_t> qc;
+    std::vector<uint32_t> stay;
+    for (uint32_t t : q) {
+        if (t == kPad) continue;
+        int R, H;
+        const uint32_t at = tok_pos(tokinfo[t]) + 1;
+        bracket_profile(bytes(t) + at, len(t) - at, true, R, H);
+        if (R <= 0 && H <= kPushLimit) stay.push_back(t);
+        else qc.push_back(t);
+    }
+    if (resume.size() * 2 * Wv * 8 <= kCloseMaskBudget) {
+        f.retmask2.assign(resume.size() * 2 * Wv, 0ull);
+        for (size_t j = 0; j < resume.size(); j++)
+            for (uint32_t b = 0; b < 2; b++)
+                for (uint32_t t : stay) {
+                    Walker w;
+                    w.q = resume[j];
+                    w.ret = g->k.start;
+                    w.cnt = 0;
+                    w.ws = 0;
+                    w.depth = 1;
+                    w.stk = b;
+                    bool ok = true;
+                    for (uint32_t i = tok_pos(tokinfo[t]) + 1; ok && i < len(t); i++)
+                        ok = step_byte(w, bytes(t)[i], g->host_comb, g->k);
+                    if (ok) f.retmask2[(j * 2 + b) * Wv + (t >> 6)] |= 1ull << (t & 63);
+                }
+    }
+    pad(qc);
+    pack(qc, f.qc_idlen, f.qc_w);
+    spans(qc, [&](uint32_t t) { return qoff(t) == len(t) ? 0u : bytes(t)[qoff(t)] + 1u; }, f.qc_tile);
+    f.qc_posch.assign(std::max<size_t>(qc.size(), 1), 0u);
+    for (size_t i = 0; i < qc.size(); i++)
+        if (qc[i] != kPad) f.qc_posch[i] = tok_pos(tokinfo[qc[i]]) | tok_chars(tokinfo[qc[i]]) << 8;
 }
 
 }  // namespace
 
-// Masks of the plain configurations (a live state outside strings, no
-// whitespace run, no open container), computed once with the fill kernels
-// themselves; the fill then copies such a row's mask instead of walking
-// tokens.  A state's registers other than the whitespace run and the
-// container stack are only read inside strings, so the mask of a plain
-// configuration depends on the state alone.  Skipped (no table) when it
-// would exceed kStateMaskBudget bytes.
-constexpr size_t kStateMaskBudget = 64ull << 20;
+// Masks computed once with the fill kernels themselves, for states outside
+// strings: context 0 = (state, whitespace run, no open container), the whole
+// mask; contexts 1 and 2 = the same inside an open object / array at depth 1,
+// kept only for the tokens in s0 (those that cannot close the container the
+// row is in and open at most kPushLimit more).  A state's registers other
+// than the whitespace run and the container stack are read only inside
+// strings, so context 0 depends on (state, run) alone; an s0 token reads of
+// the stack only the innermost container's kind and meets the depth cap
+// only if depth + kPushLimit reaches the smallest cap, so for such rows
+// context 1 / 2 holds exactly.  Rows above that depth walk as before.  The
+// table keeps to kStateMaskBudget bytes, dropping whitespace runs, then
+// open containers, when it would not fit.
+constexpr size_t kStateMaskBudget = 96ull << 20;
 
-int build_state_masks(cg_grammar *g) {
-    const size_t Wv = ((size_t)g->V + 63) / 64, n = g->plain_q.size();
-    if (n == 0 || n * Wv * 8 > kStateMaskBudget) return CG_OK;
+int build_state_masks(cg_grammar *g, const FillHost &f) {
+    const size_t Wv = ((size_t)g->V + 63) / 64;
+    const uint32_t QL = g->k.q_limit, WD = g->k.ws_max + 1;
+    // targets of whitespace bytes, and the states that can be inside an open container
+    std::vector<char> ws_target(QL, 0), inside(QL, 0);
+    std::vector<uint32_t> work;
+    int min_cap = 0;
+    for (uint32_t q = 0; q < QL; q++)
+        for (uint32_t b = 0; b < 256; b++) {
+            const uint64_t e = g->host_comb[q + b];
+            if (((uint32_t)e & 0xFFFFu) != q) continue;
+            const uint32_t op = (uint32_t)(e >> 32) & 0xFu, nx = ((uint32_t)e >> 16) & 0xFFFFu;
+            if (op == OP_WS && nx < QL) ws_target[nx] = 1;
+            if (op == OP_PUSH) {
+                const int cap = (int)((uint32_t)(e >> 36) >> 1);
+                min_cap = min_cap == 0 ? cap : std::min(min_cap, cap);
+                if (nx < QL && !inside[nx]) {
+                    inside[nx] = 1;
+                    work.push_back(nx);
+                }
+            }
+        }
+    while (!work.empty()) {
+        const uint32_t q = work.back();
+        work.pop_back();
+        for (uint32_t b = 0; b < 256; b++) {
+            const uint64_t e = g->host_comb[q + b];
+            if (((uint32_t)e & 0xFFFFu) != q) continue;
+            const uint32_t op = (uint32_t)(e >> 32) & 0xFu, arg = (uint32_t)(e >> 36);
+            uint32_t to[2] = {((uint32_t)e >> 16) & 0xFFFFu, 0xFFFFFFFFu};
+            if (op == OP_STR_CLOSE) continue;
+            if (op == OP_POP) to[0] = arg >> 14, to[1] = arg & 0x3FFFu;
+            for (uint32_t t : to)
+                if (t < QL && !inside[t]) {
+                    inside[t] = 1;
+                    work.push_back(t);
+                }
+        }
+    }
+    g->min_push_cap = min_cap;
+    struct Cfg {
+        uint32_t q, ws, ctx;
+    };
+    std::vector<Cfg> cfg;
+    const size_t cap_rows = kStateMaskBudget / (Wv * 8);
+    auto add_group = [&](uint32_t ws_lo, uint32_t ws_hi, bool ctx0, bool ctx12) {
+        std::vector<Cfg> grp;
+        for (uint32_t q : g->plain_q)
+            for (uint32_t ws = ws_lo; ws <= ws_hi; ws++) {
+                if (ws > 0 && !ws_target[q]) continue;
+                if (ctx0) grp.push_back({q, ws, 0});
+                if (ctx12 && inside[q] && min_cap > 0) {
+                    grp.push_back({q, ws, 1});
+                    grp.push_back({q, ws, 2});
+                }
+            }
+        if (cfg.size() + grp.size() <= cap_rows) cfg.insert(cfg.end(), grp.begin(), grp.end());
+    };
+    add_group(0, 0, true, false);
+    add_group(0, 0, false, true);
+    if (g->k.ws_max > 0) {
+        add_group(1, g->k.ws_max, true, false);
+        add_group(1, g->k.ws_max, false, true);
+    }
+    const size_t n = cfg.size();
+    if (n == 0) return CG_OK;
     std::vector<cg_state> st(n);
+    std::vector<uint8_t> need(n, 0);
+    std::vector<int32_t> idx((size_t)QL * WD * 3, -1);
     for (size_t i = 0; i < n; i++) {
         cg_state &c = st[i];
         memset(&c, 0, sizeof c);
-        c.q = (uint16_t)g->plain_q[i];
+        c.q = (uint16_t)cfg[i].q;
         c.ret = (uint16_t)g->k.start;
+        c.ws = (uint8_t)cfg[i].ws;
+        c.depth = cfg[i].ctx ? 1 : 0;
+        c.stk = cfg[i].ctx == 2 ? 1u : 0u;
+        need[i] = cfg[i].ctx != 0;
+        idx[((size_t)cfg[i].q * WD + cfg[i].ws) * 3 + cfg[i].ctx] = (int32_t)i;
     }
-    std::vector<int32_t> idx(g->k.q_limit, -1);
-    for (size_t i = 0; i < n; i++) idx[g->plain_q[i]] = (int32_t)i;
     cg_state *d_st = nullptr;
     void *d_ws = nullptr;
-    uint64_t *d_mask = nullptr;
+    uint64_t *d_mask = nullptr, *d_s0 = nullptr;
+    uint8_t *d_need = nullptr;
     int rc = CG_OK;
     const size_t ws_bytes = (size_t)fill_plan_stride(g) * 4 * n;
-    if (upload(&d_st, st.data(), n) != CG_OK || hipMalloc(&d_ws, ws_bytes) != hipSuccess ||
+    if (upload(&d_st, st.data(), n) != CG_OK || upload(&d_need, need.data(), n) != CG_OK ||
+        upload(&d_s0, f.s0.data(), f.s0.size()) != CG_OK || hipMalloc(&d_ws, ws_bytes) != hipSuccess ||
         hipMalloc((void **)&d_mask, n * Wv * 8) != hipSuccess) {
         set_error("state masks: allocation failed: %s", hipGetErrorString(hipGetLastError()));
         rc = CG_E_DEVICE;
     }
     if (rc == CG_OK) rc = launch_fill(g, d_st, (int)n, d_mask, (int)Wv, d_ws, nullptr);
+    if (rc == CG_OK) rc = launch_mask_and(d_mask, d_need, d_s0, (int)n, (int)Wv, nullptr);
     if (rc == CG_OK && hipStreamSynchronize(nullptr) != hipSuccess) {
         set_error("state masks: %s", hipGetErrorString(hipGetLastError()));
         rc = CG_E_DEVICE;
@@ -269,6 +450,8 @@ int build_state_masks(cg_grammar *g) {
     }
     (void)hipFree(d_st);
     (void)hipFree(d_ws);
+    (void)hipFree(d_need);
+    (void)hipFree(d_s0);
     if (rc != CG_OK) {
         (void)hipFree(d_mask);
         return rc;
@@ -339,6 +522,8 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
         build_fill_tables(g, tok_bytes, tok_offsets, tokinfo, f);
         g->lex_tiles = (int32_t)(f.lex_idlen.size() / kTile);
         g->q_tiles = (int32_t)(f.q_idlen.size() / kTile);
+        g->c_tiles = (int32_t)(f.c_idlen.size() / kTile);
+        g->qc_tiles = (int32_t)(f.qc_idlen.size() / kTile);
         if (fill_lds_bytes(g, 1) + 1024 > (size_t)g->lds_max) {
             set_error("transition table of %u slots needs %zu bytes of LDS in fill_bitmask, the device has %d",
                       g->comb_len, fill_lds_bytes(g, 1), g->lds_max);
@@ -357,6 +542,15 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
             upload(&g->dev.q_tile, f.q_tile.data(), f.q_tile.size()) ||
             upload(&g->dev.strbits, f.strbits.data(), f.strbits.size()) ||
             upload(&g->dev.closebits, f.closebits.data(), f.closebits.size()) ||
+            upload(&g->dev.c_idlen, f.c_idlen.data(), f.c_idlen.size()) ||
+            upload(&g->dev.c_jump, f.c_jump.data(), f.c_jump.size()) ||
+            upload(&g->dev.c_w, f.c_w.data(), f.c_w.size()) ||
+            upload(&g->dev.c_tile, f.c_tile.data(), f.c_tile.size()) ||
+            (!f.retmask2.empty() && (upload(&g->dev.retmask2, f.retmask2.data(), f.retmask2.size()) ||
+                                     upload(&g->dev.qc_idlen, f.qc_idlen.data(), f.qc_idlen.size()) ||
+                                     upload(&g->dev.qc_posch, f.qc_posch.data(), f.qc_posch.size()) ||
+                                     upload(&g->dev.qc_w, f.qc_w.data(), f.qc_w.size()) ||
+                                     upload(&g->dev.qc_tile, f.qc_tile.data(), f.qc_tile.size()))) ||
             (!f.retmask.empty() && (upload(&g->dev.retmask, f.retmask.data(), f.retmask.size()) ||
                                     upload(&g->dev.rq_idx, f.rq_idx.data(), f.rq_idx.size()))) ||
             (g->has_forced && upload(&g->dev.forced, g->host_forced.data(), g->host_forced.size()))) {
@@ -364,7 +558,7 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
             release(g);
             return CG_E_DEVICE;
         }
-        rc = build_state_masks(g);
+        rc = build_state_masks(g, f);
         if (rc != CG_OK) {
             release(g);
             return rc;

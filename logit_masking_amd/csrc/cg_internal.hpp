@@ -214,6 +214,7 @@ constexpr int kKeysPerLead = 257;
 constexpr int kTile = 64;          // tokens per candidate tile (one wave)
 constexpr int kStrBitsets = 33;    // in-string bitsets for budgets 0..32 code points
 constexpr uint32_t kNoQuote = 63;  // jump field of a token without a quote
+constexpr int kPushLimit = 6;      // containers a token may open and still take its bit from the table
 
 __host__ __device__ inline uint32_t lead_key(uint32_t b1, uint32_t b2, uint32_t len) {
     return b1 * kKeysPerLead + (len == 1 ? 0u : b2 + 1u);
@@ -226,11 +227,23 @@ struct DeviceTables {
     uint32_t *tokinfo = nullptr;  // [V] length + string-body summary
     uint64_t *legal = nullptr;    // [q_limit][4] bytes with a transition out of state q (256-bit set)
     uint32_t *forced = nullptr;   // [ceil(q_limit / 32)] bit q: engine-written state (null: none)
-    // Masks of plain configurations, computed once: state_mask[smask_idx[q]]
-    // is the mask of (q, no whitespace run, no open container) for a state
-    // q outside strings; smask_idx[q] < 0 where there is none (null: no table).
+    // Masks computed once, for a state q outside strings with whitespace run
+    // ws: context 0 = no open container (the whole mask), 1 / 2 = inside an
+    // open object / array (the tokens that stay inside it, see push_limit);
+    // state_mask[smask_idx[(q * (ws_max + 1) + ws) * 3 + ctx]], < 0: none.
     uint64_t *state_mask = nullptr;  // [n_smask][Wv]
-    int32_t *smask_idx = nullptr;    // [q_limit]
+    int32_t *smask_idx = nullptr;    // [q_limit * (ws_max + 1) * 3]
+    // Tokens whose brackets may close the container a row is in, or open
+    // more than kPushLimit: walked, like the lexicographic list, for rows
+    // that take context 1 / 2 from the table.
+    uint32_t *c_idlen = nullptr, *c_jump = nullptr, *c_w = nullptr;
+    uint2 *c_tile = nullptr;
+    // String rows inside an open container: retmask2[(rq_idx[R] * 2 + kind)]
+    // holds the closing tokens whose bytes after the quote stay inside it
+    // (null: no table); the other closing tokens are the qc list.
+    uint64_t *retmask2 = nullptr;    // [n_resume * 2][Wv]
+    uint32_t *qc_idlen = nullptr, *qc_posch = nullptr, *qc_w = nullptr;
+    uint2 *qc_tile = nullptr;
     // Tokens that close a string: closebits[c] = the content before the
     // quote fits a budget of c code points; retmask[rq_idx[R]] = the bytes
     // after the quote are accepted from resume state R with no open
@@ -276,6 +289,9 @@ struct cg_grammar {
     bool has_forced = false;
     std::vector<uint32_t> plain_q;  // live states outside strings (candidates of the state-mask table)
     int32_t n_smask = 0;            // rows of dev.state_mask
+    int32_t c_tiles = 0;            // tiles of the closing-token list
+    int32_t qc_tiles = 0;           // tiles of the string-closing tokens that leave the container
+    int32_t min_push_cap = 0;       // smallest depth cap of any push (0: no pushes)
     cg::DeviceTables dev;
 };
 

@@ -244,8 +244,17 @@ struct FillArgs {
     unsigned long long *mask;
     int words_per_row;
     const uint32_t *forced;  // engine-written states: empty mask (null: none)
-    const uint64_t *state_mask;  // precomputed masks of plain configurations (null: none)
+    const uint64_t *state_mask;  // masks computed once (null: none), see DeviceTables
     const int32_t *smask_idx;
+    int ws_dim;                  // ws_max + 1
+    int push_room;               // rows at depth < push_room may use contexts 1 / 2
+    const uint32_t *c_idlen, *c_jump, *c_w;  // the closing-token list
+    const uint2 *c_tile;
+    int c_tiles;
+    const uint64_t *retmask2;                 // string rows inside a container (null: none)
+    const uint32_t *qc_idlen, *qc_posch, *qc_w;
+    const uint2 *qc_tile;
+    int qc_tiles;
     const uint64_t *closebits, *retmask;  // string rows with no open container (rq_idx null: none)
     const int32_t *rq_idx;
     uint32_t *plan;       // per row: [0] listed tiles, [1..] their indices
@@ -338,6 +347,10 @@ __device__ __forceinline__ uint32_t byte_at(const uint32_t (&w)[NW], uint32_t i)
     return (x >> (8 * (i & 3))) & 0xFFu;
 }
 
+// The candidate lists a listed tile can come from (bits 30..31 of its index).
+enum : uint32_t { LIST_LEX = 0, LIST_CLOSE = 1, LIST_QSTR = 2, LIST_QCLOSE = 3 };
+constexpr uint32_t kTileMask = (1u << 30) - 1;
+
 // One tile's worth of a lane: its token (or padding) and where its walk starts.
 template <int NW>
 struct LaneTok {
@@ -346,13 +359,25 @@ struct LaneTok {
 };
 
 template <int NW>
-__device__ __forceinline__ void load_lane(LaneTok<NW> &x, bool in_str, int i, const FillArgs &a) {
-    if (in_str) {
+__device__ __forceinline__ void load_lane(LaneTok<NW> &x, uint32_t list, int i, const FillArgs &a) {
+    if (list == LIST_QSTR) {
         const int n = a.q_tiles * kTile;
         x.il = a.q_idlen[i];
         x.aux = a.q_posch[i];
 #pragma unroll
         for (int j = 0; j < NW; j++) x.w[j] = a.q_w[(size_t)j * n + i];
+    } else if (list == LIST_QCLOSE) {
+        const int n = a.qc_tiles * kTile;
+        x.il = a.qc_idlen[i];
+        x.aux = a.qc_posch[i];
+#pragma unroll
+        for (int j = 0; j < NW; j++) x.w[j] = a.qc_w[(size_t)j * n + i];
+    } else if (list == LIST_CLOSE) {
+        const int n = a.c_tiles * kTile;
+        x.il = a.c_idlen[i];
+        x.aux = a.c_jump[i];
+#pragma unroll
+        for (int j = 0; j < NW; j++) x.w[j] = a.c_w[(size_t)j * n + i];
     } else {
         const int n = a.lex_tiles * kTile;
         x.il = a.lex_idlen[i];
@@ -377,8 +402,29 @@ __global__ __launch_bounds__(kPlanThreads) void k_fill_plan(FillArgs a) {
     unsigned long long *out = a.mask + (size_t)r * a.words_per_row;
     const bool live = row_live(s, k) && !forced_state(a.forced, s.q);
     const bool in_str = live && s.q == k.s_body;
-    const int n_all = !live ? 0 : in_str ? a.q_tiles : a.lex_tiles;
-    const uint2 *tkeys = in_str ? a.q_tile : a.lex_tile;
+    // the table's row for this configuration: context 0 = no open container
+    // (the whole mask), 1 / 2 = inside an object / array within push room
+    // (the tokens that stay inside it; the closing list is walked)
+    int ctx = -1, sidx = -1;
+    if (live && !in_str && a.smask_idx && s.ws < (uint32_t)a.ws_dim) {
+        if (s.depth == 0 && s.stk == 0) ctx = 0;
+        else if (s.depth >= 1 && (int)s.depth < a.push_room) ctx = 1 + (int)(s.stk & 1u);
+        if (ctx >= 0) sidx = a.smask_idx[((size_t)s.q * a.ws_dim + s.ws) * 3 + ctx];
+    }
+    // a string row inside an open container within push room: the closing
+    // tokens that stay inside it come from retmask2, the rest are walked
+    const int ridx2 = (in_str && a.retmask2 && s.depth >= 1 && (int)s.depth < a.push_room) ? a.rq_idx[s.ret] : -1;
+    const uint32_t list = in_str ? (ridx2 >= 0 ? LIST_QCLOSE : LIST_QSTR)
+                                 : (sidx >= 0 && ctx > 0) ? LIST_CLOSE : LIST_LEX;
+    const int n_all = !live                  ? 0
+                      : list == LIST_QSTR    ? a.q_tiles
+                      : list == LIST_QCLOSE  ? a.qc_tiles
+                      : list == LIST_CLOSE   ? a.c_tiles
+                                             : a.lex_tiles;
+    const uint2 *tkeys = list == LIST_QSTR     ? a.q_tile
+                         : list == LIST_QCLOSE ? a.qc_tile
+                         : list == LIST_CLOSE  ? a.c_tile
+                                               : a.lex_tile;
     uint2 kk[kPlanKeys];
 #pragma unroll
     for (int i = 0; i < kPlanKeys; i++) {
@@ -387,21 +433,21 @@ __global__ __launch_bounds__(kPlanThreads) void k_fill_plan(FillArgs a) {
     }
     // base words: zero; inside a string, the tokens that stay inside within
     // the budget, and with no open container also the tokens that close the
-    // string and go on legally (then nothing is walked); in a plain
-    // configuration (no whitespace run, no open container, outside
-    // strings), the state's whole precomputed mask
+    // string and go on legally (then nothing is walked); outside strings,
+    // the table's row (context 0: the whole mask, nothing walked)
     const bool plain = live && s.depth == 0 && s.stk == 0;
-    const int sidx = (plain && !in_str && a.smask_idx && s.ws == 0) ? a.smask_idx[s.q] : -1;
     const int ridx = (plain && in_str && a.rq_idx) ? a.rq_idx[s.ret] : -1;
     const size_t c_off = (size_t)min(s.cnt, (uint32_t)kStrBitsets - 1u) * a.Wv;
     const uint64_t *base = in_str ? a.strbits + c_off : sidx >= 0 ? a.state_mask + (size_t)sidx * a.Wv : nullptr;
-    if (ridx >= 0) {
-        const uint64_t *cb = a.closebits + c_off, *rm = a.retmask + (size_t)ridx * a.Wv;
+    if (ridx >= 0 || ridx2 >= 0) {
+        const uint64_t *cb = a.closebits + c_off;
+        const uint64_t *rm = ridx >= 0 ? a.retmask + (size_t)ridx * a.Wv
+                                       : a.retmask2 + ((size_t)ridx2 * 2 + (s.stk & 1u)) * a.Wv;
         for (int i = tid; i < a.Wv; i += kPlanThreads) out[i] = base[i] | (cb[i] & rm[i]);
     } else {
         for (int i = tid; i < a.Wv; i += kPlanThreads) out[i] = base ? base[i] : 0ull;
     }
-    if (!live || sidx >= 0 || ridx >= 0) {
+    if (!live || (sidx >= 0 && ctx == 0) || ridx >= 0) {
         if (tid == 0) plan[0] = 0;
         return;
     }
@@ -440,7 +486,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_fill_plan(FillArgs a) {
                 act = in_str ? (kk[i].x == 0 || any_bits(after_quote, kk[i].x - 1, kk[i].y - 1))
                              : span_legal(kk[i].x, kk[i].y, valid1, second);
             }
-            append_tiles(act, (uint32_t)t, plan + 1, &n_active);
+            append_tiles(act, (uint32_t)t | (list << 30), plan + 1, &n_active);
         }
     }
     __syncthreads();
@@ -526,11 +572,11 @@ __global__ __launch_bounds__(kWalkThreads) void k_fill_walk(FillArgs a) {
         LaneTok<NW> cur{}, nxt{};
         fetch_ref(t0, g, total, prefix, nb, rb, a);
         fetch_ref(t1, g + stride, total, prefix, nb, rb, a);
-        if (g < total) load_lane(cur, t0.s.q == k.s_body, (int)t0.tile * kTile + lane, a);
+        if (g < total) load_lane(cur, t0.tile >> 30, (int)(t0.tile & kTileMask) * kTile + lane, a);
         for (; g < total; g += stride) {
             fetch_ref(t2, g + 2 * stride, total, prefix, nb, rb, a);
-            if (g + stride < total) load_lane(nxt, t1.s.q == k.s_body, (int)t1.tile * kTile + lane, a);
-            const bool in_str = t0.s.q == k.s_body;
+            if (g + stride < total) load_lane(nxt, t1.tile >> 30, (int)(t1.tile & kTileMask) * kTile + lane, a);
+            const bool in_str = (t0.tile >> 30) >= LIST_QSTR;
             const Walker w0 = load_walker(t0.s);
             const uint32_t id = cur.il & 0xFFFFFFu;
             int end = (int)(cur.il >> 24), start = 0;
@@ -596,6 +642,21 @@ int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *by
     return launch_status("force_bytes");
 }
 
+// rows[i] &= m for the rows with need[i] (the table's context 1 / 2 rows)
+__global__ __launch_bounds__(256) void k_mask_and(uint64_t *__restrict__ rows, const uint8_t *__restrict__ need,
+                                                  const uint64_t *__restrict__ m, int Wv) {
+    const int r = blockIdx.x;
+    if (!need[r]) return;
+    uint64_t *row = rows + (size_t)r * Wv;
+    for (int i = threadIdx.x; i < Wv; i += blockDim.x) row[i] &= m[i];
+}
+
+int launch_mask_and(uint64_t *rows, const uint8_t *need, const uint64_t *m, int n, int Wv, hipStream_t st) {
+    if (n == 0) return CG_OK;
+    hipLaunchKernelGGL(k_mask_and, dim3(n), dim3(256), 0, st, rows, need, m, Wv);
+    return launch_status("state masks (and)");
+}
+
 // Plan of one row: listed-tile count + up to every tile of the longer list.
 int fill_plan_stride(const cg_grammar *g) {
     return (1 + std::max(1, std::max(g->lex_tiles, g->q_tiles)) + 63) / 64 * 64;
@@ -640,6 +701,19 @@ static int launch_fill_nw(const cg_grammar *g, const cg_state *states, int B, ui
     a.forced = g->dev.forced;
     a.state_mask = g->dev.state_mask;
     a.smask_idx = g->dev.state_mask ? g->dev.smask_idx : nullptr;
+    a.ws_dim = (int)g->k.ws_max + 1;
+    a.push_room = g->min_push_cap - kPushLimit;
+    a.c_idlen = g->dev.c_idlen;
+    a.c_jump = g->dev.c_jump;
+    a.c_w = g->dev.c_w;
+    a.c_tile = g->dev.c_tile;
+    a.c_tiles = g->c_tiles;
+    a.retmask2 = g->dev.retmask ? g->dev.retmask2 : nullptr;
+    a.qc_idlen = g->dev.qc_idlen;
+    a.qc_posch = g->dev.qc_posch;
+    a.qc_w = g->dev.qc_w;
+    a.qc_tile = g->dev.qc_tile;
+    a.qc_tiles = g->qc_tiles;
     a.closebits = g->dev.closebits;
     a.retmask = g->dev.retmask;
     a.rq_idx = g->dev.retmask ? g->dev.rq_idx : nullptr;
