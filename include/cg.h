@@ -234,9 +234,10 @@ size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab);
  *     u = (w + 1/2) 2^-32, and w is word (i & 3) of Philox4x32-10 (Salmon et
  *     al., SC'11) at counter (i >> 2, d_step[r], l, 0) with key d_seed[r]
  *     (low word first).  logprob = x_id / T - logsumexp_allowed(x / T).
- *   No allowed token: id = -1, logprob = 0.
+ *   An allowed token whose logit is -inf carries no probability.  No allowed
+ *   token of finite logit: id = -1, logprob = 0.
  * ("Constrained decoding", "The guarantee": sampling runs after masking.)
- * row_stride >= vocab elements; vocab <= 6,291,456.
+ * row_stride >= vocab elements; vocab <= 4,194,304 (2048 chunks).
  * d_workspace: cg_sample_workspace_bytes(batch, vocab) bytes, 16-byte
  *   aligned; may be NULL when that size is 0 (this build keeps every
  *   intermediate on chip, so it always is).

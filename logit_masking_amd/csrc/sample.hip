@@ -518,12 +518,12 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         int c = wave;
         if (c < K) load_chunk<DT, VEC>(cur, logits, rowbase, mrow, V, c, lane);
         if (kAhead == 2 && c + kWaves < K) load_chunk<DT, VEC>(nxt, logits, rowbase, mrow, V, c + kWaves, lane);
-        // chunk noise G(1, c) for this wave's chunks (c = wave + 16 lane), while the loads fly
-        const int cg = wave + kWaves * lane;
-        if (!greedy && cg < K) {
-            const uint4 o = philox4x32_10(make_uint4((uint32_t)cg >> 2, stp, 1u, 0u), k0, k1);
-            ci[cg].g = gumbel64(pick_word(o, cg & 3));
-        }
+        // chunk noise G(1, c) of every chunk (c = wave + 16 lane + 1024 j), while the loads fly
+        if (!greedy)
+            for (int cg = wave + kWaves * lane; cg < K; cg += kWaves * 64) {
+                const uint4 o = philox4x32_10(make_uint4((uint32_t)cg >> 2, stp, 1u, 0u), k0, k1);
+                ci[cg].g = gumbel64(pick_word(o, cg & 3));
+            }
         __syncthreads();  // the mask table
         double best = -INFINITY;
         for (; c < K; c += kWaves) {
@@ -592,7 +592,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             wave_argmax(mv, mc);
             if (lane == 0) {
                 wdec.mv = mv;
-                wdec.mc = mc;
+                wdec.mc = mv > -INFINITY ? mc : -1;  // allowed tokens all at -inf: nothing to draw
             }
         } else if (!greedy) {
             Top2d cs{-INFINITY, -INFINITY, -1};

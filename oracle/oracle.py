@@ -612,9 +612,11 @@ def sample_row(x, allowed, T, seed, step, chunk=CHUNK):
     (level 0, element i).  P(id) = P(c*) P(id | c*) = softmax(x/T) on the
     mask.  logprob = x_id/T - logsumexp_{allowed} x/T.
     info: top-2 score margins at each level (inf when there is one candidate).
+    An allowed token whose logit is -inf carries no probability; with no
+    allowed token of finite logit there is nothing to draw: (-1, 0).
     """
     x = np.asarray(x, dtype=np.float64)
-    allowed = np.asarray(allowed, dtype=bool)
+    allowed = np.asarray(allowed, dtype=bool) & (x > -np.inf)
     V = len(x)
     info = {"margin_chunk": math.inf, "margin_token": math.inf}
     if not allowed.any():

@@ -1,0 +1,146 @@
+"""Edge cases of the device path against the oracle: the largest vocabulary
+the sampler takes, one past it, -inf logits, extreme temperatures, a large
+batch, and the fill at a vocabulary of a million tokens."""
+import numpy as np
+import pytest
+
+import logit_masking_amd as cg
+from logit_masking_amd import workloads as W
+from oracle import oracle as O
+from tests.gpu_util import NTHREADS, device_rows, gpu_masks, oracle_masks, random_walk, say
+
+pytestmark = pytest.mark.gpu
+
+V_MAX = 4_194_304  # 2048 chunk summaries of 24 bytes fill the 48 KiB the sampler gives them
+NEAR_TIE = 1e-6
+
+
+def _run_sample(x, bits, T, seeds, step, dtype):
+    """x: float64 [B, V] (values representable in dtype), bits: bool [B, V]."""
+    import torch
+    B, V = x.shape
+    logits = torch.from_numpy(x).to(dtype).cuda()
+    W_ = (V + 63) // 64
+    pad = np.zeros((B, W_ * 64), dtype=bool)
+    pad[:, :V] = bits
+    words = np.packbits(pad.reshape(B, W_, 64)[:, :, ::-1], axis=2, bitorder="big").view(">u8").astype(np.uint64)
+    mask = torch.from_numpy(words.reshape(B, W_).view(np.int64)).cuda()
+    temp = torch.full((B,), float(T), dtype=torch.float32, device="cuda")
+    seed_t = torch.from_numpy(np.asarray(seeds, dtype=np.uint64).view(np.int64)).cuda()
+    steps = torch.full((B,), step, dtype=torch.int32, device="cuda")
+    ws = cg.new_workspace(B, V)
+    ids = torch.empty(B, dtype=torch.int32, device="cuda")
+    lp = torch.empty(B, dtype=torch.float32, device="cuda")
+    cg.apply_mask_sample(logits, mask, temp, seed_t, steps, ws, ids, lp)
+    torch.cuda.synchronize()
+    return logits.double().cpu().numpy(), ids.cpu().numpy(), lp.cpu().numpy()
+
+
+def _check(x, bits, T, seeds, step, ids, lp):
+    ties = 0
+    for r in range(x.shape[0]):
+        i, l, info = O.sample_row(x[r], bits[r], T, int(seeds[r]), step)
+        if i < 0:
+            assert ids[r] == -1 and lp[r] == 0.0, r
+            continue
+        if T > 0 and min(info["margin_chunk"], info["margin_token"]) < NEAR_TIE:
+            ties += 1
+            assert bits[r, ids[r]]
+            continue
+        assert ids[r] == i, (r, ids[r], i)
+        assert abs(lp[r] - l) < 1e-5, (r, lp[r], l)
+    return ties
+
+
+@pytest.mark.parametrize("dtype_name,T", [("bfloat16", 0.7), ("bfloat16", 0.0), ("float32", 0.7)])
+def test_sample_max_vocab(dtype_name, T):
+    import torch
+    say("max vocab", dtype_name, T)
+    rng = np.random.default_rng(11)
+    B = 2
+    x = rng.normal(scale=3.0, size=(B, V_MAX))
+    bits = rng.random((B, V_MAX)) < 0.3
+    dt = getattr(torch, dtype_name)
+    xs, ids, lp = _run_sample(x, bits, T, [12345, 67890], 4, dt)
+    assert _check(xs, bits, T, [12345, 67890], 4, ids, lp) <= 1
+
+
+def test_sample_vocab_over_limit():
+    import torch
+    say("over limit")
+    V = V_MAX + 1
+    logits = torch.zeros((1, V), dtype=torch.bfloat16, device="cuda")
+    mask = torch.zeros((1, (V + 63) // 64), dtype=torch.int64, device="cuda")
+    one = lambda dt, v: torch.full((1,), v, dtype=dt, device="cuda")
+    ws = torch.zeros(2, dtype=torch.float64, device="cuda")
+    with pytest.raises(cg.CgError) as e:
+        cg.apply_mask_sample(logits, mask, one(torch.float32, 0.7), one(torch.int64, 1), one(torch.int32, 0), ws,
+                             one(torch.int32, 0), one(torch.float32, 0))
+    assert e.value.code == cg.CG_E_ARG
+
+
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_minus_infinity_logits(T):
+    """-inf logits carry no probability; a row whose allowed logits are all
+    -inf has nothing to draw (-1)."""
+    import torch
+    say("-inf", T)
+    rng = np.random.default_rng(12)
+    B, V = 6, 40000
+    x = rng.normal(scale=2.0, size=(B, V))
+    bits = rng.random((B, V)) < 0.4
+    x[rng.random((B, V)) < 0.3] = -np.inf
+    x[1, :] = np.where(bits[1], -np.inf, x[1, :])      # every allowed logit -inf
+    x[2, 2048:4096] = -np.inf                         # a whole chunk
+    seeds = list(range(100, 100 + B))
+    for dt in (torch.bfloat16, torch.float32):
+        xs, ids, lp = _run_sample(x, bits, T, seeds, 9, dt)
+        _check(xs, bits, T, seeds, 9, ids, lp)
+        assert ids[1] == -1
+
+
+@pytest.mark.parametrize("T", [1e-3, 50.0])
+def test_extreme_temperatures(T):
+    import torch
+    say("temperature", T)
+    rng = np.random.default_rng(13)
+    B, V = 8, 128256
+    x = rng.normal(scale=3.0, size=(B, V))
+    bits = rng.random((B, V)) < 0.5
+    seeds = [int(s) for s in rng.integers(0, 2**63, size=B)]
+    xs, ids, lp = _run_sample(x, bits, T, seeds, 2, torch.bfloat16)
+    assert _check(xs, bits, T, seeds, 2, ids, lp) <= 1
+
+
+def test_large_batch():
+    """4096 rows at once; 64 of them checked against the oracle."""
+    import torch
+    say("large batch")
+    rng = np.random.default_rng(14)
+    B, V = 4096, 32000
+    x = rng.normal(scale=2.0, size=(B, V)).astype(np.float32).astype(np.float64)
+    bits = rng.random((B, V)) < 0.6
+    seeds = [int(s) for s in rng.integers(0, 2**63, size=B)]
+    xs, ids, lp = _run_sample(x, bits, 0.7, seeds, 5, torch.float32)
+    chk = list(range(0, B, 64))
+    assert _check(xs[chk], bits[chk], 0.7, [seeds[r] for r in chk], 5, ids[chk], lp[chk]) <= 2
+
+
+def test_fill_million_token_vocab():
+    """The tool-call grammar over a vocabulary of 1,000,000 tokens: masks of
+    rows at random prefixes, bit-exact."""
+    say("million vocab")
+    blob, off = W.make_vocab(3, 1_000_000)
+    toks = [blob[off[i]:off[i + 1]] for i in range(len(off) - 1)]
+    g = cg.Grammar(W.spec_json(3), blob, off)
+    og = O.load_spec(W.spec_json(3))
+    rng = W.SplitMix(15)
+    seqs, rows = [], []
+    for r in range(8):
+        s, row = random_walk(og, toks, rng.below(40), rng)
+        seqs.append(s)
+        rows.append(row)
+    st, steps, _ = device_rows(g, seqs)
+    got = gpu_masks(g, st)
+    want, _ = oracle_masks(og, rows, blob, off)
+    assert np.array_equal(got[:, :want.shape[1]], want)

@@ -492,3 +492,20 @@ def test_sampled_logprob():
 def test_gumbel_uniform_open_interval():
     g = O.gumbel(np.array([0, 0xFFFFFFFF], dtype=np.uint64))
     assert np.all(np.isfinite(g))
+
+
+def test_minus_infinity_logits():
+    """Allowed tokens at -inf carry no probability: the pick and log-probability
+    equal those with such tokens masked out; all of them -inf: nothing to draw."""
+    rng = np.random.default_rng(9)
+    x = rng.normal(size=5000)
+    allowed = rng.random(5000) < 0.5
+    x2 = x.copy()
+    dead = allowed & (rng.random(5000) < 0.3)
+    x2[dead] = -np.inf
+    for T in (0.0, 0.7):
+        a = O.sample_row(x2, allowed, T, 77, 3)
+        b = O.sample_row(x, allowed & ~dead, T, 77, 3)
+        assert a[0] == b[0] and abs(a[1] - b[1]) < 1e-12
+        x3 = np.where(allowed, -np.inf, x)
+        assert O.sample_row(x3, allowed, T, 77, 3)[:2] == (-1, 0.0)
