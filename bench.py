@@ -356,6 +356,103 @@ def draft_bench(args):
     print(json.dumps(out))
 
 
+def overlap_bench(args):
+    """--overlap: the mask is a function of the rows' states alone, so it can
+    be computed while the model's forward pass runs ("Evaluator aware
+    decoding", "Why isn't this in production APIs yet?").  A stand-in for the
+    end of the forward pass -- the lm_head product of a batch of hidden
+    states (4096 wide, bf16) with a [4096, 128256] weight, which makes the
+    step's logits -- runs on the main stream while cg_fill_bitmask runs on a
+    second stream; cg_sample_advance waits for both.  Timed against the same
+    three calls on one stream.  Tool-call workload, batch 256.  Prints one
+    JSON line."""
+    import torch
+    import logit_masking_amd as cg
+    from logit_masking_amd import workloads as W
+    c = W.CONFIGS[CONFIG]
+    B, T = c["B"], c["T"]
+    blob, off = W.make_vocab(CONFIG)
+    V = len(off) - 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    g = cg.Grammar(W.spec_json(CONFIG), blob, off, gen_cap=W.GEN_CAP)
+    hidden = 4096
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12345)
+    w_head = (torch.randn((hidden, V), generator=gen, device=dev) * (3.0 / hidden ** 0.5)).to(torch.bfloat16)
+    hs = [torch.randn((B, hidden), generator=gen, device=dev).to(torch.bfloat16) for _ in range(8)]
+    mask = torch.empty((B, g.W), dtype=torch.int64, device=dev)
+    temp = torch.full((B,), T, dtype=torch.float32, device=dev)
+    seed = torch.from_numpy(np.array(W.row_seeds(CONFIG, B), dtype=np.uint64).view(np.int64)).to(dev)
+    ws = cg.new_workspace(B, V, dev)
+    fws = g.new_fill_workspace(B, dev)
+    ids = torch.empty(B, dtype=torch.int32, device=dev)
+    lp = torch.empty(B, dtype=torch.float32, device=dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=dev)  # default priority
+    n = args.steps
+
+    def run(overlap, st, steps, status):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ready = torch.cuda.Event()
+        torch.cuda.synchronize()
+        e0.record(main)
+        for s in range(n):
+            if overlap:
+                side.wait_stream(main)                 # the previous step's advance
+                g.fill_bitmask(st, mask, fws, side)
+                ready.record(side)
+                logits = torch.matmul(hs[s % len(hs)], w_head)
+                main.wait_event(ready)
+            else:
+                g.fill_bitmask(st, mask, fws, main)
+                logits = torch.matmul(hs[s % len(hs)], w_head)
+            g.sample_advance(logits, mask, temp, seed, steps, ws, ids, lp, st, status, main)
+        e1.record(main)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def fresh():
+        st = g.new_states(B, dev)
+        g.init_state(st)
+        return st, torch.zeros(B, dtype=torch.int32, device=dev), torch.zeros(B, dtype=torch.int32, device=dev)
+
+    for _ in range(2):  # load kernels and the GEMM plan
+        run(False, *fresh())
+        run(True, *fresh())
+    st_a, steps_a, status_a = fresh()
+    us_serial = run(False, st_a, steps_a, status_a)
+    st_b, steps_b, status_b = fresh()
+    us_overlap = run(True, st_b, steps_b, status_b)
+    same = bool(torch.equal(st_a, st_b) and torch.equal(steps_a, steps_b))
+    # the product alone
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for s in range(n):
+        torch.matmul(hs[s % len(hs)], w_head)
+    e1.record(main)
+    torch.cuda.synchronize()
+    us_gemm = e0.elapsed_time(e1) * 1e3 / n
+    out = {
+        "metric": "us per decode step with the fill on a second stream, behind a stand-in lm_head product",
+        "value": round(us_overlap, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": n,
+        "higher_is_better": False,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"tool-call grammar (8 tools), vocab {V}, batch {B}; lm_head stand-in "
+                               f"[{B}, {hidden}] x [{hidden}, {V}] bf16 (hipBLASLt via torch.matmul)",
+                   "batch": B, "vocab": V},
+        "us_step_one_stream": round(us_serial, 2),
+        "us_step_fill_on_second_stream": round(us_overlap, 2),
+        "us_lm_head_alone": round(us_gemm, 2),
+        "same_trajectory": same,
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,6 +469,8 @@ def main():
                     help="workload (1-6); the headline line is config 3, the others are for reference")
     ap.add_argument("--draft", type=int, default=0,
                     help="measure masks along K-token drafts instead (its own JSON line)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="measure the fill on a second stream behind a stand-in lm_head product (its own JSON line)")
     ap.add_argument("--inject", action="store_true",
                     help="measure result injection on text with calc spans instead (its own JSON line)")
     args = ap.parse_args()
@@ -385,6 +484,9 @@ def main():
         return
     if args.draft:
         draft_bench(args)
+        return
+    if args.overlap:
+        overlap_bench(args)
         return
 
     import torch

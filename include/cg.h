@@ -144,7 +144,9 @@ typedef struct {
  *   additionalProperties:false (required whenever properties is given);
  *   string enum; maxLength; integer minimum/maximum; items; maxItems;
  *   anyOf whose alternatives start with different bytes; {} = any JSON
- *   value.  Anything else -- $ref, pattern, format, oneOf, allOf, minItems,
+ *   value; the string pattern "^-?(0|[1-9][0-9]*)$" (a canonical signed
+ *   integer, see cg_contract_model_spec).  Anything else -- $ref, any other
+ *   pattern, format, oneOf, allOf, minItems,
  *   minLength, multipleOf, ... -- is refused with CG_E_UNSUPPORTED and its
  *   JSON path ("Constrained Decoding Under Matched Conditions", "What exists
  *   beyond the experiment": typed fail-closed refusals).
@@ -154,15 +156,27 @@ typedef struct {
  *   At most 32 bytes per token.
  * opts: may be NULL (gen_cap 2048, upload).
  * out: receives the handle.  Returns CG_OK or a CG_E_* code.
+ * Compiled grammars are cached: a compile with the same spec text,
+ * vocabulary, options and device returns the same read-only handle with one
+ * more reference (cg_free_grammar drops one); up to 8 handles no one holds
+ * are kept for later identical compiles ("Evaluator aware decoding", "A
+ * concrete prototype on llama.cpp": grammar caching keeps repeated grammars
+ * from costing compilation).  Thread-safe.
  */
 int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *tok_bytes,
                        const uint32_t *tok_offsets, int32_t vocab_size, const cg_options *opts, cg_grammar **out);
 
-/* Release host and device memory of a grammar.  NULL is ignored. */
+/* Drop one reference to a grammar; its memory is released when none is left
+ * and it falls out of the cache.  NULL is ignored. */
 void cg_free_grammar(cg_grammar *g);
 
 /* Sizes of a compiled grammar. */
 int cg_grammar_info(const cg_grammar *g, cg_info *info);
+
+/* The grammar cache: live entries (held or idle), compiles answered from it,
+ * compiles that built new tables.  cg_cache_clear releases every idle entry. */
+int cg_cache_stats(int32_t *entries, int64_t *hits, int64_t *misses);
+int cg_cache_clear(void);
 
 /* Set d_states[0..batch) to the start of the grammar (flags cleared). */
 int cg_init_state(const cg_grammar *g, cg_state *d_states, int32_t batch, void *stream);

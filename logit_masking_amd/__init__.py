@@ -23,7 +23,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 # Symbols the C ABI (include/cg.h) exports.
 EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
            "cg_fill_bitmask", "cg_sample_advance", "cg_force_bytes", "cg_eval_calc", "cg_draft_workspace_bytes",
-           "cg_fill_draft", "cg_contract_model_spec", "cg_contract_reverse",
+           "cg_fill_draft", "cg_contract_model_spec", "cg_contract_reverse", "cg_cache_stats", "cg_cache_clear",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
 
 
@@ -73,6 +73,10 @@ def lib():
                                              ctypes.POINTER(ctypes.c_int32)]
         L.cg_contract_reverse.argtypes = [ctypes.c_char_p, sz, vp, sz, vp, sz, ctypes.POINTER(sz)]
         L.cg_draft_workspace_bytes.argtypes = [vp, i32, i32]
+        L.cg_cache_stats.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.cg_cache_stats.restype = ctypes.c_int
+        L.cg_cache_clear.argtypes = []
+        L.cg_cache_clear.restype = ctypes.c_int
         L.cg_draft_workspace_bytes.restype = sz
         L.cg_fill_draft.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]
         L.cg_eval_calc.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_int64)]
@@ -285,6 +289,17 @@ def eval_calc(span: bytes):
     if rc != CG_OK:
         return rc, lib().cg_last_error().decode(errors="replace")
     return CG_OK, v.value
+
+
+def cache_stats():
+    """(entries, hits, misses) of the library's grammar cache."""
+    e, h, m = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().cg_cache_stats(ctypes.byref(e), ctypes.byref(h), ctypes.byref(m)))
+    return e.value, h.value, m.value
+
+
+def cache_clear():
+    _check(lib().cg_cache_clear())
 
 
 def _sized_call(fn, *args):

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <functional>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -461,11 +462,58 @@ int build_state_masks(cg_grammar *g, const FillHost &f) {
     return CG_OK;
 }
 
-extern "C" {
+// Compiled grammars are shared by (spec text, vocabulary, options, device):
+// an identical compile returns the same read-only handle with one more
+// reference ("Evaluator aware decoding", "A concrete prototype on
+// llama.cpp": cross-grammar caching keeps repeated grammars from blowing up
+// compilation).  Up to kCacheIdle handles no one holds any more are kept
+// for later identical compiles (least recently released first out).
+namespace {
+constexpr size_t kCacheIdle = 8;
 
-int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *tok_bytes, const uint32_t *tok_offsets,
-                       int32_t vocab_size, const cg_options *opts, cg_grammar **out) {
-    if (!out) return arg_error("out is NULL");
+struct CacheEntry {
+    std::string spec;
+    uint64_t h1, h2;  // two independent hashes of the vocabulary
+    int32_t V;
+    uint32_t gen_cap, flags;
+    int device;
+    cg_grammar *g;
+    uint64_t idle_since;  // 0 while referenced
+};
+
+std::mutex g_cache_mu;
+std::vector<CacheEntry> g_cache;
+uint64_t g_clock = 0;
+int64_t g_hits = 0, g_misses = 0;
+
+void vocab_hash(const uint8_t *bytes, const uint32_t *off, int32_t V, uint64_t &h1, uint64_t &h2) {
+    h1 = 0xcbf29ce484222325ull;  // FNV-1a, then a second FNV-style pass with another basis and prime
+    h2 = 0x84222325cbf29ce4ull;
+    auto mix = [&](uint8_t b) {
+        h1 = (h1 ^ b) * 0x100000001b3ull;
+        h2 = (h2 ^ b) * 0x00000100000001b3ull + 0x9e3779b97f4a7c15ull;
+    };
+    for (int32_t t = 0; t <= V; t++)
+        for (int k = 0; k < 4; k++) mix((uint8_t)(off[t] >> (8 * k)));
+    for (uint32_t i = 0; i < off[V]; i++) mix(bytes[i]);
+}
+
+void evict_idle() {
+    size_t idle = 0;
+    for (auto &e : g_cache) idle += e.g->refs == 0;
+    while (idle > kCacheIdle) {
+        size_t oldest = g_cache.size();
+        for (size_t i = 0; i < g_cache.size(); i++)
+            if (g_cache[i].g->refs == 0 && (oldest == g_cache.size() || g_cache[i].idle_since < g_cache[oldest].idle_since))
+                oldest = i;
+        release(g_cache[oldest].g);
+        g_cache.erase(g_cache.begin() + oldest);
+        idle--;
+    }
+}
+
+int compile_uncached(const char *spec_json, size_t spec_len, const uint8_t *tok_bytes, const uint32_t *tok_offsets,
+                     int32_t vocab_size, const cg_options *opts, cg_grammar **out) {
     *out = nullptr;
     if (!spec_json) return arg_error("spec_json is NULL");
     if (vocab_size < 1 || !tok_offsets) return arg_error("vocabulary is empty");
@@ -568,7 +616,79 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
     return CG_OK;
 }
 
-void cg_free_grammar(cg_grammar *g) { release(g); }
+}  // namespace
+
+extern "C" {
+
+int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *tok_bytes, const uint32_t *tok_offsets,
+                       int32_t vocab_size, const cg_options *opts, cg_grammar **out) {
+    if (!out) return arg_error("out is NULL");
+    *out = nullptr;
+    if (!spec_json) return arg_error("spec_json is NULL");
+    if (vocab_size < 1 || !tok_offsets) return arg_error("vocabulary is empty");
+    if (tok_offsets[vocab_size] > 0 && !tok_bytes) return arg_error("tok_bytes is NULL");
+    const uint32_t gen_cap = (opts && opts->gen_cap) ? opts->gen_cap : 2048u;
+    const uint32_t flags = opts ? opts->flags : 0u;
+    int device = -1;
+    if (!(flags & CG_HOST_ONLY) && hipGetDevice(&device) != hipSuccess) device = -2;
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    // offsets are checked by the compile below before the hash reads the bytes
+    bool offsets_ok = tok_offsets[0] == 0;
+    for (int32_t t = 0; offsets_ok && t < vocab_size; t++) offsets_ok = tok_offsets[t + 1] >= tok_offsets[t];
+    uint64_t h1 = 0, h2 = 0;
+    if (offsets_ok) {
+        vocab_hash(tok_bytes, tok_offsets, vocab_size, h1, h2);
+        const std::string spec(spec_json, spec_len);
+        for (auto &e : g_cache)
+            if (e.V == vocab_size && e.h1 == h1 && e.h2 == h2 && e.gen_cap == gen_cap && e.flags == flags &&
+                e.device == device && e.spec == spec) {
+                e.g->refs++;
+                e.idle_since = 0;
+                g_hits++;
+                *out = e.g;
+                return CG_OK;
+            }
+    }
+    g_misses++;
+    const int rc = compile_uncached(spec_json, spec_len, tok_bytes, tok_offsets, vocab_size, opts, out);
+    if (rc != CG_OK) return rc;
+    g_cache.push_back(CacheEntry{std::string(spec_json, spec_len), h1, h2, vocab_size, gen_cap, flags, device, *out, 0});
+    return CG_OK;
+}
+
+void cg_free_grammar(cg_grammar *g) {
+    if (!g) return;
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    if (--g->refs > 0) return;
+    for (auto &e : g_cache)
+        if (e.g == g) {
+            e.idle_since = ++g_clock;  // kept for a later identical compile
+            evict_idle();
+            return;
+        }
+    release(g);
+}
+
+int cg_cache_stats(int32_t *entries, int64_t *hits, int64_t *misses) {
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    if (entries) *entries = (int32_t)g_cache.size();
+    if (hits) *hits = g_hits;
+    if (misses) *misses = g_misses;
+    return CG_OK;
+}
+
+int cg_cache_clear(void) {
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    for (size_t i = 0; i < g_cache.size();) {
+        if (g_cache[i].g->refs == 0) {
+            release(g_cache[i].g);
+            g_cache.erase(g_cache.begin() + i);
+        } else {
+            i++;
+        }
+    }
+    return CG_OK;
+}
 
 int cg_grammar_info(const cg_grammar *g, cg_info *info) {
     if (!g || !info) return arg_error("NULL argument");

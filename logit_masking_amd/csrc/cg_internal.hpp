@@ -287,6 +287,7 @@ struct cg_grammar {
     uint64_t *host_comb = nullptr;
     std::vector<uint32_t> host_forced;  // bit q: state q is inside an engine-written region
     bool has_forced = false;
+    int refs = 1;                   // handles given out by cg_compile_grammar (the cache shares them)
     std::vector<uint32_t> plain_q;  // live states outside strings (candidates of the state-mask table)
     int32_t n_smask = 0;            // rows of dev.state_mask
     int32_t c_tiles = 0;            // tiles of the closing-token list

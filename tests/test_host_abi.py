@@ -1,5 +1,6 @@
 """CPU tests of the C ABI library: exports, decoupling, the host compiler and
 its table walker (cg_try_input) against the oracle.  No device calls."""
+import json
 import os
 import re
 import subprocess
@@ -204,3 +205,44 @@ def test_generation_strings_host():
     _agree(og3, hg3, b'set_timer({"seconds":86400,"label":"' + b"x" * 41)
     _agree(og3, hg3, b'read_document({"path":"a"})')
     _agree(og3, hg3, b'read_document({"path":"a","max_pages":0')
+
+
+def test_grammar_cache():
+    """Identical compiles share one handle; any difference in spec text,
+    vocabulary or options builds a new one; idle handles stay cached up to a
+    bound and cache_clear releases them."""
+    import gc
+    import logit_masking_amd as cg
+    cg.cache_clear()
+    e0, h0, m0 = cg.cache_stats()
+    blob, off = W.make_vocab(2, 4096)
+    spec = W.spec_json(2)
+    a = cg.Grammar(spec, blob, off, host_only=True)
+    b = cg.Grammar(spec, blob, off, host_only=True)
+    assert a._h.value == b._h.value
+    e, h, m = cg.cache_stats()
+    assert (h - h0, m - m0) == (1, 1)
+    c = cg.Grammar(spec, blob, off, gen_cap=100, host_only=True)      # options differ
+    blob2 = bytes(blob[:-1]) + bytes([blob[-1] ^ 1])                 # one byte of the vocabulary differs
+    d = cg.Grammar(spec, blob2, off, host_only=True)
+    f = cg.Grammar(spec + b" ", blob, off, host_only=True)            # spec text differs
+    assert len({a._h.value, c._h.value, d._h.value, f._h.value}) == 4
+    assert a.try_input(b'{"eligibility"')[0] == 14
+    del a
+    gc.collect()
+    assert b.try_input(b'{"eligibility"')[0] == 14                  # still held by b
+    del b, c, d, f
+    gc.collect()
+    e, h, m = cg.cache_stats()
+    assert e == e0 + 4                                               # all idle, all kept
+    g2 = cg.Grammar(spec, blob, off, host_only=True)                 # answered from the cache
+    assert cg.cache_stats()[1] == h + 1
+    del g2
+    gc.collect()
+    # more idle grammars than the cache keeps: the oldest go
+    keep = [cg.Grammar(json.dumps({"kind": "calc", "int_max": 10 + i}), blob, off, host_only=True) for i in range(12)]
+    del keep
+    gc.collect()
+    assert cg.cache_stats()[0] <= e0 + 8
+    cg.cache_clear()
+    assert cg.cache_stats()[0] == e0
