@@ -17,6 +17,7 @@
  *   cg_fill_draft        masks along each row's k-token draft (device)
  *   cg_force_bytes       engine-written bytes (an evaluated result) (device)
  *   cg_eval_calc         evaluate a calc span (host)
+ *   cg_eval_strop        evaluate a string-operation span (host)
  *   cg_contract_model_spec  integer-string contract: the model-facing spec (host)
  *   cg_contract_reverse  the exact inverse, then validation (host)
  *   cg_try_input         where a candidate string is refused (host)
@@ -128,6 +129,14 @@ typedef struct {
  *       the engine (cg_force_bytes), never sampled: rows inside it have an
  *       empty mask ("Evaluator aware decoding", "A concrete prototype on
  *       llama.cpp");
+ *       With "evaluators":["calc","strop"] (default ["calc"]) the text may
+ *       also hold string-operation spans, "<strop>" NAME "(" ARGS ")"
+ *       "</strop>" (see cg_eval_strop; string arguments are '"' printable
+ *       ASCII other than '"', '\\' and '<' '"', integers "-"? 1-6 digits,
+ *       W "," W between arguments), followed by "<result>" TEXT'
+ *       "</result>" (TEXT': printable ASCII other than '<') or the error
+ *       block ("Evaluator aware decoding", "Not just arithmetic: string
+ *       operations");
  *   {"kind":"json_schema", "schema":{...}, settings...}
  *       a JSON value of the schema ("Guided Decoding & Structured-Output
  *       Reliability", "Design 1 -- base schema, validators-first ordering");
@@ -353,6 +362,20 @@ int cg_contract_model_spec(const char *ext_spec, size_t len, char *out, size_t c
                            int32_t *n_fields);
 int cg_contract_reverse(const char *ext_spec, size_t len, const uint8_t *text, size_t text_len, char *out,
                         size_t cap, size_t *out_len);
+
+/*
+ * Host-side evaluator of a string-operation span ("Evaluator aware
+ * decoding", "Not just arithmetic: string operations"):
+ * "<strop>" NAME "(" ARGS ")" "</strop>" as the calc_text grammar with the
+ * "strop" evaluator spells it.  count(s, t): non-overlapping occurrences of
+ * t in s, left to right (an empty t occurs len + 1 times); len(s);
+ * reverse(s); upper(s): ASCII letters upper-cased; substr(s, i, j): the
+ * characters from i up to j, negative positions counted from the end, both
+ * clamped to the string.  Writes the result text (count and len as decimal
+ * text) with a terminating zero to out[cap]; *out_len = its length.
+ * CG_E_PARSE for a malformed span, CG_E_LIMIT when cap is too small.
+ */
+int cg_eval_strop(const uint8_t *span, size_t len, char *out, size_t cap, size_t *out_len);
 
 /*
  * Host-side diagnostic: run `bytes` against the automaton from its start.

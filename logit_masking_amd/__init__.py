@@ -24,6 +24,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
            "cg_fill_bitmask", "cg_sample_advance", "cg_force_bytes", "cg_eval_calc", "cg_draft_workspace_bytes",
            "cg_fill_draft", "cg_contract_model_spec", "cg_contract_reverse", "cg_cache_stats", "cg_cache_clear",
+           "cg_eval_strop",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
 
 
@@ -73,6 +74,8 @@ def lib():
                                              ctypes.POINTER(ctypes.c_int32)]
         L.cg_contract_reverse.argtypes = [ctypes.c_char_p, sz, vp, sz, vp, sz, ctypes.POINTER(sz)]
         L.cg_draft_workspace_bytes.argtypes = [vp, i32, i32]
+        L.cg_eval_strop.argtypes = [vp, sz, vp, sz, ctypes.POINTER(sz)]
+        L.cg_eval_strop.restype = ctypes.c_int
         L.cg_cache_stats.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.cg_cache_stats.restype = ctypes.c_int
         L.cg_cache_clear.argtypes = []
@@ -289,6 +292,17 @@ def eval_calc(span: bytes):
     if rc != CG_OK:
         return rc, lib().cg_last_error().decode(errors="replace")
     return CG_OK, v.value
+
+
+def eval_strop(span: bytes):
+    """cg_eval_strop: (CG_OK, result bytes) or (error code, message)."""
+    if isinstance(span, str):
+        span = span.encode()
+    buf = ctypes.create_string_buffer(span, len(span)) if span else None
+    rc, out = _sized_call(lambda b, c, n: lib().cg_eval_strop(buf, len(span), b, c, n))
+    if rc != CG_OK:
+        return rc, lib().cg_last_error().decode(errors="replace")
+    return CG_OK, out
 
 
 def cache_stats():

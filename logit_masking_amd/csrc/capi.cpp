@@ -880,6 +880,98 @@ int cg_eval_calc(const uint8_t *span, size_t len, int64_t *value) {
     }
 }
 
+int cg_eval_strop(const uint8_t *span, size_t len, char *out, size_t cap, size_t *out_len) {
+    if (!out_len || (len && !span) || (cap && !out)) return arg_error("NULL argument");
+    const std::string s((const char *)span, len);
+    static const char *const kNames[5] = {"count", "len", "reverse", "upper", "substr"};
+    static const char *const kArgs[5] = {"SS", "S", "S", "S", "SII"};
+    auto fail = [&](const char *m) {
+        set_error("strop span: %s", m);
+        return CG_E_PARSE;
+    };
+    const std::string open = "<strop>", close = ")</strop>";
+    if (s.size() < open.size() + close.size() || s.compare(0, open.size(), open) != 0 ||
+        s.compare(s.size() - close.size(), close.size(), close) != 0)
+        return fail("not a <strop> span");
+    size_t i = open.size();
+    const size_t end = s.size() - close.size();
+    int op = -1;
+    for (int k = 0; k < 5; k++) {
+        const size_t n = strlen(kNames[k]);
+        if (s.compare(i, n, kNames[k]) == 0 && i + n < end + 1 && s[i + n] == '(') {
+            op = k;
+            i += n + 1;
+            break;
+        }
+    }
+    if (op < 0) return fail("unknown operation");
+    std::string str[2];
+    long long num[2] = {0, 0};
+    int ns = 0, ni = 0;
+    auto skip = [&]() {
+        while (i < end && (s[i] == ' ' || s[i] == '\t' || s[i] == '\n' || s[i] == '\r')) i++;
+    };
+    for (const char *a = kArgs[op]; *a; a++) {
+        skip();
+        if (a != kArgs[op]) {
+            if (i >= end || s[i] != ',') return fail("expected ','");
+            i++;
+            skip();
+        }
+        if (*a == 'S') {
+            if (i >= end || s[i] != '"') return fail("expected a string");
+            const size_t q = s.find('"', i + 1);
+            if (q == std::string::npos || q >= end) return fail("unterminated string");
+            str[ns++] = s.substr(i + 1, q - i - 1);
+            i = q + 1;
+        } else {
+            bool neg = false;
+            if (i < end && s[i] == '-') neg = true, i++;
+            size_t d = 0;
+            long long v = 0;
+            while (i < end && s[i] >= '0' && s[i] <= '9' && d < 18) v = v * 10 + (s[i++] - '0'), d++;
+            if (d == 0) return fail("expected an integer");
+            num[ni++] = neg ? -v : v;
+        }
+    }
+    skip();
+    if (i != end) return fail("trailing input");
+    std::string r;
+    const std::string &a0 = str[0];
+    switch (op) {
+    case 0: {  // non-overlapping occurrences, left to right; "" occurs len + 1 times
+        long long n = 0;
+        if (str[1].empty()) n = (long long)a0.size() + 1;
+        else
+            for (size_t p = a0.find(str[1]); p != std::string::npos; p = a0.find(str[1], p + str[1].size())) n++;
+        r = std::to_string(n);
+        break;
+    }
+    case 1: r = std::to_string(a0.size()); break;
+    case 2: r.assign(a0.rbegin(), a0.rend()); break;
+    case 3:
+        r = a0;
+        for (char &c : r)
+            if (c >= 'a' && c <= 'z') c = (char)(c - 32);
+        break;
+    default: {  // positions from the end when negative, clamped to the string
+        const long long n = (long long)a0.size();
+        auto norm = [&](long long x) { return std::min(std::max(x < 0 ? x + n : x, 0LL), n); };
+        const long long b = norm(num[0]), e = norm(num[1]);
+        if (b < e) r = a0.substr((size_t)b, (size_t)(e - b));
+        break;
+    }
+    }
+    *out_len = r.size();
+    if (r.size() + 1 > cap) {
+        set_error("output needs %zu bytes (with the terminating zero)", r.size() + 1);
+        return CG_E_LIMIT;
+    }
+    memcpy(out, r.data(), r.size());
+    out[r.size()] = 0;
+    return CG_OK;
+}
+
 int cg_try_input(const cg_grammar *g, const uint8_t *bytes, size_t len, size_t *refused_at, int *complete) {
     if (!g || !refused_at || !complete || (len && !bytes)) return arg_error("NULL argument");
     Walker w;

@@ -101,6 +101,7 @@ struct Settings {
     int64_t open_cap = 256;  // -1 uncapped
     int open_int_digits = 20;
     int64_t calc_min = 0, calc_max = 999;
+    bool calc = true, strop = false;  // evaluators whose spans a text may hold
 };
 
 bool is_annotation(const std::string &k) {
@@ -836,37 +837,108 @@ struct Builder {
         calc_span(start, accept);
     }
 
-    // Text with evaluated spans: TEXT* ("<calc>" W E W "</calc>" RESULT
-    // TEXT*)* "<end>", TEXT = LF or printable ASCII other than '<'.  RESULT is
-    // written by the engine, never sampled, so its states are marked forced:
-    // "<result>" "-"? digit{1,20} "</result>" for a value, or
-    // "<result_error>" MSG "</result_error>" for a failed evaluation, MSG =
-    // printable ASCII other than '<'.
+    // A string-operation span ("Evaluator aware decoding", "Not just
+    // arithmetic: string operations"): "<strop>" NAME "(" W ARGS W ")"
+    // "</strop>" with NAME(ARGS) one of count(S, S), len(S), reverse(S),
+    // upper(S), substr(S, I, I); arguments separated by W "," W; S = '"'
+    // (printable ASCII other than '"', '\\' and '<')* '"'; I = "-"? digit{1,6}.
+    void strop_span(int from, int to) {
+        const int NS = add();
+        trie(from, {"<strop>"}, NS);
+        const int T = add();
+        trie(T, {"</strop>"}, to);
+        auto str_arg = [&](int s) {
+            const int Bd = add(), E = add();
+            edge(s, '"', '"', OP_NONE, 0, Bd);
+            edge(Bd, 0x20, 0x21, OP_NONE, 0, Bd);
+            edge(Bd, 0x23, 0x3B, OP_NONE, 0, Bd);
+            edge(Bd, 0x3D, 0x5B, OP_NONE, 0, Bd);
+            edge(Bd, 0x5D, 0x7E, OP_NONE, 0, Bd);
+            edge(Bd, '"', '"', OP_NONE, 0, E);
+            return E;
+        };
+        const struct {
+            const char *name;
+            const char *args;  // S: string, I: integer
+        } ops[] = {{"count(", "SS"}, {"len(", "S"}, {"reverse(", "S"}, {"upper(", "S"}, {"substr(", "SII"}};
+        for (const auto &op : ops) {
+            int q = add();
+            trie(NS, {op.name}, q);
+            ws_loop(q);
+            const int n = (int)strlen(op.args);
+            for (int i = 0; i < n; i++) {
+                const bool last = i + 1 == n;
+                // what follows an argument: whitespace, then ',' and the next argument, or ')'
+                const int J = add(), N = last ? -1 : add();
+                ws_loop(J);
+                if (last) edge(J, ')', ')', OP_NONE, 0, T);
+                else edge(J, ',', ',', OP_NONE, 0, N);
+                if (op.args[i] == 'S') {
+                    copy_from(str_arg(q), J);
+                } else {
+                    const int M = add();
+                    int D[7];
+                    for (int k = 1; k <= 6; k++) D[k] = add();
+                    edge(q, '-', '-', OP_NONE, 0, M);
+                    edge(q, '0', '9', OP_NONE, 0, D[1]);
+                    edge(M, '0', '9', OP_NONE, 0, D[1]);
+                    for (int k = 1; k < 6; k++) edge(D[k], '0', '9', OP_NONE, 0, D[k + 1]);
+                    for (int k = 1; k <= 6; k++) copy_from(D[k], J);
+                }
+                if (!last) {
+                    ws_loop(N);
+                    q = N;
+                }
+            }
+        }
+    }
+
+    // Text with evaluated spans: TEXT* (SPAN RESULT TEXT*)* "<end>", TEXT = LF
+    // or printable ASCII other than '<', SPAN a calc span and/or a string
+    // operation (the evaluators the spec names).  RESULT is written by the
+    // engine, never sampled, so its states are marked forced: after a calc
+    // span "<result>" "-"? digit{1,20} "</result>", after a string operation
+    // "<result>" TEXT' "</result>" (TEXT' = printable ASCII other than '<'),
+    // or after either "<result_error>" MSG "</result_error>" for a failed
+    // evaluation, MSG = printable ASCII other than '<'.
     void calc_text() {
         const int TX = start = add();
         edge(TX, '\n', '\n', OP_NONE, 0, TX);
         edge(TX, 0x20, '<' - 1, OP_NONE, 0, TX);
         edge(TX, '<' + 1, 0x7E, OP_NONE, 0, TX);
-        const int R0 = add();
-        calc_span(TX, R0);
+        const int R0 = S.calc ? add() : -1, R1 = S.strop ? add() : -1;
+        if (S.calc) calc_span(TX, R0);
+        if (S.strop) strop_span(TX, R1);
         trie(TX, {"<end>"}, accept);
         const int first_forced = (int)st.size();
-        const int RV = add(), RN = add(), RM = add();
-        int RD[21];
-        for (int d = 1; d <= 20; d++) RD[d] = add();
-        trie(R0, {"<result>"}, RV);
-        trie(R0, {"<result_error>"}, RM);
-        edge(RV, '-', '-', OP_NONE, 0, RN);
-        edge(RV, '0', '9', OP_NONE, 0, RD[1]);
-        edge(RN, '0', '9', OP_NONE, 0, RD[1]);
-        for (int d = 1; d <= 20; d++) {
-            if (d < 20) edge(RD[d], '0', '9', OP_NONE, 0, RD[d + 1]);
-            trie(RD[d], {"</result>"}, TX);
-        }
+        const int RM = add();
         edge(RM, 0x20, '<' - 1, OP_NONE, 0, RM);
         edge(RM, '<' + 1, 0x7E, OP_NONE, 0, RM);
         trie(RM, {"</result_error>"}, TX);
-        st[R0].forced = true;
+        if (S.calc) {
+            const int RV = add(), RN = add();
+            int RD[21];
+            for (int d = 1; d <= 20; d++) RD[d] = add();
+            trie(R0, {"<result>"}, RV);
+            trie(R0, {"<result_error>"}, RM);
+            edge(RV, '-', '-', OP_NONE, 0, RN);
+            edge(RV, '0', '9', OP_NONE, 0, RD[1]);
+            edge(RN, '0', '9', OP_NONE, 0, RD[1]);
+            for (int d = 1; d <= 20; d++) {
+                if (d < 20) edge(RD[d], '0', '9', OP_NONE, 0, RD[d + 1]);
+                trie(RD[d], {"</result>"}, TX);
+            }
+            st[R0].forced = true;
+        }
+        if (S.strop) {
+            const int RT = add();
+            trie(R1, {"<result>"}, RT);
+            trie(R1, {"<result_error>"}, RM);
+            edge(RT, 0x20, '<' - 1, OP_NONE, 0, RT);
+            edge(RT, '<' + 1, 0x7E, OP_NONE, 0, RT);
+            trie(RT, {"</result>"}, TX);
+            st[R1].forced = true;
+        }
         for (int q = first_forced; q < (int)st.size(); q++) st[q].forced = true;
     }
 };
@@ -1038,6 +1110,16 @@ int compile_spec(const char *spec, size_t len, cg_grammar *g) {
             S.calc_min = setting(root, "int_min", 0, 0, 1000000000, false);
             S.calc_max = setting(root, "int_max", 999, 0, 1000000000, false);
             if (S.calc_min > S.calc_max) refuse("$", "empty integer range");
+            if (const Json *ev = root.get("evaluators")) {
+                if (k != "calc_text" || ev->t != Json::ARR || ev->a.empty())
+                    refuse("$.evaluators", "evaluators must be a non-empty list (calc_text only)");
+                S.calc = S.strop = false;
+                for (auto &e : ev->a) {
+                    if (e.t == Json::STR && e.s == "calc") S.calc = true;
+                    else if (e.t == Json::STR && e.s == "strop") S.strop = true;
+                    else refuse("$.evaluators", "evaluators are \"calc\" and \"strop\"");
+                }
+            }
         } else if (k == "json_schema") {
             json_root = R.schema(root.get("schema"), "$.schema");
             if (R.nodes[json_root].first & FC_NUM)

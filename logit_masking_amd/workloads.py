@@ -21,7 +21,8 @@ The workloads restate the pages' settings:
   * a recursive-JSON stress grammar capped at 2048 tokens.
   * text with evaluated calc spans ("Evaluator aware decoding", "A concrete
     prototype on llama.cpp"): the model writes prose and <calc> spans, the
-    engine writes <result> / <result_error> blocks.
+    engine writes <result> / <result_error> blocks; and the same with
+    string-operation spans too ("Not just arithmetic: string operations").
 
 Random numbers come from splitmix64 written in plain Python so that every
 vocabulary is byte-identical across numpy versions.
@@ -180,6 +181,8 @@ SPECS = {
     5: {"kind": "json_schema", "ws_max": 4, "open_string_cap": None, "depth_cap": 32,
         "schema": {"anyOf": [{"type": "object"}, {"type": "array"}]}},
     6: {"kind": "calc_text", "int_min": 0, "int_max": 999, "ws_max": 2, "depth_cap": 16},
+    7: {"kind": "calc_text", "evaluators": ["calc", "strop"], "int_min": 0, "int_max": 999, "ws_max": 2,
+        "depth_cap": 16},
 }
 
 
@@ -204,6 +207,8 @@ CONFIGS = {
             T=1.0, steps=2048, maxlen=32, mean=7.0, seed=0xC0F5),
     6: dict(name="calc-text", B=256, V=128256, dtype="bf16", logits="normal", sigma=3.0,
             T=0.7, steps=256, maxlen=16, mean=5.0, seed=0xC0F6),
+    7: dict(name="eval-text", B=256, V=128256, dtype="bf16", logits="normal", sigma=3.0,
+            T=0.7, steps=256, maxlen=16, mean=5.0, seed=0xC0F7),
 }
 
 GEN_CAP = 2048  # engine cap on one constrained generation, in tokens
@@ -247,6 +252,8 @@ _TEXT_FRAGS = ["<calc>", "</calc>", "<result>", "</result>", "<result_error>", "
                "<", ">", "</", "calc", "result", " + ", " - ", " * ", " / ", "+", "-", "*", "/", "(", ")",
                " (", ") ", " = ", "=", " is", " the", " answer", " total", ".", ",", "\n", " "]
 
+_STROP_FRAGS = ["<strop>", "</strop>", "count(", "len(", "reverse(", "upper(", "substr(", '"', '", "', '")',
+                '", ', ", ", ")</strop>", "(", ")", "strawberry", "r", "hello", "abc"]
 _CALC_BYTES = b"0123456789+-*/() "
 _TEXT_PUNCT = b".,;:!?'\"\n\t <>"
 _LETTERS = b"abcdefghijklmnopqrstuvwxyz"
@@ -259,13 +266,14 @@ def _utf8_piece(rng: SplitMix) -> bytes:
     return chr(lo + rng.below(hi - lo + 1)).encode("utf-8")
 
 
-def _gen_text_token(rng: SplitMix, L: int) -> bytes:
-    """One candidate token of exactly L bytes for text with calc spans."""
+def _gen_text_token(rng: SplitMix, L: int, strop: bool = False) -> bytes:
+    """One candidate token of exactly L bytes for text with evaluated spans."""
     u = rng.uniform()
     out = bytearray()
     if u < 0.30:  # tags, operators and glue
+        frags = _TEXT_FRAGS + _STROP_FRAGS if strop else _TEXT_FRAGS
         while len(out) < L:
-            piece = rng.choice(_TEXT_FRAGS).encode()
+            piece = rng.choice(frags).encode()
             if not out and len(piece) > 1 and rng.uniform() < 0.4:
                 piece = piece[rng.below(len(piece)):]
             out += piece
@@ -346,9 +354,9 @@ def make_vocab(cfg: int, V: int | None = None):
             L = 2 + rng.below(5)
             t = bytes((_CALC_ALPHA[rng.below(len(_CALC_ALPHA))] if rng.uniform() < 0.8
                        else _PRINTABLE[rng.below(len(_PRINTABLE))]) for _ in range(L))
-        elif cfg == 6:
+        elif cfg in (6, 7):
             L = min(c["maxlen"], 2 + rng.poisson(c["mean"] - 2.0))
-            t = _gen_text_token(rng, L)
+            t = _gen_text_token(rng, L, strop=cfg == 7)
         else:
             L = min(c["maxlen"], 2 + rng.poisson(c["mean"] - 2.0))
             t = _gen_token(rng, cfg, L)
@@ -438,9 +446,35 @@ def calc_expr(rng: SplitMix, spec, depth: int = 0, budget: int = 6) -> bytes:
     return expr(depth, budget)
 
 
+_STROP_WORDS = ["strawberry", "r", "hello world", "abc", "", "banana", "an", "racecar", "Mixed Case 12"]
+
+
+def strop_call(rng: SplitMix, spec) -> bytes:
+    """A random string-operation span body: NAME(ARGS) with whitespace runs
+    within ws_max after the commas."""
+    wsm = spec.get("ws_max", 4)
+
+    def ws():
+        return b" " * rng.below(wsm + 1) if wsm else b""
+
+    def s():
+        return b'"' + rng.choice(_STROP_WORDS).encode() + b'"'
+
+    def i():
+        return str(rng.below(25) - 8).encode()
+
+    k = rng.below(5)
+    if k == 0:
+        return b"count(" + s() + b"," + ws() + s() + b")"
+    if k == 4:
+        return b"substr(" + s() + b"," + ws() + i() + b"," + ws() + i() + b")"
+    return (b"len(", b"reverse(", b"upper(")[k - 1] + s() + b")"
+
+
 def calc_text_script(rng: SplitMix, spec, n_spans: int) -> list:
-    """Model segments of one row: prose, then "<calc>" EXPR "</calc>", n_spans
-    times, then prose and "<end>"."""
+    """Model segments of one row: prose, then a closed span ("<calc>" EXPR
+    "</calc>", or "<strop>" CALL "</strop>" when the spec has that
+    evaluator), n_spans times, then prose and "<end>"."""
     def prose():
         words = [rng.choice(_PROSE_WORDS) for _ in range(rng.below(6))]
         text = b" ".join(words)
@@ -449,7 +483,11 @@ def calc_text_script(rng: SplitMix, spec, n_spans: int) -> list:
         return text + (b" " if text else b"")
 
     segs = []
+    strop = "strop" in spec.get("evaluators", ["calc"])
     for _ in range(n_spans):
+        if strop and rng.uniform() < 0.5:
+            segs.append(prose() + b"<strop>" + strop_call(rng, spec) + b"</strop>")
+            continue
         w = spec.get("ws_max", 4)
         lead = b" " * rng.below(w + 1) if w else b""
         tail = b" " * rng.below(w + 1) if w else b""

@@ -32,6 +32,7 @@ import ctypes
 import json
 import math
 import os
+import re
 import subprocess
 import threading
 from fractions import Fraction
@@ -76,7 +77,7 @@ class OG(ctypes.Structure):
                 ("open_cap", ctypes.c_int32), ("calc_min", ctypes.c_int32), ("calc_max", ctypes.c_int32),
                 ("open_obj", ctypes.c_int32), ("open_arr", ctypes.c_int32),
                 ("nodes", ctypes.POINTER(ONode)), ("props", ctypes.POINTER(OProp)),
-                ("pool", ctypes.POINTER(ctypes.c_uint8))]
+                ("pool", ctypes.POINTER(ctypes.c_uint8)), ("evaluators", ctypes.c_int32)]
 
 
 def lib():
@@ -338,8 +339,15 @@ class Grammar:
         og = OG()
         og.ws_max, og.depth_cap, og.open_cap = s["ws_max"], s["depth_cap"], s["open_cap"]
         og.root, og.tools_first, og.tools_count = -1, 0, 0
+        og.evaluators = 1
         if kind in ("calc", "calc_text"):
             og.gkind = G_CALC if kind == "calc" else G_TEXT
+            if "evaluators" in spec:
+                ev = spec["evaluators"]
+                if kind != "calc_text" or not isinstance(ev, list) or not ev or \
+                        not all(e in ("calc", "strop") for e in ev):
+                    raise Unsupported("$.evaluators", "evaluators are 'calc' and 'strop' (calc_text only)")
+                og.evaluators = (1 if "calc" in ev else 0) | (2 if "strop" in ev else 0)
             og.calc_min = _setting(spec, "int_min", 0, 10**9)
             og.calc_max = _setting(spec, "int_max", 0, 10**9)
             if og.calc_min > og.calc_max:
@@ -878,3 +886,70 @@ def contract_reverse(spec: dict, text: bytes):
         return False, None, str(e)
     k, complete = Grammar(spec).try_input(out)
     return complete, out, "" if complete else f"refused at byte {k}"
+
+
+# ---------------------------------------------------------------------------
+# String operations (page "Evaluator aware decoding", section "Not just
+# arithmetic: string operations"): a small registry of pure functions over
+# the span's arguments.  count = non-overlapping occurrences scanning left to
+# right (an empty pattern occurs len + 1 times), len = characters, reverse,
+# upper = ASCII letters upper-cased, substr(s, i, j) = the characters from i
+# up to j, negative positions counting from the end, clamped to the string.
+# Integer results are written as decimal text, string results as they are.
+# ---------------------------------------------------------------------------
+def _count(s, t):
+    if not t:
+        return len(s) + 1
+    n = i = 0
+    while True:
+        k = s.find(t, i)
+        if k < 0:
+            return n
+        n += 1
+        i = k + len(t)
+
+
+def _slice(s, i, j):
+    n = len(s)
+
+    def norm(x):
+        x = x + n if x < 0 else x
+        return min(max(x, 0), n)
+
+    a, b = norm(i), norm(j)
+    return s[a:b] if a < b else ""
+
+
+def eval_strop(span: bytes) -> bytes:
+    s = span.decode("ascii")
+    m = re.fullmatch(r'<strop>(count|len|reverse|upper|substr)\((.*)\)</strop>', s, re.S)
+    if not m:
+        raise CalcError("not a string-operation span")
+    name, rest = m.group(1), m.group(2)
+    args = []
+    i = 0
+    while i < len(rest):
+        ch = rest[i]
+        if ch in " \t\n\r,":
+            i += 1
+        elif ch == '"':
+            j = rest.index('"', i + 1)
+            args.append(rest[i + 1:j])
+            i = j + 1
+        else:
+            j = i + 1
+            while j < len(rest) and rest[j].isdigit():
+                j += 1
+            args.append(int(rest[i:j]))
+            i = j
+    if name == "count":
+        out = str(_count(args[0], args[1]))
+    elif name == "len":
+        out = str(len(args[0]))
+    elif name == "reverse":
+        out = args[0][::-1]
+    elif name == "upper":
+        out = "".join(chr(ord(c) - 32) if "a" <= c <= "z" else c for c in args[0])
+    else:
+        out = _slice(args[0], args[1], args[2])
+    return out.encode("ascii")

@@ -73,10 +73,11 @@ typedef struct {
     const onode *nodes;
     const oprop *props;
     const uint8_t *pool;
+    int32_t evaluators;      /* TEXT: 1 calc spans, 2 string-operation spans */
 } og;
 
 /* ---- configuration ---------------------------------------------------- */
-enum { F_ROOT = 1, F_OBJ, F_ARR, F_STR, F_INT, F_NUM, F_LIT, F_ENUM, F_CALC, F_TEXT };
+enum { F_ROOT = 1, F_OBJ, F_ARR, F_STR, F_INT, F_NUM, F_LIT, F_ENUM, F_CALC, F_TEXT, F_STROP };
 #define MAXF 48
 
 typedef struct {
@@ -640,6 +641,83 @@ static int step_calc(const og *g, ofr *f, int ch) {
     }
 }
 
+/* string-operation span (page "Evaluator aware decoding", "Not just
+ * arithmetic: string operations"): "<strop>" NAME "(" W ARGS W ")" "</strop>",
+ * NAME(ARGS) one of count(S, S), len(S), reverse(S), upper(S), substr(S, I, I),
+ * arguments separated by W "," W; S = '"' (printable ASCII but '"', '\\',
+ * '<')* '"'; I = "-"? digit{1,6}.  a = the operation, b = position in a
+ * literal or the argument index, aux = digits of an integer, cand = names
+ * still matching. */
+enum { S_TAG = 0, S_NAME, S_ARG, S_STR, S_INT, S_AFTER, S_CLOSE };
+static const char STROP_OPEN[] = "<strop>";
+static const char STROP_CLOSE[] = "</strop>";
+static const char *const STROP_NAMES[5] = {"count(", "len(", "reverse(", "upper(", "substr("};
+static const char *const STROP_ARGS[5] = {"SS", "S", "S", "S", "SII"};
+
+static int step_strop(const og *g, ofr *f, int ch) {
+    int w;
+    for (;;) {
+        switch (f->phase) {
+        case S_TAG:
+            if (ch != STROP_OPEN[f->b]) return R_DEAD;
+            if (++f->b == 7) { f->phase = S_NAME; f->b = 0; f->cand = 31; }
+            return R_OK;
+        case S_NAME: {
+            uint64_t nc = 0;
+            for (int i = 0; i < 5; i++)
+                if (((f->cand >> i) & 1) && STROP_NAMES[i][f->b] == ch) nc |= 1ull << i;
+            if (!nc) return R_DEAD;
+            f->cand = nc;
+            f->b++;
+            for (int i = 0; i < 5; i++)
+                if (((nc >> i) & 1) && STROP_NAMES[i][f->b] == 0) {
+                    f->a = i;
+                    f->phase = S_ARG;
+                    f->b = 0;
+                    f->ws = 0;
+                }
+            return R_OK;
+        }
+        case S_ARG:
+            if ((w = take_ws(g, f, ch))) return w > 0 ? R_OK : R_DEAD;
+            if (STROP_ARGS[f->a][f->b] == 'S') {
+                if (ch != '"') return R_DEAD;
+                f->phase = S_STR;
+                return R_OK;
+            }
+            if (ch != '-' && !is_digit(ch)) return R_DEAD;
+            f->phase = S_INT;
+            f->aux = is_digit(ch) ? 1 : 0;
+            return R_OK;
+        case S_STR:
+            if (ch == '"') { f->phase = S_AFTER; f->ws = 0; return R_OK; }
+            return (ch >= 0x20 && ch <= 0x7E && ch != '\\' && ch != '<') ? R_OK : R_DEAD;
+        case S_INT:
+            if (is_digit(ch)) {
+                if (f->aux >= 6) return R_DEAD;
+                f->aux++;
+                return R_OK;
+            }
+            if (f->aux == 0) return R_DEAD;
+            f->phase = S_AFTER;
+            f->ws = 0;
+            continue; /* the byte belongs to what follows the integer */
+        case S_AFTER: {
+            if ((w = take_ws(g, f, ch))) return w > 0 ? R_OK : R_DEAD;
+            const int last = STROP_ARGS[f->a][f->b + 1] == 0;
+            if (!last && ch == ',') { f->b++; f->phase = S_ARG; f->ws = 0; return R_OK; }
+            if (last && ch == ')') { f->phase = S_CLOSE; f->b = 0; return R_OK; }
+            return R_DEAD;
+        }
+        case S_CLOSE:
+            if (ch != STROP_CLOSE[f->b]) return R_DEAD;
+            return ++f->b == 8 ? R_DONE_TOOK : R_OK;
+        default:
+            return R_DEAD;
+        }
+    }
+}
+
 /* text with evaluated spans (page "Evaluator aware decoding", "A concrete
  * prototype on llama.cpp": the model writes a span, the engine evaluates it
  * and writes the result, or an error the model can recover from, back):
@@ -658,18 +736,27 @@ static const char ERR_CLOSE[] = "</result_error>";
 
 static int printable(int ch) { return ch >= 0x20 && ch <= 0x7E; }
 
-static int step_text(oconf *c, ofr *f, int ch) {
+static int step_text(const og *g, oconf *c, ofr *f, int ch) {
     switch (f->phase) {
     case X_TEXT:
         if (ch == '<') { f->phase = X_LT; return R_OK; }
         return (ch == '\n' || printable(ch)) ? R_OK : R_DEAD;
     case X_LT:
         if (ch == 'e') { f->phase = X_END; f->b = 2; return R_OK; }
-        if (ch == 'c') {
+        if (ch == 'c' && (g->evaluators & 1)) {
             ofr *k = push(c, F_CALC, -1);
             k->phase = C_OPEN;
             k->b = 2; /* "<c" matched */
             f->phase = X_CALC;
+            f->aux = 0;
+            return R_OK;
+        }
+        if (ch == 's' && (g->evaluators & 2)) {
+            ofr *k = push(c, F_STROP, -1);
+            k->phase = S_TAG;
+            k->b = 2; /* "<s" matched */
+            f->phase = X_CALC;
+            f->aux = 1;
             return R_OK;
         }
         return R_DEAD;
@@ -685,7 +772,7 @@ static int step_text(oconf *c, ofr *f, int ch) {
                 f->b++;
                 return R_OK;
             }
-            if (ch == '>') { f->a = 1; return R_OK; }
+            if (ch == '>') { f->a = f->aux ? 8 : 1; return R_OK; }
             if (ch == '_') { f->a = 5; f->b = 1; return R_OK; }
             return R_DEAD;
         case 1:
@@ -720,6 +807,9 @@ static int step_text(oconf *c, ofr *f, int ch) {
             if (ch != ERR_CLOSE[f->b]) return R_DEAD;
             if (++f->b == 15) f->phase = X_TEXT;
             return R_OK;
+        case 8: /* a string operation's result: text up to "</result>" */
+            if (ch == '<') { f->a = 4; f->b = 1; return R_OK; }
+            return printable(ch) ? R_OK : R_DEAD;
         }
         return R_DEAD;
     default:
@@ -899,7 +989,8 @@ static int step_frame(const og *g, oconf *c, ofr *f, int ch) {
     case F_LIT: return step_lit(f, ch);
     case F_ENUM: return step_enum(g, f, ch);
     case F_CALC: return step_calc(g, f, ch);
-    case F_TEXT: return step_text(c, f, ch);
+    case F_TEXT: return step_text(g, c, f, ch);
+    case F_STROP: return step_strop(g, f, ch);
     }
     return R_DEAD;
 }

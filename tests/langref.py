@@ -342,6 +342,17 @@ def _calc_member(spec, s):
 
 
 _RESULT_RE = re.compile(rb"<result>-?[0-9]{1,20}</result>|<result_error>[\x20-\x3b\x3d-\x7e]*</result_error>")
+_TEXT_RESULT_RE = re.compile(rb"<result>[\x20-\x3b\x3d-\x7e]*</result>|<result_error>[\x20-\x3b\x3d-\x7e]*</result_error>")
+
+
+def _strop_re(ws_max):
+    w = rb"[ \t\n\r]{0,%d}" % ws_max
+    s = rb'"[\x20\x21\x23-\x3b\x3d-\x5b\x5d-\x7e]*"'
+    i = rb"-?[0-9]{1,6}"
+    c = w + rb"," + w
+    body = (rb"count\(" + w + s + c + s + w + rb"\)|(?:len|reverse|upper)\(" + w + s + w + rb"\)|substr\(" + w + s + c
+            + i + c + i + w + rb"\)")
+    return re.compile(rb"<strop>(?:" + body + rb")</strop>")
 _TEXT_RE = re.compile(rb"[\n\x20-\x3b\x3d-\x7e]*")
 
 
@@ -349,6 +360,8 @@ def calc_text_parts(spec, data: bytes):
     """Split a complete calc_text member into (who, bytes) pieces, who =
     "model" or "engine"; None if `data` is not a member.  Reads the text
     left to right with regular expressions and the calc-span validator."""
+    evaluators = spec.get("evaluators", ["calc"])
+    strop_re = _strop_re(_get(spec, "ws_max"))
     parts = []
     i = 0
     while True:
@@ -359,14 +372,21 @@ def calc_text_parts(spec, data: bytes):
         if data[i:] == b"<end>":
             parts.append(("model", b"<end>"))
             return parts
-        if not data.startswith(b"<calc>", i):
+        if "calc" in evaluators and data.startswith(b"<calc>", i):
+            j = data.find(b"</calc>", i)
+            if j < 0 or not _calc_member(spec, data[i:j + 7]):
+                return None
+            end, result_re = j + 7, _RESULT_RE
+        elif "strop" in evaluators and data.startswith(b"<strop>", i):
+            s = strop_re.match(data, i)
+            if not s:
+                return None
+            end, result_re = s.end(), _TEXT_RESULT_RE
+        else:
             return None
-        j = data.find(b"</calc>", i)
-        if j < 0 or not _calc_member(spec, data[i:j + 7]):
-            return None
-        parts.append(("model", data[i:j + 7]))
-        i = j + 7
-        r = _RESULT_RE.match(data, i)
+        parts.append(("model", data[i:end]))
+        i = end
+        r = result_re.match(data, i)
         if not r:
             return None
         parts.append(("engine", r.group(0)))

@@ -27,15 +27,17 @@ CFG = 6
 SPEC = W.SPECS[CFG]
 
 
-def _setup(V=4096, gen_cap=W.GEN_CAP):
-    blob, off = W.make_vocab(CFG, V)
+def _setup(V=4096, gen_cap=W.GEN_CAP, cfg=CFG):
+    blob, off = W.make_vocab(cfg, V)
     toks = [blob[off[i]:off[i + 1]] for i in range(len(off) - 1)]
-    g = cg.Grammar(W.spec_json(CFG), blob, off, gen_cap=gen_cap)
-    og = O.load_spec(W.spec_json(CFG))
+    g = cg.Grammar(W.spec_json(cfg), blob, off, gen_cap=gen_cap)
+    og = O.load_spec(W.spec_json(cfg))
     return g, og, blob, off, toks
 
 
 def _oracle_result(span: bytes) -> bytes:
+    if span.startswith(b"<strop>"):
+        return b"<result>" + O.eval_strop(span) + b"</result>"
     try:
         return b"<result>%d</result>" % O.eval_calc(span, O.INT64_RANGE)
     except O.CalcError as e:
@@ -43,6 +45,10 @@ def _oracle_result(span: bytes) -> bytes:
 
 
 def _device_result(span: bytes) -> bytes:
+    if span.startswith(b"<strop>"):
+        rc, v = cg.eval_strop(span)
+        assert rc == cg.CG_OK, (span, v)
+        return b"<result>" + v + b"</result>"
     rc, v = cg.eval_calc(span)
     if rc == cg.CG_OK:
         return b"<result>%d</result>" % v
@@ -51,17 +57,17 @@ def _device_result(span: bytes) -> bytes:
 
 
 def _last_span(text: bytes) -> bytes:
-    return text[text.rindex(b"<calc>"):]
+    return text[max(text.rfind(b"<calc>"), text.rfind(b"<strop>")):]
 
 
-def _events(og, toks, pre, rng, n_events, split_results=True, stop_at_inject=False):
+def _events(og, toks, pre, rng, n_events, split_results=True, stop_at_inject=False, spec=SPEC):
     """A row's events, following a script: ("tok", id) for what the model
     writes, ("force", bytes) for what the engine writes after a closed span
     (sometimes in two pieces).  The oracle row is advanced alongside.
     stop_at_inject: end at the first event after which the engine must
     write (a closed span, or a result forced only in part)."""
     row = O.Row(og, W.GEN_CAP)
-    segs = W.calc_text_script(rng, SPEC, (1 if stop_at_inject else 0) + rng.below(4))
+    segs = W.calc_text_script(rng, spec, (1 if stop_at_inject else 0) + rng.below(4))
     ev = []
     for seg in segs:
         pos = 0
@@ -131,16 +137,16 @@ def _masks(g, st):
     return mask.cpu().numpy().view(np.uint64)
 
 
-@pytest.mark.parametrize("V", [4096, 32000])
-def test_mask_parity_at_injection_points(V):
-    say("inject masks", V)
-    g, og, blob, off, toks = _setup(V)
+@pytest.mark.parametrize("V,cfg", [(4096, 6), (32000, 6), (8000, 7)])
+def test_mask_parity_at_injection_points(V, cfg):
+    say("inject masks", V, cfg)
+    g, og, blob, off, toks = _setup(V, cfg=cfg)
     pre = W.ScriptTokens(toks)
     rng = W.SplitMix(0x1A1 + V)
     B = 96
     events, rows = [], []
     for r in range(B):
-        ev, row = _events(og, toks, pre, rng, 1 + rng.below(60), stop_at_inject=r % 4 == 0)
+        ev, row = _events(og, toks, pre, rng, 1 + rng.below(60), stop_at_inject=r % 4 == 0, spec=W.SPECS[cfg])
         events.append(ev)
         rows.append(row)
     st, steps = _replay(g, B, events)
@@ -222,20 +228,20 @@ def _bias_toward_script(logits, targets, bonus=40.0):
     return (logits.float() + add.to(logits.device)).to(logits.dtype)
 
 
-@pytest.mark.parametrize("fused,T", [(True, 0.7), (False, 0.7), (True, 0.0)])
-def test_decode_loop_with_injection(fused, T):
+@pytest.mark.parametrize("fused,T,cfg", [(True, 0.7, 6), (False, 0.7, 6), (True, 0.0, 6), (True, 0.7, 7)])
+def test_decode_loop_with_injection(fused, T, cfg):
     """fill -> sample -> advance; rows that report CG_ROW_INJECT get their
     span evaluated on the host (cg_eval_calc) and the result forced
     (cg_force_bytes).  The oracle runs the same loop with its own masks,
     sampler, rows and evaluator; logits lean toward each row's script."""
     import torch
-    say("inject loop", fused, T)
+    say("inject loop", fused, T, cfg)
     V = 4096
-    g, og, blob, off, toks = _setup(V)
+    g, og, blob, off, toks = _setup(V, cfg=cfg)
     pre = W.ScriptTokens(toks)
     B = 12
     rng = W.SplitMix(0x1A5 + int(fused) + int(T * 10))
-    scripts = [W.calc_text_script(rng, SPEC, 1 + rng.below(3)) for _ in range(B)]
+    scripts = [W.calc_text_script(rng, W.SPECS[cfg], 1 + rng.below(3)) for _ in range(B)]
     st = g.new_states(B)
     g.init_state(st)
     stepc = torch.zeros(B, dtype=torch.int32, device="cuda")
@@ -243,7 +249,7 @@ def test_decode_loop_with_injection(fused, T):
     fstatus = torch.zeros(B, dtype=torch.int32, device="cuda")
     mask = torch.empty((B, g.W), dtype=torch.int64, device="cuda")
     temp = torch.full((B,), float(T), dtype=torch.float32, device="cuda")
-    seeds = np.array(W.row_seeds(CFG, B), dtype=np.uint64)
+    seeds = np.array(W.row_seeds(cfg, B), dtype=np.uint64)
     seed_t = torch.from_numpy(seeds.view(np.int64)).cuda()
     ws = cg.new_workspace(B, V)
     ids = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -261,7 +267,7 @@ def test_decode_loop_with_injection(fused, T):
             seg = scripts[r][min(seg_i[r], len(scripts[r]) - 1)]
             targets.append(pre.longest(seg[len(written):]) if not row.done and seg.startswith(written)
                            and len(written) < len(seg) else None)
-        logits = _bias_toward_script(W.make_logits(CFG, s, B, V, "cuda"), targets)
+        logits = _bias_toward_script(W.make_logits(cfg, s, B, V, "cuda"), targets)
         g.fill_bitmask(st, mask)
         if fused:
             g.sample_advance(logits, mask, temp, seed_t, stepc, ws, ids, lp, st, status)
