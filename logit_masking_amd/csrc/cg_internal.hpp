@@ -124,11 +124,13 @@ __host__ __device__ inline bool step_byte(Walker &w, uint32_t b, const uint64_t 
     return ok;
 }
 
-// Copy n table slots to LDS with up to 16 loads per thread in flight before
-// the first store (a plain load/store loop waits out one round trip per slot).
-__device__ inline void stage_table(uint64_t *dst, const uint64_t *__restrict__ src, uint32_t n) {
+// Copy table slots [start, n) to LDS with up to 16 loads per thread in
+// flight before the first store (a plain load/store loop waits out one round
+// trip per slot).
+__device__ inline void stage_table(uint64_t *dst, const uint64_t *__restrict__ src, uint32_t n,
+                                   uint32_t start = 0) {
     constexpr int kInFlight = 16;
-    for (uint32_t base = 0; base < n; base += kInFlight * blockDim.x) {
+    for (uint32_t base = start; base < n; base += kInFlight * blockDim.x) {
         uint64_t v[kInFlight];
 #pragma unroll
         for (int j = 0; j < kInFlight; j++) {

@@ -20,7 +20,9 @@ namespace cg {
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 2048;            // ids per chunk (32 mask words)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr double kContendChunk = 2e-5;  // screened chunk scores carry < 2e-6 of rounding
+// Screened chunk scores carry < 1.2e-5 of error (float noise < 1e-5, float
+// chunk sums ~1e-6): a gap above this decides the chunk outright.
+constexpr double kContendChunk = 5e-5;
 
 template <int DT>
 __device__ inline float load_logit(const void *p, size_t i) {
@@ -64,17 +66,6 @@ __device__ __forceinline__ int dpp_i(int v) {
 }
 constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
-template <class F>
-__device__ __forceinline__ float wave_reduce_f(float v, F op) {
-    v = op(v, __int_as_float(dpp_i<kQuadSwap1>(__float_as_int(v))));
-    v = op(v, __int_as_float(dpp_i<kQuadSwap2>(__float_as_int(v))));
-    v = op(v, __int_as_float(dpp_i<kRowRor4>(__float_as_int(v))));
-    v = op(v, __int_as_float(dpp_i<kRowRor8>(__float_as_int(v))));
-    const int b = __float_as_int(v);
-    return op(op(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
-              op(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
-}
-
 template <int CTRL>
 __device__ __forceinline__ double dpp_d(double v) {
     const long long u = __double_as_longlong(v);
@@ -96,10 +87,29 @@ __device__ __forceinline__ double wave_reduce_d(double v, F op) {
     return op(op(readlane_d(v, 0), readlane_d(v, 16)), op(readlane_d(v, 32), readlane_d(v, 48)));
 }
 
-__device__ inline float wave_max_f(float v) { return wave_reduce_f(v, [](float a, float b) { return fmaxf(a, b); }); }
+// Wave-wide max / sum of a float in six DPP-fused instructions: four steps
+// within each 16-lane row, then two row broadcasts (lane 15 of each row into
+// the next row, lane 31 into rows 2 and 3) leave the result in lane 63.
+// Every lane must be active.  Two wait states before each DPP read of the
+// value the previous instruction wrote.
+#define CG_DPP_WAVE_REDUCE(OP)                                                    \
+    "s_nop 1\n\t" OP " %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t" \
+    "s_nop 1\n\t" OP " %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t" \
+    "s_nop 1\n\t" OP " %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"          \
+    "s_nop 1\n\t" OP " %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"          \
+    "s_nop 1\n\t" OP " %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"       \
+    "s_nop 1\n\t" OP " %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"       \
+    "s_nop 1"
+__device__ __forceinline__ float wave_max_f(float v) {
+    asm(CG_DPP_WAVE_REDUCE("v_max_f32_dpp") : "+v"(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 __device__ inline double wave_max_d(double v) { return wave_reduce_d(v, [](double a, double b) { return fmax(a, b); }); }
 __device__ inline double wave_sum_d(double v) { return wave_reduce_d(v, [](double a, double b) { return a + b; }); }
-__device__ inline float wave_sum_f(float v) { return wave_reduce_f(v, [](float a, float b) { return a + b; }); }
+__device__ __forceinline__ float wave_sum_f(float v) {
+    asm(CG_DPP_WAVE_REDUCE("v_add_f32_dpp") : "+v"(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 
 // argmax of (value, index): larger value, then lower index; index -1 = none
 __device__ inline void arg_better(double &v, int &i, double ov, int oi) {
@@ -127,56 +137,90 @@ __device__ inline void wave_argmax(double &v, int &i) {
     i = bi;
 }
 
-// Lane l holds ids c*2048 + g*512 + 8l + j (g = 0..3, j = 0..7): every load
-// instruction covers one contiguous 1 KB (bf16) / 2 KB (f32) of the row.
+// Lane l holds the 32 ids c*2048 + 32l + j (j = 0..31): 64 (bf16) or 128
+// (float32) contiguous bytes of the row, and their 32 mask bits as one
+// dword.  Group g = ids 8g .. 8g + 7 of the lane, mask byte g.
 template <int DT>
 struct ChunkRegs {
     uint32_t d[DT == 1 ? 16 : 32];
-    uint32_t mb[4];
+    uint32_t mw;
 };
 
+// Bounds-checked load (the row's partial last chunk, or rows whose storage
+// is not 16-byte aligned): ids past V read as 0 with their mask bits clear.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DT> &R, const void *logits, size_t rowbase,
                                            const uint8_t *mrow, int V, int c, int lane) {
+    const int e0 = c * kChunk + lane * 32;
+    uint32_t mw = 0;
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-        const int e0 = c * kChunk + g * 512 + lane * 8;
-        R.mb[g] = (e0 < V) ? mrow[e0 >> 3] : 0u;
-        if (VEC && e0 + 8 <= V) {
-            if (DT == 1) {
-                const uint4 v = *(const uint4 *)((const uint16_t *)logits + rowbase + e0);
-                R.d[g * 4 + 0] = v.x; R.d[g * 4 + 1] = v.y; R.d[g * 4 + 2] = v.z; R.d[g * 4 + 3] = v.w;
-            } else {
-                const uint4 v0 = *(const uint4 *)((const float *)logits + rowbase + e0);
-                const uint4 v1 = *(const uint4 *)((const float *)logits + rowbase + e0 + 4);
-                R.d[g * 8 + 0] = v0.x; R.d[g * 8 + 1] = v0.y; R.d[g * 8 + 2] = v0.z; R.d[g * 8 + 3] = v0.w;
-                R.d[g * 8 + 4] = v1.x; R.d[g * 8 + 5] = v1.y; R.d[g * 8 + 6] = v1.z; R.d[g * 8 + 7] = v1.w;
-            }
+    for (int b = 0; b < 4; b++)
+        if (e0 + 8 * b < V) mw |= (uint32_t)mrow[(e0 >> 3) + b] << (8 * b);
+    if (e0 + 32 > V) mw &= (e0 >= V) ? 0u : ((1u << (V - e0)) - 1u);
+    R.mw = mw;
+    if (VEC && e0 + 32 <= V) {
+        constexpr int kVec = DT == 1 ? 4 : 8;  // 16-byte loads per lane
+#pragma unroll
+        for (int k = 0; k < kVec; k++) {
+            const uint4 v = DT == 1 ? *(const uint4 *)((const uint16_t *)logits + rowbase + e0 + 8 * k)
+                                    : *(const uint4 *)((const float *)logits + rowbase + e0 + 4 * k);
+            R.d[4 * k] = v.x; R.d[4 * k + 1] = v.y; R.d[4 * k + 2] = v.z; R.d[4 * k + 3] = v.w;
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+        const float x = (e0 + j < V) ? load_logit<DT>(logits, rowbase + e0 + j) : 0.f;
+        if (DT == 1) {
+            const uint32_t u = __float_as_uint(x) >> 16;
+            if (j & 1) R.d[j / 2] |= u << 16;
+            else R.d[j / 2] = u;
         } else {
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float x = (e0 + j < V) ? load_logit<DT>(logits, rowbase + e0 + j) : 0.f;
-                if (DT == 1) {
-                    const uint32_t u = __float_as_uint(x) >> 16;
-                    if (j & 1) R.d[g * 4 + j / 2] |= u << 16;
-                    else R.d[g * 4 + j / 2] = u;
-                } else {
-                    R.d[g * 8 + j] = __float_as_uint(x);
-                }
-            }
-            if (e0 + 8 > V) R.mb[g] &= (e0 >= V) ? 0u : ((1u << (V - e0)) - 1u);
+            R.d[j] = __float_as_uint(x);
         }
     }
 }
 
-// logit j of group g, or -inf where the mask bit is clear (a sign-extended
-// 1-bit field selects between the value and -inf)
+// The row as two buffer resources (logits and mask words): a buffer load past
+// the resource's size returns zeros, so every chunk, the row's partial last
+// one included, is read with the same unguarded vector loads.  The logits'
+// size is rounded up to whole dwords (a dword that holds the last id is read
+// whole, from the dword-aligned row).
+struct RowBufs {
+    __amdgpu_buffer_rsrc_t x, m;
+};
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+
+template <int DT>
+__device__ __forceinline__ void load_buf(ChunkRegs<DT> &R, const RowBufs &rb, int c, int lane) {
+    const int e0 = c * kChunk + lane * 32;
+    constexpr int kVec = DT == 1 ? 4 : 8, kEs = DT == 1 ? 2 : 4;
+#pragma unroll
+    for (int k = 0; k < kVec; k++) {
+        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.x, e0 * kEs + 16 * k, 0, 0));
+        R.d[4 * k] = v.x; R.d[4 * k + 1] = v.y; R.d[4 * k + 2] = v.z; R.d[4 * k + 3] = v.w;
+    }
+    R.mw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb.m, e0 >> 3, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t mask_byte(uint32_t mw, int g) { return (mw >> (8 * g)) & 0xFFu; }
+
+
+// max of three floats in one instruction.  fmaxf on values made by bit
+// manipulation costs an extra canonicalising instruction per operand; the
+// values here are logits or -inf, never signalling NaNs.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// float32 logit j of group g, or -inf where the mask bit is clear (a
+// sign-extended 1-bit field selects between the value and -inf)
 template <int DT>
 __device__ __forceinline__ float masked_x(const ChunkRegs<DT> &R, int g, int j) {
-    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)R.mb[g], j, 1);
-    uint32_t u;
-    if (DT == 1) u = (j & 1) ? (R.d[g * 4 + j / 2] & 0xFFFF0000u) : (R.d[g * 4 + j / 2] << 16);
-    else u = R.d[g * 8 + j];
+    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)R.mw, 8 * g + j, 1);
+    const uint32_t u = R.d[g * 8 + j];
     return __uint_as_float((sel & u) | (~sel & 0xFF800000u));
 }
 
@@ -193,29 +237,32 @@ __device__ __forceinline__ void init_pair_lut(uint4 *lut) {
     }
 }
 
-// masked max m and sum over allowed ids of 2^((x - m) kk), kk = log2(e) / T'.
-// The exponent is one fma, x kk - r(m kk), whose only error beyond a single
-// rounding is the constant offset m kk - r(m kk); that offset is taken out of
-// the chunk sum once, in double precision.  The 64 lane sums (each of 32
-// terms <= 1) are added as a tree in float: relative error ~1e-6.  Groups of
-// 8 ids with no allowed id skip the exponentials (most of a structural row).
+// Masked max m and sum over allowed ids of 2^((x - m) kk), kk = log2(e) / T'.
+// The masked values (masked-out ids as -inf) are widened to float once and
+// kept for the exponential pass.  The exponent is one fma, x kk - r(m kk),
+// whose only error beyond a single rounding is the constant offset
+// m kk - r(m kk); that offset is taken out of the chunk sum once.  The 64
+// lane sums (each of 32 terms <= 1) are added as a tree in float: relative
+// error ~1e-6.  Groups of 8 ids with no allowed id skip the exponentials
+// (most of a structural row).
 template <int DT>
 __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4 *lut, float kk, float &m_out,
-                                             double &s_out, bool &any_out) {
-    any_out = __any(R.mb[0] | R.mb[1] | R.mb[2] | R.mb[3]);
+                                             float &s_out, bool &any_out) {
+    any_out = __any(R.mw);
     m_out = -INFINITY;
-    s_out = 0.0;
+    s_out = 0.f;
     if (!any_out) return;
     float xm[32];
     float m = -INFINITY;
 #pragma unroll
     for (int g = 0; g < 4; g++) {
         if (DT == 1) {
-            const uint4 sel = lut[R.mb[g]];
+            const uint4 sel = lut[mask_byte(R.mw, g)];
             const uint32_t sp[4] = {sel.x, sel.y, sel.z, sel.w};
 #pragma unroll
             for (int p = 0; p < 4; p++) {
-                const uint32_t u = (R.d[g * 4 + p] & sp[p]) | (~sp[p] & 0xFF80FF80u);
+                uint32_t u = (R.d[g * 4 + p] & sp[p]) | (~sp[p] & 0xFF80FF80u);
+                asm("" : "+v"(u));  // one select, then two widenings (not re-derived per half)
                 xm[g * 8 + 2 * p] = __uint_as_float(u << 16);
                 xm[g * 8 + 2 * p + 1] = __uint_as_float(u & 0xFFFF0000u);
             }
@@ -224,7 +271,7 @@ __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4
             for (int j = 0; j < 8; j++) xm[g * 8 + j] = masked_x<DT>(R, g, j);
         }
 #pragma unroll
-        for (int j = 0; j < 8; j++) m = fmaxf(m, xm[g * 8 + j]);
+        for (int j = 0; j < 8; j += 2) m = max3f(m, xm[g * 8 + j], xm[g * 8 + j + 1]);
     }
     m = wave_max_f(m);
     m_out = m;
@@ -233,16 +280,17 @@ __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4
     float s = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; g++) {
-        if (R.mb[g]) {
+        if (mask_byte(R.mw, g)) {
             float sg = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; j++) sg += __builtin_amdgcn_exp2f(__builtin_fmaf(xm[g * 8 + j], kk, -mk));
             s += sg;
         }
     }
-    // every term carries the factor 2^(m kk - r(m kk)); divide it out
-    const double off = (double)m * (double)kk - (double)mk;
-    s_out = (double)wave_sum_f(s) * (1.0 - off * 0.6931471805599453);
+    // every term carries the factor 2^off, off = m kk - r(m kk) (exact from
+    // one fma, |off| <= half an ulp of m kk); divide it out
+    const float off = __builtin_fmaf(m, kk, -mk);
+    s_out = wave_sum_f(s) * (1.f - off * 0.69314718f);
 }
 
 // ---- block-wide reductions (kWaves waves) --------------------------------
@@ -288,14 +336,22 @@ __device__ __forceinline__ int wave_min_i(int v) {
 }
 
 struct ChunkInfo {
-    double g;     // chunk noise G(1, c) (sampled rows)
-    double s;     // sum over allowed ids of 2^((x - m) kk)
+    float s;      // sum over allowed ids of 2^((x - m) kk)
     float m;      // largest allowed logit
+    float g;      // chunk noise G(1, c) in float, for screening (sampled rows)
     int any;      // the chunk has an allowed id
 };
 
+// The row's decision as the three reducing waves publish it.
+struct RowDecision {
+    double lse_all, cs1, cs2;
+    float mv;
+    int mc, c1;
+};
+
 struct Decision {
-    double lmax, mv, lse_all, cs1;
+    double lse_all, cs1;
+    float mv;
     int mc, chosen;
     bool exact_chunk;
 };
@@ -433,19 +489,8 @@ __device__ __forceinline__ Top2 top2_slots(const float *v1, const int *i1, const
     return r;
 }
 
-// One workgroup per row.  Its 16 waves stream the row's 2048-id chunks
-// (wave w takes chunks w, w + 16, ...; the next chunk's loads are issued
-// before the current one is reduced) and leave one summary per chunk in LDS;
-// then the whole workgroup forms the log-normaliser and picks the token.
-// No state crosses workgroups, so no device-wide fence is ever needed.
-// The row's decision as the three reducing waves publish it.
-struct RowDecision {
-    double lmax, lse_all, mv, cs1, cs2;
-    int mc, c1;
-};
-
 // Per-wave copy of the best chunk seen so far (bf16 rows): the chunk's logits
-// in id order (4 KB) and its mask bytes, so the pick inside the chosen chunk
+// in id order (4 KB) and its mask words, so the pick inside the chosen chunk
 // reads LDS instead of HBM.
 constexpr int kStashWords = kChunk / 2;  // bf16 pairs per chunk
 struct Stash {
@@ -474,6 +519,16 @@ struct AdvanceArgs {
 // byte offset of the stash in dynamic LDS: after the chunk summaries, 16-byte aligned
 __host__ __device__ inline size_t stash_offset(int K) { return ((size_t)K * sizeof(ChunkInfo) + 15) / 16 * 16; }
 
+// table slots fetched into registers ahead of the logits (the rest, if any, after them)
+constexpr int kStageRegs = 4;
+
+// One workgroup per row.  Its 16 waves stream the row's 2048-id chunks (wave
+// w takes chunks w, w + 16, ...; the next chunk's loads are in flight while
+// one is reduced), leave one summary
+// per chunk in LDS and fold each chunk into a running per-wave summary.  After
+// one barrier every wave merges the 16 wave summaries into the row's decision
+// and the workgroup picks the token inside the chosen chunk.  No state crosses
+// workgroups, so no device-wide fence is ever needed.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
                                                  const uint64_t *__restrict__ mask, int words_per_row,
@@ -487,7 +542,9 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     __shared__ Slots sl[4];
     __shared__ uint4 lut[256];
     __shared__ RowDecision wdec;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index through readfirstlane: the compiler then knows it (and
+    // every chunk index derived from it) is uniform, and branches on scalars
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = blockIdx.x;
     const float Tf = temp[r];
     const uint64_t sd = seed[r];
@@ -501,104 +558,179 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const size_t rowbase = (size_t)r * (size_t)stride;
     constexpr double kLn2d = 0.6931471805599453, kLog2ed = 1.4426950408889634;
     const bool stash = DT == 1 && use_stash;
-    if (DT == 1) init_pair_lut(lut);
-    if (stash && lane == 0) st->c[wave] = -1;
-    // fused advance: the table is staged while the logits stream
+    // fused advance: the transition table is fetched after the stream (into
+    // registers, in flight across the decision) and staged in LDS before the
+    // pick; the walk of the chosen token reads it there
     const bool fuse = adv.comb != nullptr;
     uint64_t *lds_comb = (uint64_t *)((char *)dyn + adv.comb_off);
-    if (fuse) stage_table(lds_comb, adv.comb, adv.comb_len);
+    const uint32_t tn = fuse ? adv.comb_len : 0u;
     // the pick (thread 0): every exit path below leaves it here
     int pick = -1;
     float pick_lp = 0.f;
+    Decision dc;
     {
-        // chunks per wave in flight: the one being reduced and the next two
-        // (bf16), or the next one (float32, whose chunks take twice the registers)
-        constexpr int kAhead = DT == 1 ? 2 : 1;
-        ChunkRegs<DT> cur, nxt, nxt2;
+        // Chunks stream in groups of four per wave, as straight-line code:
+        // three chunks' loads in flight, each chunk reduced as soon as its
+        // own loads are in, the fourth load issued into the first buffer once
+        // it is free.  Loads take chunk indices clamped into the row (a wave
+        // with fewer chunks re-reads one, from cache), so every path issues
+        // the same loads and the compiler's waits count exactly the loads
+        // behind each chunk.  Rows whose storage is not 16-byte aligned are
+        // read one chunk at a time with bounds-checked loads instead.
+        const int Kf = VEC ? K : 0;  // chunks read through buffer loads
+        RowBufs rb;
+        rb.x = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)logits + rowbase * (DT == 1 ? 2 : 4)), (short)0,
+                                                 (V * (DT == 1 ? 2 : 4) + 3) & ~3, kRsrcWord3);
+        rb.m = __builtin_amdgcn_make_buffer_rsrc((void *)mrow, (short)0, words_per_row * 8, kRsrcWord3);
+        // (a scheduling barrier after each chunk's loads keeps the compiler
+        // from regrouping loads across chunks, which would make the first
+        // chunk wait for the others)
+        auto load = [&](ChunkRegs<DT> &R, int cc) {
+            load_buf<DT>(R, rb, min(cc, Kf - 1), lane);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // mask bits of this lane's ids past V in the last chunk (a caller's
+        // mask may carry set bits there)
+        const int tail_ids = V - ((K - 1) * kChunk + lane * 32);
+        const uint32_t tail_mw = tail_ids >= 32 ? ~0u : tail_ids <= 0 ? 0u : ((1u << tail_ids) - 1u);
+        if (DT == 1) init_pair_lut(lut);
+        if (stash && lane == 0) st->c[wave] = -1;
+        __syncthreads();  // the mask table
+        // The barrier comes before the loads: a wave whose loads are issued
+        // starts reducing without waiting for the others to issue theirs.
+        ChunkRegs<DT> b0, b1, b2;
+        auto start_group = [&](int c0) {
+            load(b0, c0);
+            load(b1, c0 + kWaves);
+            if (DT == 1) load(b2, c0 + 2 * kWaves);
+        };
+        // The first group's loads: every wave issues them (clamped, even with
+        // no chunk of its own) whenever the row has pipelined chunks at all,
+        // so that the loads before the first reduction are the same on every
+        // path.
         int c = wave;
-        if (c < K) load_chunk<DT, VEC>(cur, logits, rowbase, mrow, V, c, lane);
-        if (kAhead == 2 && c + kWaves < K) load_chunk<DT, VEC>(nxt, logits, rowbase, mrow, V, c + kWaves, lane);
-        // chunk noise G(1, c) of every chunk (c = wave + 16 lane + 1024 j), while the loads fly
+        if (Kf > 0) start_group(c);
+        // screening noise G(1, c) of this wave's chunks (c = wave + 16 lane +
+        // 1024 j; written and read by the same wave), while the loads fly
         if (!greedy)
             for (int cg = wave + kWaves * lane; cg < K; cg += kWaves * 64) {
                 const uint4 o = philox4x32_10(make_uint4((uint32_t)cg >> 2, stp, 1u, 0u), k0, k1);
-                ci[cg].g = gumbel64(pick_word(o, cg & 3));
+                ci[cg].g = gumbel32(pick_word(o, cg & 3));
             }
-        __syncthreads();  // the mask table
-        double best = -INFINITY;
-        for (; c < K; c += kWaves) {
-            if (c + kAhead * kWaves < K)
-                load_chunk<DT, VEC>(kAhead == 2 ? nxt2 : nxt, logits, rowbase, mrow, V, c + kAhead * kWaves, lane);
-            float m;
-            double s;
+        // reduce chunk cc into its summary; the wave's best chunk so far (by
+        // the chunk score in float: m for greedy rows, m/T + ln s + G(1, c)
+        // for sampled ones) is copied to the stash.  A near-tie that the
+        // float score orders differently from the decision's only costs
+        // the pick a read of the chunk from memory.
+        float best = -INFINITY;
+        const float invTf = (float)invT;
+        auto process = [&](ChunkRegs<DT> &R, int cc) {
+            if (VEC && cc == K - 1) R.mw &= tail_mw;
+            float m, s;
             bool any;
-            reduce_chunk<DT>(cur, lut, kk, m, s, any);
+            reduce_chunk<DT>(R, lut, kk, m, s, any);
             if (lane == 0) {
-                ci[c].m = m;
-                ci[c].s = s;
-                ci[c].any = any ? 1 : 0;
+                ci[cc].s = s;
+                ci[cc].m = m;
+                ci[cc].any = any ? 1 : 0;
             }
-            if (stash && any) {
-                // the same score the row's decision ranks chunks by
-                double score = (double)m;
-                if (!greedy)
-                    score = (s > 0.0) ? (double)m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)s) + ci[c].g
-                                      : -INFINITY;
-                if (score > best) {
-                    best = score;
+            if (!stash || !any) return;
+            const float score =
+                greedy ? m : (s > 0.f ? m * invTf + 0.69314718f * __builtin_amdgcn_logf(s) + ci[cc].g : -INFINITY);
+            if (score > best) {
+                best = score;
 #pragma unroll
-                    for (int g = 0; g < 4; g++)
-                        *(uint4 *)&st->d[wave][g * 256 + lane * 4] =
-                            make_uint4(cur.d[g * 4], cur.d[g * 4 + 1], cur.d[g * 4 + 2], cur.d[g * 4 + 3]);
-                    st->mb[wave][lane] = cur.mb[0] | cur.mb[1] << 8 | cur.mb[2] << 16 | cur.mb[3] << 24;
-                    if (lane == 0) st->c[wave] = c;
-                }
+                for (int k = 0; k < 4; k++)
+                    *(uint4 *)&st->d[wave][lane * 16 + k * 4] =
+                        make_uint4(R.d[k * 4], R.d[k * 4 + 1], R.d[k * 4 + 2], R.d[k * 4 + 3]);
+                st->mb[wave][lane] = R.mw;
+                if (lane == 0) st->c[wave] = cc;
             }
-            cur = nxt;
-            if (kAhead == 2) nxt = nxt2;
+        };
+        // a group of four chunks whose loads start_group issued
+        auto group = [&](int c0) {
+            if (DT == 1) {
+                process(b0, c0);
+                load(b0, c0 + 3 * kWaves);
+                if (c0 + kWaves < Kf) process(b1, c0 + kWaves);
+                if (c0 + 2 * kWaves < Kf) process(b2, c0 + 2 * kWaves);
+                if (c0 + 3 * kWaves < Kf) process(b0, c0 + 3 * kWaves);
+            } else {
+                // float32 chunks take twice the registers: two in flight
+                process(b0, c0);
+                load(b0, c0 + 2 * kWaves);
+                if (c0 + kWaves < Kf) process(b1, c0 + kWaves);
+                load(b1, c0 + 3 * kWaves);
+                if (c0 + 2 * kWaves < Kf) process(b0, c0 + 2 * kWaves);
+                if (c0 + 3 * kWaves < Kf) process(b1, c0 + 3 * kWaves);
+            }
+        };
+        // The first group runs outside any loop, so that no merge of loop
+        // paths blurs the compiler's count of loads in flight (a vocabulary
+        // of up to 131072 ids is one group per wave); later groups loop.
+        if (c < Kf) group(c);
+        for (c += 4 * kWaves; c < Kf; c += 4 * kWaves) {
+            start_group(c);
+            group(c);
+        }
+        // rows not 16-byte aligned: every chunk, bounds-checked
+        for (c = wave < Kf ? wave + ((Kf - 1 - wave) / kWaves + 1) * kWaves : wave; c < K; c += kWaves) {
+            load_chunk<DT, VEC>(b0, logits, rowbase, mrow, V, c, lane);
+            process(b0, c);
         }
     }
+    // fused: the table's first slots into registers now, stored after the
+    // decision (indices clamped rather than guarded: a fixed number of loads
+    // keeps the wait before the stores exact)
+    const uint32_t treg = min(tn, (uint32_t)(kStageRegs * blockDim.x));
+    uint64_t tv[kStageRegs];
+    if (fuse) {
+#pragma unroll
+        for (int j = 0; j < kStageRegs; j++) tv[j] = adv.comb[min(j * blockDim.x + threadIdx.x, treg - 1)];
+    }
     __syncthreads();
-    // ---- the row's decision, three independent reductions over the chunk
-    // summaries on three waves at once: (0) the log-normaliser, (1) the
-    // largest logit (lowest chunk), (2) the two best chunk scores
-    // L_c + G(1, c).  L_c = m/T + ln s (ln from v_log_f32: the chunk sums
-    // carry ~1e-6 of float rounding anyway).
+    // ---- the row's decision: three independent reductions over the chunk
+    // summaries (lane j takes chunks j, j + 64, ...) on three waves at once:
+    // (0) the log-normaliser over the chunk log-masses L_c = m/T + ln s (ln
+    // from v_log_f32: the chunk sums carry ~1e-6 of float rounding anyway),
+    // (1) the largest allowed logit and the lowest chunk holding it, (2) the
+    // two best chunk scores L_c + G(1, c).  The other waves stage the table.
     if (wave < 3) {
         auto lmass = [&](const ChunkInfo &x) -> double {
-            return (x.any && x.s > 0.0) ? (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s)
-                                        : -INFINITY;
+            return (x.any && x.s > 0.f) ? (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf(x.s) : -INFINITY;
         };
         if (wave == 0) {
-            double lc = -INFINITY;
-            for (int c = lane; c < K; c += 64) lc = fmax(lc, lmass(ci[c]));
-            lc = wave_max_d(lc);
-            float acc = 0.f;
-            if (lc > -INFINITY)
-                for (int c = lane; c < K; c += 64) {
-                    const double l = lmass(ci[c]);
-                    if (l > -INFINITY) acc += __builtin_amdgcn_exp2f((float)((l - lc) * kLog2ed));
+            double lmax = -INFINITY;
+            float lsum = 0.f;
+            for (int cc = lane; cc < K; cc += 64) {
+                const double l = lmass(ci[cc]);
+                if (!(l > -INFINITY)) continue;
+                if (l > lmax) {
+                    lsum = lsum * __builtin_amdgcn_exp2f((float)((lmax - l) * kLog2ed)) + 1.f;
+                    lmax = l;
+                } else {
+                    lsum += __builtin_amdgcn_exp2f((float)((l - lmax) * kLog2ed));
                 }
-            const double sum = wave_sum_d((double)acc);
-            if (lane == 0) {
-                wdec.lmax = lc;
-                wdec.lse_all = lc + kLn2d * (double)__builtin_amdgcn_logf((float)sum);
             }
+            const double L = wave_max_d(lmax);
+            const float t =
+                wave_sum_f(lmax > -INFINITY ? lsum * __builtin_amdgcn_exp2f((float)((lmax - L) * kLog2ed)) : 0.f);
+            if (lane == 0) wdec.lse_all = L > -INFINITY ? L + kLn2d * (double)__builtin_amdgcn_logf(t) : -INFINITY;
         } else if (wave == 1) {
             double mv = -INFINITY;
             int mc = -1;
-            for (int c = lane; c < K; c += 64)
-                if (ci[c].any) arg_better(mv, mc, (double)ci[c].m, c);
+            for (int cc = lane; cc < K; cc += 64)
+                if (ci[cc].any) arg_better(mv, mc, (double)ci[cc].m, cc);
             wave_argmax(mv, mc);
             if (lane == 0) {
-                wdec.mv = mv;
+                wdec.mv = (float)mv;
                 wdec.mc = mv > -INFINITY ? mc : -1;  // allowed tokens all at -inf: nothing to draw
             }
         } else if (!greedy) {
             Top2d cs{-INFINITY, -INFINITY, -1};
-            for (int c = lane; c < K; c += 64) {
-                const double l = lmass(ci[c]);
-                if (l > -INFINITY) top2d_merge(cs, l + ci[c].g, c, -INFINITY);
+            for (int cc = lane; cc < K; cc += 64) {
+                const double l = lmass(ci[cc]);
+                if (l > -INFINITY) top2d_merge(cs, l + (double)ci[cc].g, cc, -INFINITY);
             }
             cs = top2d_wave(cs);
             if (lane == 0) {
@@ -608,9 +740,16 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             }
         }
     }
-    __syncthreads();
-    Decision dc;
-    dc.lmax = wdec.lmax;
+    // the table to LDS (made visible by the next barrier)
+    if (fuse) {
+#pragma unroll
+        for (int j = 0; j < kStageRegs; j++) {
+            const uint32_t i = j * blockDim.x + threadIdx.x;
+            if (i < treg) lds_comb[i] = tv[j];
+        }
+        if (tn > treg) stage_table(lds_comb, adv.comb, tn, treg);
+    }
+    __syncthreads();  // the decision (and the table)
     dc.lse_all = wdec.lse_all;
     dc.mv = wdec.mv;
     dc.mc = wdec.mc;
@@ -620,15 +759,20 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     do {
     if (dc.mc < 0) break;  // nothing allowed: a finished row
     if (dc.exact_chunk) {
-        // two chunks within the screening window: decide on exact log-masses (rare)
+        // two chunks within the screening window: decide on exact log-masses
+        // and noise in double (rare)
         double bb = -INFINITY;
         int bbc = -1;
         for (int c = 0; c < K; c++) {
             const ChunkInfo x = ci[c];
-            if (!x.any || !(x.s > 0.0)) continue;
-            const double l = (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf((float)x.s);
-            if (l + x.g < dc.cs1 - 2 * kContendChunk) continue;
-            arg_better(bb, bbc, chunk_lse_exact<DT>(logits, rowbase, mrow, V, c, T, (double)x.m, sl[1].a) + x.g, c);
+            if (!x.any || !(x.s > 0.f)) continue;
+            const double l = (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf(x.s);
+            if (l + (double)x.g < dc.cs1 - 2 * kContendChunk) continue;
+            const uint4 o = philox4x32_10(make_uint4((uint32_t)c >> 2, stp, 1u, 0u), k0, k1);
+            arg_better(bb, bbc,
+                       chunk_lse_exact<DT>(logits, rowbase, mrow, V, c, T, (double)x.m, sl[1].a) +
+                           gumbel64(pick_word(o, c & 3)),
+                       c);
         }
         dc.chosen = bbc;  // every thread computed the same
     }
@@ -636,9 +780,11 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     if (chosen < 0) break;  // every allowed logit is -inf: no distribution to draw from
     // (3) inside the chunk: threads 0..511 take 4 ids each, e = 4t .. 4t + 3
     // (one Philox block), from the stash of the wave that reduced the chunk,
-    // else from HBM
+    // else from HBM.  Eight waves, not sixteen: the Philox rounds dominate
+    // and cost per wave, whatever the ids per lane.
     const int t = threadIdx.x;
-    const bool tok = t < kChunk / 4;
+    constexpr int kTokWaves = kChunk / 4 / 64;
+    const bool tok = wave < kTokWaves;
     const int e = chosen * kChunk + 4 * t;
     const int ws = chosen % kWaves;
     const bool from_stash = stash && st->c[ws] == chosen;
@@ -651,8 +797,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             xq[1] = __uint_as_float(dw.x & 0xFFFF0000u);
             xq[2] = __uint_as_float(dw.y << 16);
             xq[3] = __uint_as_float(dw.y & 0xFFFF0000u);
-            const int li = 4 * t;
-            mb4 = (st->mb[ws][(li & 511) >> 3] >> (8 * (li >> 9) + (li & 7))) & 15u;
+            mb4 = (st->mb[ws][t >> 3] >> ((4 * t) & 31)) & 15u;
         } else {
 #pragma unroll
             for (int j = 0; j < 4; j++)
@@ -670,27 +815,23 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         }
         return load_logit<DT>(logits, rowbase + id);
     };
-    constexpr int kTokWaves = kChunk / 4 / 64;
     if (greedy) {
         // the lowest id of the chunk holding the largest logit
         int im = 0x7FFFFFFF;
 #pragma unroll
         for (int j = 3; j >= 0; j--)
-            if (((mb4 >> j) & 1u) && (double)xq[j] == dc.mv) im = e + j;
-        if (wave < kTokWaves) {
+            if (((mb4 >> j) & 1u) && xq[j] == dc.mv) im = e + j;
+        if (tok) {
             im = wave_min_i(im);
             if (lane == 0) sl[2].i[wave] = im;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
-            int si[kTokWaves];
+            int best = sl[2].i[0];
 #pragma unroll
-            for (int w = 0; w < kTokWaves; w++) si[w] = sl[2].i[w];
-            int best = si[0];
-#pragma unroll
-            for (int w = 1; w < kTokWaves; w++) best = min(best, si[w]);
+            for (int w = 1; w < kTokWaves; w++) best = min(best, sl[2].i[w]);
             pick = best;
-            pick_lp = (float)(dc.mv - dc.lse_all);
+            pick_lp = (float)((double)dc.mv - dc.lse_all);
         }
         break;
     }
@@ -701,7 +842,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     uint4 o = make_uint4(0, 0, 0, 0);
     if (mb4) o = philox4x32_10(make_uint4((uint32_t)e >> 2, stp, 0u, 0u), k0, k1);
     const uint32_t wq[4] = {o.x, o.y, o.z, o.w};
-    if (wave < kTokWaves) {
+    if (tok) {
         Top2 ts{-INFINITY, -INFINITY, -1};
 #pragma unroll
         for (int j = 0; j < 4; j++)
@@ -730,7 +871,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     if ((double)tt.v1 - (double)tt.v2 > win) {
         if (threadIdx.x == 0) {
             pick = tt.i1;
-            pick_lp = (float)((double)x_of(tt.i1) / T - dc.lse_all);
+            pick_lp = (float)((double)x_of(tt.i1) * invT - dc.lse_all);
         }
         break;
     }
@@ -743,7 +884,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         if ((double)(xq[j] * it + gumbel32(wq[j])) >= (double)tt.v1 - win)
             arg_better(tv, ti, (double)xq[j] / T + gumbel64(wq[j]), e + j);
     }
-    if (wave < kTokWaves) {
+    if (tok) {
         wave_argmax(tv, ti);
         if (lane == 0) {
             sl[3].b[wave] = tv;
@@ -756,7 +897,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         int i = sl[3].j[0];
         for (int k = 1; k < kTokWaves; k++) arg_better(v, i, sl[3].b[k], sl[3].j[k]);
         pick = i;
-        pick_lp = (float)((double)x_of(i) / T - dc.lse_all);
+        pick_lp = (float)((double)x_of(i) * invT - dc.lse_all);
     }
     } while (0);
     // ---- epilogue: thread 0 publishes the pick and, fused, commits it ---------
@@ -800,9 +941,10 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
     (void)ws;
     if (B == 0) return CG_OK;
     const int K = (V + kChunk - 1) / kChunk;
+    constexpr int kMaxChunks = 2048;  // 32 KiB of chunk summaries
     const size_t lds_ci = (size_t)K * sizeof(ChunkInfo);
-    if (lds_ci > 48 * 1024) {
-        set_error("apply_mask_sample: vocab above %d", 48 * 1024 / (int)sizeof(ChunkInfo) * kChunk);
+    if (K > kMaxChunks) {
+        set_error("apply_mask_sample: vocab above %d", kMaxChunks * kChunk);
         return CG_E_ARG;
     }
     int dev = 0, lds_max = 65536;
