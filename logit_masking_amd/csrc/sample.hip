@@ -137,55 +137,46 @@ __device__ inline void wave_argmax(double &v, int &i) {
     i = bi;
 }
 
-// Lane l holds the 32 ids c*2048 + 32l + j (j = 0..31): 64 (bf16) or 128
-// (float32) contiguous bytes of the row, and their 32 mask bits as one
-// dword.  Group g = ids 8g .. 8g + 7 of the lane, mask byte g.
+// Lane l holds, in group g = 0..3, the ids c*2048 + g*512 + 8l + j (j =
+// 0..7): every load instruction covers a contiguous 1 KB (bf16) or 2 KB
+// (float32, two instructions per group) of the row, and group g's mask
+// bits are the byte c*256 + 64g + l of the row's mask, one byte load per
+// group, also contiguous across the lanes.
 template <int DT>
 struct ChunkRegs {
     uint32_t d[DT == 1 ? 16 : 32];
-    uint32_t mw;
+    uint32_t mb[4];
 };
 
-// Bounds-checked load (the row's partial last chunk, or rows whose storage
-// is not 16-byte aligned): ids past V read as 0 with their mask bits clear.
+// Bounds-checked load (rows whose storage is not 16-byte aligned): ids past
+// V read as 0 with their mask bits clear.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DT> &R, const void *logits, size_t rowbase,
                                            const uint8_t *mrow, int V, int c, int lane) {
-    const int e0 = c * kChunk + lane * 32;
-    uint32_t mw = 0;
 #pragma unroll
-    for (int b = 0; b < 4; b++)
-        if (e0 + 8 * b < V) mw |= (uint32_t)mrow[(e0 >> 3) + b] << (8 * b);
-    if (e0 + 32 > V) mw &= (e0 >= V) ? 0u : ((1u << (V - e0)) - 1u);
-    R.mw = mw;
-    if (VEC && e0 + 32 <= V) {
-        constexpr int kVec = DT == 1 ? 4 : 8;  // 16-byte loads per lane
+    for (int g = 0; g < 4; g++) {
+        const int e0 = c * kChunk + g * 512 + lane * 8;
+        R.mb[g] = (e0 < V) ? mrow[e0 >> 3] : 0u;
+        if (e0 + 8 > V) R.mb[g] &= (e0 >= V) ? 0u : ((1u << (V - e0)) - 1u);
 #pragma unroll
-        for (int k = 0; k < kVec; k++) {
-            const uint4 v = DT == 1 ? *(const uint4 *)((const uint16_t *)logits + rowbase + e0 + 8 * k)
-                                    : *(const uint4 *)((const float *)logits + rowbase + e0 + 4 * k);
-            R.d[4 * k] = v.x; R.d[4 * k + 1] = v.y; R.d[4 * k + 2] = v.z; R.d[4 * k + 3] = v.w;
-        }
-        return;
-    }
-#pragma unroll
-    for (int j = 0; j < 32; j++) {
-        const float x = (e0 + j < V) ? load_logit<DT>(logits, rowbase + e0 + j) : 0.f;
-        if (DT == 1) {
-            const uint32_t u = __float_as_uint(x) >> 16;
-            if (j & 1) R.d[j / 2] |= u << 16;
-            else R.d[j / 2] = u;
-        } else {
-            R.d[j] = __float_as_uint(x);
+        for (int j = 0; j < 8; j++) {
+            const float x = (e0 + j < V) ? load_logit<DT>(logits, rowbase + e0 + j) : 0.f;
+            if (DT == 1) {
+                const uint32_t u = __float_as_uint(x) >> 16;
+                if (j & 1) R.d[g * 4 + j / 2] |= u << 16;
+                else R.d[g * 4 + j / 2] = u;
+            } else {
+                R.d[g * 8 + j] = __float_as_uint(x);
+            }
         }
     }
 }
 
-// The row as two buffer resources (logits and mask words): a buffer load past
-// the resource's size returns zeros, so every chunk, the row's partial last
-// one included, is read with the same unguarded vector loads.  The logits'
-// size is rounded up to whole dwords (a dword that holds the last id is read
-// whole, from the dword-aligned row).
+// The row as two buffer resources (logits and mask): a buffer load past the
+// resource's size returns zeros without touching memory, so every chunk, the
+// row's partial last one included, is read with the same unguarded vector
+// loads.  The logits' size is rounded up to whole dwords (a dword that holds
+// the last id is read whole, from the dword-aligned row).
 struct RowBufs {
     __amdgpu_buffer_rsrc_t x, m;
 };
@@ -193,17 +184,23 @@ constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, 
 
 template <int DT>
 __device__ __forceinline__ void load_buf(ChunkRegs<DT> &R, const RowBufs &rb, int c, int lane) {
-    const int e0 = c * kChunk + lane * 32;
-    constexpr int kVec = DT == 1 ? 4 : 8, kEs = DT == 1 ? 2 : 4;
+    constexpr int kEs = DT == 1 ? 2 : 4;
 #pragma unroll
-    for (int k = 0; k < kVec; k++) {
-        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.x, e0 * kEs + 16 * k, 0, 0));
-        R.d[4 * k] = v.x; R.d[4 * k + 1] = v.y; R.d[4 * k + 2] = v.z; R.d[4 * k + 3] = v.w;
+    for (int g = 0; g < 4; g++) {
+        const int e0 = c * kChunk + g * 512 + lane * 8;
+#pragma unroll
+        for (int h = 0; h < (DT == 1 ? 1 : 2); h++) {
+            const uint4 v =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.x, e0 * kEs + 16 * h, 0, 0));
+            uint32_t *d = &R.d[g * (DT == 1 ? 4 : 8) + 4 * h];
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        }
     }
-    R.mw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb.m, e0 >> 3, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+        R.mb[g] = __builtin_amdgcn_raw_buffer_load_b8(rb.m, c * 256 + g * 64 + lane, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t mask_byte(uint32_t mw, int g) { return (mw >> (8 * g)) & 0xFFu; }
 
 
 // max of three floats in one instruction.  fmaxf on values made by bit
@@ -219,7 +216,7 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // sign-extended 1-bit field selects between the value and -inf)
 template <int DT>
 __device__ __forceinline__ float masked_x(const ChunkRegs<DT> &R, int g, int j) {
-    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)R.mw, 8 * g + j, 1);
+    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)R.mb[g], j, 1);
     const uint32_t u = R.d[g * 8 + j];
     return __uint_as_float((sel & u) | (~sel & 0xFF800000u));
 }
@@ -248,7 +245,7 @@ __device__ __forceinline__ void init_pair_lut(uint4 *lut) {
 template <int DT>
 __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4 *lut, float kk, float &m_out,
                                              float &s_out, bool &any_out) {
-    any_out = __any(R.mw);
+    any_out = __any(R.mb[0] | R.mb[1] | R.mb[2] | R.mb[3]);
     m_out = -INFINITY;
     s_out = 0.f;
     if (!any_out) return;
@@ -257,7 +254,7 @@ __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4
 #pragma unroll
     for (int g = 0; g < 4; g++) {
         if (DT == 1) {
-            const uint4 sel = lut[mask_byte(R.mw, g)];
+            const uint4 sel = lut[R.mb[g]];
             const uint32_t sp[4] = {sel.x, sel.y, sel.z, sel.w};
 #pragma unroll
             for (int p = 0; p < 4; p++) {
@@ -280,7 +277,7 @@ __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4
     float s = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; g++) {
-        if (mask_byte(R.mw, g)) {
+        if (R.mb[g]) {
             float sg = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; j++) sg += __builtin_amdgcn_exp2f(__builtin_fmaf(xm[g * 8 + j], kk, -mk));
@@ -490,8 +487,8 @@ __device__ __forceinline__ Top2 top2_slots(const float *v1, const int *i1, const
 }
 
 // Per-wave copy of the best chunk seen so far (bf16 rows): the chunk's logits
-// in id order (4 KB) and its mask words, so the pick inside the chosen chunk
-// reads LDS instead of HBM.
+// in id order (4 KB) and each lane's four mask bytes, so the pick inside the
+// chosen chunk reads LDS instead of HBM.
 constexpr int kStashWords = kChunk / 2;  // bf16 pairs per chunk
 struct Stash {
     uint32_t d[kWaves][kStashWords];
@@ -572,11 +569,12 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         // Chunks stream in groups of four per wave, as straight-line code:
         // three chunks' loads in flight, each chunk reduced as soon as its
         // own loads are in, the fourth load issued into the first buffer once
-        // it is free.  Loads take chunk indices clamped into the row (a wave
-        // with fewer chunks re-reads one, from cache), so every path issues
-        // the same loads and the compiler's waits count exactly the loads
-        // behind each chunk.  Rows whose storage is not 16-byte aligned are
-        // read one chunk at a time with bounds-checked loads instead.
+        // it is free.  A wave with fewer chunks still issues every load, for
+        // the chunk one past the row's last (wholly outside both buffer
+        // resources: zeros, no memory traffic), so every path issues the
+        // same loads and the compiler's waits count exactly the loads behind
+        // each chunk.  Rows whose storage is not 16-byte aligned are read one
+        // chunk at a time with bounds-checked loads instead.
         const int Kf = VEC ? K : 0;  // chunks read through buffer loads
         RowBufs rb;
         rb.x = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)logits + rowbase * (DT == 1 ? 2 : 4)), (short)0,
@@ -586,13 +584,18 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         // from regrouping loads across chunks, which would make the first
         // chunk wait for the others)
         auto load = [&](ChunkRegs<DT> &R, int cc) {
-            load_buf<DT>(R, rb, min(cc, Kf - 1), lane);
+            load_buf<DT>(R, rb, min(cc, Kf), lane);
             __builtin_amdgcn_sched_barrier(0);
         };
-        // mask bits of this lane's ids past V in the last chunk (a caller's
+        // clears the mask bits of ids past V in the last chunk (a caller's
         // mask may carry set bits there)
-        const int tail_ids = V - ((K - 1) * kChunk + lane * 32);
-        const uint32_t tail_mw = tail_ids >= 32 ? ~0u : tail_ids <= 0 ? 0u : ((1u << tail_ids) - 1u);
+        auto clear_tail = [&](ChunkRegs<DT> &R) {
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int n = V - ((K - 1) * kChunk + g * 512 + lane * 8);
+                R.mb[g] &= n >= 8 ? 0xFFu : n <= 0 ? 0u : ((1u << n) - 1u);
+            }
+        };
         if (DT == 1) init_pair_lut(lut);
         if (stash && lane == 0) st->c[wave] = -1;
         __syncthreads();  // the mask table
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         float best = -INFINITY;
         const float invTf = (float)invT;
         auto process = [&](ChunkRegs<DT> &R, int cc) {
-            if (VEC && cc == K - 1) R.mw &= tail_mw;
+            if (VEC && cc == K - 1) clear_tail(R);
             float m, s;
             bool any;
             reduce_chunk<DT>(R, lut, kk, m, s, any);
@@ -640,10 +643,10 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             if (score > best) {
                 best = score;
 #pragma unroll
-                for (int k = 0; k < 4; k++)
-                    *(uint4 *)&st->d[wave][lane * 16 + k * 4] =
-                        make_uint4(R.d[k * 4], R.d[k * 4 + 1], R.d[k * 4 + 2], R.d[k * 4 + 3]);
-                st->mb[wave][lane] = R.mw;
+                for (int g = 0; g < 4; g++)
+                    *(uint4 *)&st->d[wave][g * 256 + lane * 4] =
+                        make_uint4(R.d[g * 4], R.d[g * 4 + 1], R.d[g * 4 + 2], R.d[g * 4 + 3]);
+                st->mb[wave][lane] = R.mb[0] | R.mb[1] << 8 | R.mb[2] << 16 | R.mb[3] << 24;
                 if (lane == 0) st->c[wave] = cc;
             }
         };
@@ -797,7 +800,8 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             xq[1] = __uint_as_float(dw.x & 0xFFFF0000u);
             xq[2] = __uint_as_float(dw.y << 16);
             xq[3] = __uint_as_float(dw.y & 0xFFFF0000u);
-            mb4 = (st->mb[ws][t >> 3] >> ((4 * t) & 31)) & 15u;
+            const int li = 4 * t;
+            mb4 = (st->mb[ws][(li & 511) >> 3] >> (8 * (li >> 9) + (li & 7))) & 15u;
         } else {
 #pragma unroll
             for (int j = 0; j < 4; j++)
