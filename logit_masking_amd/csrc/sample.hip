@@ -110,6 +110,29 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     asm(CG_DPP_WAVE_REDUCE("v_add_f32_dpp") : "+v"(v));
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+__device__ __forceinline__ int wave_min_i_fast(int v) {
+    asm(CG_DPP_WAVE_REDUCE("v_min_i32_dpp") : "+v"(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Wave max of a double: rounding to float is monotone, so the lanes that
+// hold the double max hold the float max; a float max picks the candidate
+// lanes and the exact max is taken among them (nearly always one lane).
+__device__ __forceinline__ double wave_max_d_fast(double v) {
+    const float f = (float)v;
+    const float fm = wave_max_f(f);
+    if (fm == -INFINITY) return -INFINITY;
+    uint64_t cand = __ballot(f == fm);
+    double best = -INFINITY;
+    while (cand) {
+        const int l = __builtin_ctzll(cand);
+        cand &= cand - 1;
+        const long long u = ((long long)__builtin_amdgcn_readlane((int)(__double_as_longlong(v) >> 32), l) << 32) |
+                            (unsigned)__builtin_amdgcn_readlane((int)__double_as_longlong(v), l);
+        best = fmax(best, __longlong_as_double(u));
+    }
+    return best;
+}
 
 // argmax of (value, index): larger value, then lower index; index -1 = none
 __device__ inline void arg_better(double &v, int &i, double ov, int oi) {
@@ -418,6 +441,16 @@ __device__ __forceinline__ void top2_rows(Top2 &a) {
     top2_step<kRowRor4>(a);
     top2_step<kRowRor8>(a);
 }
+// The same from two wave maxes: the best value, the lowest index holding it,
+// then the best of everything else.
+__device__ __forceinline__ Top2 top2_wave_fast(const Top2 &a) {
+    Top2 r;
+    r.v1 = wave_max_f(a.v1);
+    r.i1 = wave_min_i_fast((a.i1 >= 0 && a.v1 == r.v1) ? a.i1 : 0x7FFFFFFF);
+    if (r.i1 == 0x7FFFFFFF) r.i1 = -1;
+    r.v2 = wave_max_f(a.i1 == r.i1 ? a.v2 : a.v1);
+    return r;
+}
 __device__ __forceinline__ Top2 top2_wave(Top2 a) {
     top2_rows(a);
     Top2 r;
@@ -715,19 +748,25 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
                     lsum += __builtin_amdgcn_exp2f((float)((l - lmax) * kLog2ed));
                 }
             }
-            const double L = wave_max_d(lmax);
+            const double L = wave_max_d_fast(lmax);
             const float t =
                 wave_sum_f(lmax > -INFINITY ? lsum * __builtin_amdgcn_exp2f((float)((lmax - L) * kLog2ed)) : 0.f);
             if (lane == 0) wdec.lse_all = L > -INFINITY ? L + kLn2d * (double)__builtin_amdgcn_logf(t) : -INFINITY;
         } else if (wave == 1) {
-            double mv = -INFINITY;
+            float mv = -INFINITY;
             int mc = -1;
-            for (int cc = lane; cc < K; cc += 64)
-                if (ci[cc].any) arg_better(mv, mc, (double)ci[cc].m, cc);
-            wave_argmax(mv, mc);
+            for (int cc = lane; cc < K; cc += 64) {
+                const ChunkInfo x = ci[cc];
+                if (x.any && x.m > mv) {  // chunks in increasing order: ties keep the lowest
+                    mv = x.m;
+                    mc = cc;
+                }
+            }
+            const float m = wave_max_f(mv);
+            const int c = wave_min_i_fast((mc >= 0 && mv == m) ? mc : 0x7FFFFFFF);
             if (lane == 0) {
-                wdec.mv = (float)mv;
-                wdec.mc = mv > -INFINITY ? mc : -1;  // allowed tokens all at -inf: nothing to draw
+                wdec.mv = m;
+                wdec.mc = m > -INFINITY ? c : -1;  // allowed tokens all at -inf: nothing to draw
             }
         } else if (!greedy) {
             Top2d cs{-INFINITY, -INFINITY, -1};
@@ -735,11 +774,15 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
                 const double l = lmass(ci[cc]);
                 if (l > -INFINITY) top2d_merge(cs, l + (double)ci[cc].g, cc, -INFINITY);
             }
-            cs = top2d_wave(cs);
+            // best score, the lowest chunk holding it, the best of the rest
+            const double v1 = wave_max_d_fast(cs.v1);
+            int c1 = wave_min_i_fast((cs.i1 >= 0 && cs.v1 == v1) ? cs.i1 : 0x7FFFFFFF);
+            if (c1 == 0x7FFFFFFF) c1 = -1;
+            const double v2 = wave_max_d_fast(cs.i1 == c1 ? cs.v2 : cs.v1);
             if (lane == 0) {
-                wdec.c1 = cs.i1;
-                wdec.cs1 = cs.v1;
-                wdec.cs2 = cs.v2;
+                wdec.c1 = c1;
+                wdec.cs1 = v1;
+                wdec.cs2 = v2;
             }
         }
     }
@@ -759,6 +802,9 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     dc.chosen = greedy ? wdec.mc : wdec.c1;
     dc.exact_chunk = !greedy && wdec.c1 >= 0 && !(wdec.cs1 - wdec.cs2 > kContendChunk);
     dc.cs1 = wdec.cs1;
+    // fused: the row's state is fetched now, its round trip hidden by the pick
+    cg_state row_state{};
+    if (fuse && threadIdx.x == 0) row_state = adv.states[r];
     do {
     if (dc.mc < 0) break;  // nothing allowed: a finished row
     if (dc.exact_chunk) {
@@ -826,7 +872,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         for (int j = 3; j >= 0; j--)
             if (((mb4 >> j) & 1u) && xq[j] == dc.mv) im = e + j;
         if (tok) {
-            im = wave_min_i(im);
+            im = wave_min_i_fast(im);
             if (lane == 0) sl[2].i[wave] = im;
         }
         __syncthreads();
@@ -851,7 +897,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
 #pragma unroll
         for (int j = 0; j < 4; j++)
             if ((mb4 >> j) & 1u) top2_merge(ts, xq[j] * it + gumbel32(wq[j]), e + j, -INFINITY);
-        ts = top2_wave(ts);
+        ts = top2_wave_fast(ts);
         if (lane == 0) {
             sl[2].f[wave] = ts.v1;
             sl[2].h[wave] = ts.v2;
@@ -909,7 +955,6 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     out_id[r] = pick;
     out_lp[r] = pick_lp;
     if (!fuse) return;
-    cg_state row_state = adv.states[r];  // loaded with the token bytes: one round trip
     uint32_t words[kMaxTokenLen / 4];
     uint32_t n = 0;
 #pragma unroll
