@@ -534,8 +534,10 @@ __global__ __launch_bounds__(kWalkThreads) void k_fill_walk(FillArgs a) {
     uint32_t *prefix = (uint32_t *)(lds + a.comb_len);
     const WalkConsts &k = a.k;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // the table is staged while the first block's tile counts are scanned
-    // (nearly every workgroup has tiles to walk)
+    // the first row block's first tile count of this thread is fetched
+    // before the table, so that the two round trips overlap
+    const int nb0 = min(kWalkRowBlock, a.B), per0 = (nb0 + kWalkThreads - 1) / kWalkThreads;
+    const uint32_t first_n = tid * per0 < nb0 ? a.plan[(size_t)(tid * per0) * a.plan_stride] : 0u;
     stage_table(lds_comb, a.comb, a.comb_len);
     for (int rb = 0; rb < a.B; rb += kWalkRowBlock) {
         const int nb = min(kWalkRowBlock, a.B - rb);
@@ -544,7 +546,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_fill_walk(FillArgs a) {
         const int r0 = min(nb, tid * per), r1 = min(nb, r0 + per);
         uint32_t sum = 0;
         for (int i = r0; i < r1; i++) {
-            const uint32_t n = a.plan[(size_t)(rb + i) * a.plan_stride];
+            const uint32_t n = (rb == 0 && i == r0) ? first_n : a.plan[(size_t)(rb + i) * a.plan_stride];
             prefix[i] = n;  // the count, until the scan below replaces it
             sum += n;
         }
