@@ -1,8 +1,11 @@
 """Benchmark of the constrained-decoding hot path on one MI355X.
 
-A step is one pass of the whole path over the batch: fill_bitmask, then
-mask_softmax_sample + advance in one launch (cg_sample_advance; --separate
-runs cg_apply_mask_sample and cg_advance as two launches).  Workload: the tool-call grammar (8 tools),
+A step is one pass of the whole path over the batch: mask_softmax_sample +
+advance + the next step's fill_bitmask, as cg_sample_advance_fill (one
+launch samples, commits and plans each row's next mask; a second walks the
+listed token tiles).  --plain-fill runs cg_fill_bitmask then
+cg_sample_advance; --separate runs cg_fill_bitmask, cg_apply_mask_sample and
+cg_advance as three calls.  Workload: the tool-call grammar (8 tools),
 vocabulary 128,256, batch 256, bf16 N(0, 3^2) logits, T = 0.7 Philox
 Gumbel sampling, a 256-step trajectory from the start state (the 256-token
 bench cap of "Constrained decoding", "What it is worth"), engine cap 2048.
@@ -33,13 +36,17 @@ WORKLOADS = {
     6: "text with calc spans, vocab 128256, batch 256, bf16 N(0,9) logits, T=0.7 Philox two-level Gumbel",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_sample_hbm_traffic_toolcall_v128k_b256.md")
-KERNEL_SRC = os.path.join(ROOT, "logit_masking_amd", "csrc", "sample.hip")
+# the sources of the measured launch: the sampler and the plan it runs
+KERNEL_SRCS = [os.path.join(ROOT, "logit_masking_amd", "csrc", f) for f in ("sample.hip", "fill_plan.hpp")]
 
 
 def kernel_source_sha():
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def recorded_traffic():
@@ -53,7 +60,7 @@ def recorded_traffic():
         if line.startswith("- ") and ": " in line:
             k, v = line[2:].split(": ", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("sample.hip sha256") != kernel_source_sha():
+    if vals.get("sample.hip + fill_plan.hpp sha256") != kernel_source_sha():
         return None
     try:
         return float(vals["hbm bytes per launch"])
@@ -463,6 +470,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="cg_apply_mask_sample and cg_advance as two launches instead of cg_sample_advance")
+    ap.add_argument("--plain-fill", action="store_true",
+                    help="cg_fill_bitmask + cg_sample_advance per step, instead of cg_sample_advance_fill (the next "
+                         "step's mask planned in the sampler's launch, then walked)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 64 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--config", type=int, default=CONFIG,
@@ -522,6 +532,21 @@ def main():
 
     def step(s, ev=None):
         ids = ids_hist[s]
+        if fused_fill:
+            # this step's mask was left by the previous call (the first by
+            # cg_fill_bitmask); timed apart, the call's two launches are made
+            # as two calls with events between them
+            if ev is None:
+                g.sample_advance_fill(pool[s % npool], mask, temp, seed, steps, ws, ids, lp, st, status, fws, stream)
+                return
+            ev[0].record(stream)
+            g.sample_advance_fill(pool[s % npool], mask, temp, seed, steps, ws, ids, lp, st, status, fws, stream,
+                                  split=True)
+            ev[1].record(stream)
+            g.fill_walk(st, mask, fws, stream)
+            ev[2].record(stream)
+            ev[3].record(stream)
+            return
         if ev is not None:
             ev[0].record(stream)
         g.fill_bitmask(st, mask, fws, stream)
@@ -540,11 +565,14 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    fused_fill = not (args.plain_fill or args.separate)
+    if fused_fill:
+        g.fill_bitmask(st, mask, fws, stream)
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
     # the timed region: K steps between two events, nothing else on the stream
-    st0, steps0 = st.clone(), steps.clone()
+    st0, steps0, mask0 = st.clone(), steps.clone(), mask.clone()
     start_ev = torch.cuda.Event(enable_timing=True)
     end_ev = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -563,13 +591,18 @@ def main():
     # pair around every launch: per-kernel durations on the launch stream
     st.copy_(st0)
     steps.copy_(steps0)
+    mask.copy_(mask0)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
         step(args.warmup + k, evs[k])
     torch.cuda.synchronize()
-    fill_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    samp_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    if fused_fill:  # [0, 1): sample + advance + next plan; [1, 2): the walk
+        samp_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        fill_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    else:
+        fill_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        samp_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     adv_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     assert np.array_equal(steps.cpu().numpy(), st_h), "replay diverged from the timed trajectory"
@@ -579,11 +612,16 @@ def main():
     sample_bytes = B * V * es + B * g.W * 8 + B * 8
     if not args.separate:
         sample_bytes += B * (2 * 24 + 2 * 4 + 4)
+    if fused_fill:
+        sample_bytes += B * g.W * 8  # the next mask's words, written once by the plan
     sample_gbps = sample_bytes / (samp_ms.mean() * 1e-3) / 1e9
     fill_checks = B * V / (fill_ms.mean() * 1e-3)
     dominant = "fill_bitmask" if fill_ms.mean() >= samp_ms.mean() else "mask_softmax_sample"
+    kernel_name = ("k_sample (mask_softmax_sample)" if args.separate
+                   else "k_sample (mask_softmax_sample + advance, one launch)" if not fused_fill
+                   else "k_sample (mask_softmax_sample + advance + the next mask's plan, one launch)")
     roofline = {
-        "kernel": "k_sample (mask_softmax_sample" + (")" if args.separate else " + advance, one launch)"),
+        "kernel": kernel_name,
         "bound": "hbm",
         "achieved": round(sample_gbps, 1),
         "peak": HBM_PEAK_GBPS,
@@ -606,7 +644,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[cfg] + f", {args.steps}-step trajectory, engine cap 2048",
                    "batch": B, "vocab": V, "logits_pool": npool},
-        "fill_token_checks_per_s": round(fill_checks, 1),
+        "step": ("cg_sample_advance_fill (sample + advance + next plan; walk)" if fused_fill
+                 else "cg_fill_bitmask; cg_apply_mask_sample; cg_advance" if args.separate
+                 else "cg_fill_bitmask; cg_sample_advance"),
+        "fill_token_checks_per_s": None if fused_fill else round(fill_checks, 1),
         "masked_sample_GBps": round(sample_gbps, 1),
         "masked_sample_frac_hbm": round(sample_gbps / HBM_PEAK_GBPS, 4),
         "us_per_step": {"mean": round(1e3 * ms_per_step, 2), "p50": round(1e3 * pct(step_ms, 50), 2),

@@ -14,6 +14,8 @@
  *   cg_apply_mask_sample masked softmax + greedy / Gumbel-max pick (device)
  *   cg_advance           walk the chosen tokens, update rows (device)
  *   cg_sample_advance    the last two in one launch (device)
+ *   cg_sample_advance_fill  the same, then the next step's bitmask (device)
+ *   cg_sample_advance_plan, cg_fill_walk  its two launches, one call each
  *   cg_fill_draft        masks along each row's k-token draft (device)
  *   cg_force_bytes       engine-written bytes (an evaluated result) (device)
  *   cg_eval_calc         evaluate a calc span (host)
@@ -285,6 +287,44 @@ int cg_sample_advance(const cg_grammar *g, const void *d_logits, int32_t dtype, 
                       const uint64_t *d_mask, int32_t words_per_row, const float *d_temperature,
                       const uint64_t *d_seed, int32_t *d_step, void *d_workspace, int32_t *d_out_ids,
                       float *d_out_logprob, cg_state *d_states, int32_t *d_status, void *stream);
+
+/*
+ * One decode step and the next step's bitmask: cg_sample_advance (same
+ * arguments, same results), whose workgroups then plan each row's next mask
+ * from the state they have just committed -- the base words and the token
+ * tiles worth walking, the first part of cg_fill_bitmask -- followed by the
+ * walk that completes it (two launches on `stream`).  The mask depends on
+ * the automaton's state alone, so it is begun the moment the state is known
+ * ("Evaluator aware decoding", "Why isn't this in production APIs yet?").
+ * d_mask is read as this step's mask and rewritten in place: afterwards (in
+ * stream order) it holds exactly what cg_fill_bitmask writes for the updated
+ * states (words beyond ceil(vocab_size / 64) untouched).  d_fill_workspace:
+ * as for cg_fill_bitmask (cg_fill_workspace_bytes(g, batch) bytes, 16-byte
+ * aligned, no initialisation, scratch after the call).  The first step of a
+ * batch takes its mask from cg_fill_bitmask.
+ */
+int cg_sample_advance_fill(const cg_grammar *g, const void *d_logits, int32_t dtype, int32_t batch,
+                           int64_t row_stride, uint64_t *d_mask, int32_t words_per_row, const float *d_temperature,
+                           const uint64_t *d_seed, int32_t *d_step, void *d_workspace, int32_t *d_out_ids,
+                           float *d_out_logprob, cg_state *d_states, int32_t *d_status, void *d_fill_workspace,
+                           void *stream);
+
+/*
+ * The two launches of cg_sample_advance_fill as calls of their own (so that
+ * a caller may time them apart, or put other work between them): the first
+ * (same arguments) samples, commits and plans, leaving d_mask holding the
+ * next masks' base words and d_fill_workspace the token tiles to walk; the
+ * second completes d_mask from those (the arguments of cg_fill_bitmask, with
+ * the updated d_states and the same workspace).  Nothing may use d_mask or
+ * the workspace between the two.
+ */
+int cg_sample_advance_plan(const cg_grammar *g, const void *d_logits, int32_t dtype, int32_t batch,
+                           int64_t row_stride, uint64_t *d_mask, int32_t words_per_row, const float *d_temperature,
+                           const uint64_t *d_seed, int32_t *d_step, void *d_workspace, int32_t *d_out_ids,
+                           float *d_out_logprob, cg_state *d_states, int32_t *d_status, void *d_fill_workspace,
+                           void *stream);
+int cg_fill_walk(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
+                 int32_t words_per_row, void *d_workspace, void *stream);
 
 /*
  * Walk d_token_ids[r] for every row: -1 is a no-op (CG_ROW_NOOP).  A token

@@ -22,7 +22,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # Symbols the C ABI (include/cg.h) exports.
 EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
-           "cg_fill_bitmask", "cg_sample_advance", "cg_force_bytes", "cg_eval_calc", "cg_draft_workspace_bytes",
+           "cg_fill_bitmask", "cg_sample_advance", "cg_sample_advance_fill",
+           "cg_sample_advance_plan", "cg_fill_walk", "cg_force_bytes", "cg_eval_calc", "cg_draft_workspace_bytes",
            "cg_fill_draft", "cg_contract_model_spec", "cg_contract_reverse", "cg_cache_stats", "cg_cache_clear",
            "cg_eval_strop",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
@@ -84,9 +85,13 @@ def lib():
         L.cg_fill_draft.argtypes = [vp, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]
         L.cg_eval_calc.argtypes = [vp, sz, ctypes.POINTER(ctypes.c_int64)]
         L.cg_sample_advance.argtypes = [vp, vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.cg_sample_advance_fill.argtypes = [vp, vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.cg_sample_advance_plan.argtypes = [vp, vp, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.cg_fill_walk.argtypes = [vp, vp, i32, vp, i32, vp, vp]
         L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
         L.cg_last_error.restype = ctypes.c_char_p
         for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask", "cg_sample_advance",
+                     "cg_sample_advance_fill", "cg_sample_advance_plan", "cg_fill_walk",
                      "cg_force_bytes", "cg_eval_calc", "cg_fill_draft", "cg_contract_model_spec",
                      "cg_contract_reverse",
                      "cg_apply_mask_sample", "cg_advance", "cg_try_input"):
@@ -225,6 +230,54 @@ class Grammar:
         _check(lib().cg_sample_advance(self._h, _ptr(logits), dt, B, logits.stride(0), _ptr(mask), mask.shape[1],
                                        _ptr(temperature), _ptr(seed), _ptr(steps), _ptr(workspace), _ptr(out_ids),
                                        _ptr(out_logprob), _ptr(states), _ptr(status), _stream(stream)))
+
+    def sample_advance_fill(self, logits, mask, temperature, seed, steps, workspace, out_ids, out_logprob, states,
+                            status, fill_workspace=None, stream=None, split=False):
+        """cg_sample_advance_fill: sample_advance, then the next step's mask
+        written over `mask` (fill_workspace: from new_fill_workspace(B); None
+        allocates one for this call).  split=True makes the first of its two
+        launches only (cg_sample_advance_plan); fill_walk completes the mask."""
+        import torch
+        if logits.dtype == torch.float32:
+            dt = DTYPE_F32
+        elif logits.dtype == torch.bfloat16:
+            dt = DTYPE_BF16
+        else:
+            raise ValueError("logits must be float32 or bfloat16")
+        if not logits.is_cuda or logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[1] < self.V:
+            raise ValueError("logits must be a 2-D device tensor [B, >= vocab] with unit column stride")
+        B = logits.shape[0]
+        _dev(mask, torch.int64, "mask", 2)
+        _dev(temperature, torch.float32, "temperature", 1)
+        _dev(seed, torch.int64, "seed", 1)
+        _dev(states, torch.uint8, "states", 2)
+        for t, n in ((steps, "steps"), (out_ids, "out_ids"), (status, "status")):
+            _dev(t, torch.int32, n, 1)
+        _dev(out_logprob, torch.float32, "out_logprob", 1)
+        if workspace.numel() * workspace.element_size() < sample_workspace_bytes(B, self.V):
+            raise ValueError("workspace too small")
+        for t, n in ((mask, "mask"), (temperature, "temperature"), (seed, "seed"), (steps, "steps"),
+                     (out_ids, "out_ids"), (out_logprob, "out_logprob"), (states, "states"), (status, "status")):
+            if t.shape[0] < B:
+                raise ValueError(f"{n} has fewer rows than logits")
+        if fill_workspace is None:
+            fill_workspace = self.new_fill_workspace(B)
+        elif fill_workspace.numel() * fill_workspace.element_size() < self.fill_workspace_bytes(B):
+            raise ValueError("fill workspace too small")
+        fn = lib().cg_sample_advance_plan if split else lib().cg_sample_advance_fill
+        _check(fn(self._h, _ptr(logits), dt, B, logits.stride(0), _ptr(mask), mask.shape[1], _ptr(temperature),
+                  _ptr(seed), _ptr(steps), _ptr(workspace), _ptr(out_ids), _ptr(out_logprob), _ptr(states),
+                  _ptr(status), _ptr(fill_workspace), _stream(stream)))
+
+    def fill_walk(self, states, mask, workspace, stream=None):
+        """cg_fill_walk: the second launch of sample_advance_fill (after
+        split=True, with the same mask and fill workspace)."""
+        import torch
+        _dev(states, torch.uint8, "states", 2)
+        _dev(mask, torch.int64, "mask", 2)
+        B = states.shape[0]
+        _check(lib().cg_fill_walk(self._h, _ptr(states), B, _ptr(mask), mask.shape[1], _ptr(workspace),
+                                  _stream(stream)))
 
     def advance(self, states, ids, steps, status, stream=None):
         import torch

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "cg_internal.hpp"
+#include "fill_plan.hpp"
 
 namespace cg {
 const char *last_error();
@@ -28,7 +29,10 @@ size_t fill_lds_bytes(const cg_grammar *g, int items_per_row);
 int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, const uint64_t *mask, int wpr,
                   const float *temp, const uint64_t *seed, const int32_t *step, void *ws, int32_t *out_id,
                   float *out_lp, const cg_grammar *g, cg_state *states, int32_t *steps_rw, int32_t *status,
-                  hipStream_t st);
+                  hipStream_t st, const FillArgs *plan = nullptr);
+FillArgs make_fill_args(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws);
+int fill_check(const cg_grammar *g, int B);
+int launch_fill_walk(const cg_grammar *g, const FillArgs &a, hipStream_t st);
 }  // namespace cg
 
 using namespace cg;
@@ -788,6 +792,70 @@ int cg_sample_advance(const cg_grammar *g, const void *d_logits, int32_t dtype, 
     return launch_sample(d_logits, dtype, batch, g->V, row_stride, d_mask, words_per_row, d_temperature, d_seed,
                          d_step, d_workspace, d_out_ids, d_out_logprob, g, d_states, d_step, d_status,
                          (hipStream_t)stream);
+}
+
+namespace {
+int sample_advance_next(const cg_grammar *g, const void *d_logits, int32_t dtype, int32_t batch, int64_t row_stride,
+                        uint64_t *d_mask, int32_t words_per_row, const float *d_temperature, const uint64_t *d_seed,
+                        int32_t *d_step, void *d_workspace, int32_t *d_out_ids, float *d_out_logprob,
+                        cg_state *d_states, int32_t *d_status, void *d_fill_workspace, void *stream, bool walk) {
+    if (!on_device(g)) return arg_error("grammar has no device tables");
+    if (dtype != 0 && dtype != 1) return arg_error("dtype must be 0 (float32) or 1 (bfloat16)");
+    if (batch < 0) return arg_error("bad batch");
+    if (row_stride < g->V) return arg_error("row_stride < vocab_size");
+    if (words_per_row < (g->V + 63) / 64) return arg_error("words_per_row < ceil(vocab_size / 64)");
+    if (batch == 0) return CG_OK;
+    if (!d_logits || !d_mask || !d_temperature || !d_seed || !d_step || !d_out_ids || !d_out_logprob || !d_states ||
+        !d_status)
+        return arg_error("NULL device pointer");
+    if (sample_workspace_bytes(batch, g->V) > 0 && (!d_workspace || (uintptr_t)d_workspace % 16))
+        return arg_error("workspace must be a 16-byte aligned device buffer");
+    if (!d_fill_workspace || (uintptr_t)d_fill_workspace % 16)
+        return arg_error("fill workspace must be a 16-byte aligned device buffer of cg_fill_workspace_bytes bytes");
+    const int chk = fill_check(g, batch);
+    if (chk != CG_OK) return chk;
+    hipStream_t st = (hipStream_t)stream;
+    const FillArgs a = make_fill_args(g, d_states, batch, d_mask, words_per_row, d_fill_workspace);
+    const int rc = launch_sample(d_logits, dtype, batch, g->V, row_stride, d_mask, words_per_row, d_temperature,
+                                 d_seed, d_step, d_workspace, d_out_ids, d_out_logprob, g, d_states, d_step, d_status,
+                                 st, &a);
+    if (rc != CG_OK || !walk) return rc;
+    return launch_fill_walk(g, a, st);
+}
+}  // namespace
+
+int cg_sample_advance_fill(const cg_grammar *g, const void *d_logits, int32_t dtype, int32_t batch,
+                           int64_t row_stride, uint64_t *d_mask, int32_t words_per_row, const float *d_temperature,
+                           const uint64_t *d_seed, int32_t *d_step, void *d_workspace, int32_t *d_out_ids,
+                           float *d_out_logprob, cg_state *d_states, int32_t *d_status, void *d_fill_workspace,
+                           void *stream) {
+    return sample_advance_next(g, d_logits, dtype, batch, row_stride, d_mask, words_per_row, d_temperature, d_seed,
+                               d_step, d_workspace, d_out_ids, d_out_logprob, d_states, d_status, d_fill_workspace,
+                               stream, true);
+}
+
+int cg_sample_advance_plan(const cg_grammar *g, const void *d_logits, int32_t dtype, int32_t batch,
+                           int64_t row_stride, uint64_t *d_mask, int32_t words_per_row, const float *d_temperature,
+                           const uint64_t *d_seed, int32_t *d_step, void *d_workspace, int32_t *d_out_ids,
+                           float *d_out_logprob, cg_state *d_states, int32_t *d_status, void *d_fill_workspace,
+                           void *stream) {
+    return sample_advance_next(g, d_logits, dtype, batch, row_stride, d_mask, words_per_row, d_temperature, d_seed,
+                               d_step, d_workspace, d_out_ids, d_out_logprob, d_states, d_status, d_fill_workspace,
+                               stream, false);
+}
+
+int cg_fill_walk(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
+                 int32_t words_per_row, void *d_workspace, void *stream) {
+    if (!on_device(g)) return arg_error("grammar has no device tables");
+    if (batch < 0 || (batch > 0 && (!d_states || !d_mask))) return arg_error("bad states / mask / batch");
+    if (words_per_row < (g->V + 63) / 64) return arg_error("words_per_row < ceil(vocab_size / 64)");
+    if (batch == 0) return CG_OK;
+    if (!d_workspace || (uintptr_t)d_workspace % 16)
+        return arg_error("workspace must be a 16-byte aligned device buffer of cg_fill_workspace_bytes bytes");
+    const int chk = fill_check(g, batch);
+    if (chk != CG_OK) return chk;
+    return launch_fill_walk(g, make_fill_args(g, d_states, batch, d_mask, words_per_row, d_workspace),
+                            (hipStream_t)stream);
 }
 
 int cg_advance(const cg_grammar *g, cg_state *d_states, int32_t batch, const int32_t *d_token_ids, int32_t *d_step,

@@ -12,6 +12,7 @@
 #include <algorithm>
 
 #include "cg_internal.hpp"
+#include "fill_plan.hpp"
 
 namespace cg {
 
@@ -559,19 +560,24 @@ constexpr int kStageRegs = 4;
 // one barrier every wave merges the 16 wave summaries into the row's decision
 // and the workgroup picks the token inside the chosen chunk.  No state crosses
 // workgroups, so no device-wide fence is ever needed.
+// plan_next (with the fused advance): after the commit, the workgroup plans
+// its row's next mask from the committed state (fill_plan.hpp), rewriting
+// the row's mask words it has finished reading (mask is not restrict).
 template <int DT, bool VEC>
 __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
-                                                 const uint64_t *__restrict__ mask, int words_per_row,
+                                                 const uint64_t *mask, int words_per_row,
                                                  const float *__restrict__ temp, const uint64_t *__restrict__ seed,
                                                  const int32_t *__restrict__ step, int K, int use_stash,
                                                  int32_t *__restrict__ out_id, float *__restrict__ out_lp,
-                                                 AdvanceArgs adv) {
+                                                 AdvanceArgs adv, FillArgs pa, int plan_next) {
     extern __shared__ uint64_t dyn[];
     ChunkInfo *ci = (ChunkInfo *)dyn;
     Stash *st = (Stash *)((char *)dyn + stash_offset(K));  // valid when use_stash (bf16 only)
     __shared__ Slots sl[4];
     __shared__ uint4 lut[256];
     __shared__ RowDecision wdec;
+    __shared__ PlanShared psh;
+    __shared__ cg_state next_state;
     // the wave index through readfirstlane: the compiler then knows it (and
     // every chunk index derived from it) is uniform, and branches on scalars
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -951,27 +957,36 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     }
     } while (0);
     // ---- epilogue: thread 0 publishes the pick and, fused, commits it ---------
-    if (threadIdx.x != 0) return;
-    out_id[r] = pick;
-    out_lp[r] = pick_lp;
-    if (!fuse) return;
-    uint32_t words[kMaxTokenLen / 4];
-    uint32_t n = 0;
+    if (threadIdx.x == 0) {
+        out_id[r] = pick;
+        out_lp[r] = pick_lp;
+        if (fuse) {
+            uint32_t words[kMaxTokenLen / 4];
+            uint32_t n = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxTokenLen / 4; j++) words[j] = 0;
-    if (pick >= 0 && pick < adv.V) {
-        n = tok_len(adv.tokinfo[pick]);
+            for (int j = 0; j < kMaxTokenLen / 4; j++) words[j] = 0;
+            if (pick >= 0 && pick < adv.V) {
+                n = tok_len(adv.tokinfo[pick]);
 #pragma unroll
-        for (int j = 0; j < kMaxTokenLen / 4; j++)
-            if (j < adv.nw) words[j] = adv.tokw[(size_t)j * adv.V + pick];
+                for (int j = 0; j < kMaxTokenLen / 4; j++)
+                    if (j < adv.nw) words[j] = adv.tokw[(size_t)j * adv.V + pick];
+            }
+            int stp1 = (int)stp;
+            const int res =
+                commit_token(row_state, stp1, pick, adv.V, n, words, lds_comb, adv.k, adv.gen_cap, adv.forced);
+            if (token_taken(res)) {
+                adv.states[r] = row_state;
+                adv.steps[r] = stp1;
+            }
+            adv.status[r] = res;
+            next_state = row_state;  // unchanged unless the token was taken
+        }
     }
-    int stp1 = (int)stp;
-    const int res = commit_token(row_state, stp1, pick, adv.V, n, words, lds_comb, adv.k, adv.gen_cap, adv.forced);
-    if (token_taken(res)) {
-        adv.states[r] = row_state;
-        adv.steps[r] = stp1;
-    }
-    adv.status[r] = res;
+    if (!plan_next) return;
+    // the next mask of this row, from the committed state; every read of
+    // the row's current mask is done (the pick has been made)
+    __syncthreads();
+    plan_row(pa, r, next_state, lds_comb, psh);
 }
 
 // ---------------------------------------------------------------------------
@@ -986,7 +1001,7 @@ size_t sample_workspace_bytes(int B, int V) {
 int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, const uint64_t *mask, int wpr,
                   const float *temp, const uint64_t *seed, const int32_t *step, void *ws, int32_t *out_id,
                   float *out_lp, const cg_grammar *g, cg_state *states, int32_t *steps_rw, int32_t *status,
-                  hipStream_t st) {
+                  hipStream_t st, const FillArgs *plan) {
     (void)ws;
     if (B == 0) return CG_OK;
     const int K = (V + kChunk - 1) / kChunk;
@@ -1000,7 +1015,8 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         lds_max = 65536;
-    const size_t static_lds = 4 * sizeof(Slots) + 256 * sizeof(uint4) + sizeof(RowDecision) + 256;
+    const size_t static_lds =
+        4 * sizeof(Slots) + 256 * sizeof(uint4) + sizeof(RowDecision) + sizeof(PlanShared) + sizeof(cg_state) + 256;
     const size_t table = g ? (size_t)g->comb_len * 8 : 0;
     // bf16 rows keep each wave's best chunk in LDS when it fits beside the table
     const int use_stash =
@@ -1027,6 +1043,9 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
         adv.gen_cap = g->gen_cap;
         adv.forced = g->dev.forced;
     }
+    static_assert(kWaves * 64 == kPlanThreads, "the plan runs on the sampler's workgroup");
+    const FillArgs pa = plan ? *plan : FillArgs{};
+    const int plan_next = (plan && g) ? 1 : 0;
     const int es = dt == 0 ? 4 : 2;
     const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * es) % 16 == 0);
 #define CG_LAUNCH_SAMPLE(D, VV)                                                                                  \
@@ -1035,7 +1054,7 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) \
             return launch_status("apply_mask_sample (LDS attribute)");                                           \
         hipLaunchKernelGGL((k_sample<D, VV>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask, wpr, \
-                           temp, seed, step, K, use_stash, out_id, out_lp, adv);                                 \
+                           temp, seed, step, K, use_stash, out_id, out_lp, adv, pa, plan_next);              \
     } while (0)
     if (dt == 0) {
         if (vec) CG_LAUNCH_SAMPLE(0, true);
