@@ -87,8 +87,9 @@ def cpu_baseline(ids_hist, B, V, blob, off, budget_s, cfg=CONFIG):
     seeds = W.row_seeds(cfg, B)
     T = W.CONFIGS[cfg]["T"]
     checks = walked = row_steps = 0
-    t_cpu = 0.0
+    t_cpu = t_mask = 0.0
     last = 0
+    t1 = None
     for s in range(ids_hist.shape[0]):
         live = [r for r in range(nrows) if not rows[r].done]
         if not live or t_cpu >= budget_s:
@@ -97,9 +98,15 @@ def cpu_baseline(ids_hist, B, V, blob, off, budget_s, cfg=CONFIG):
         x = logits.float().numpy().astype(np.float64)
         t0 = time.perf_counter()
         words, w = og.mask_rows([rows[r].conf for r in live], [False] * len(live), blob, off, threads)
+        tm = time.perf_counter()
         for k, r in enumerate(live):
             O.sample_row(x[r], O.unpack_mask(words[k], V), T, seeds[r], rows[r].step)
         t_cpu += time.perf_counter() - t0
+        t_mask += tm - t0
+        if s == 20:  # the same masks again on one thread (rows in mixed states by now)
+            u0 = time.perf_counter()
+            og.mask_rows([rows[r].conf for r in live], [False] * len(live), blob, off, 1)
+            t1 = (len(live) * V, time.perf_counter() - u0, tm - t0)
         checks += len(live) * V
         walked += w
         row_steps += len(live)
@@ -116,7 +123,63 @@ def cpu_baseline(ids_hist, B, V, blob, off, budget_s, cfg=CONFIG):
                   f"full-vocabulary mask + float64 two-level sample per row-step; {row_steps} row-steps, "
                   f"{checks} token checks, {walked / max(1, checks):.2f} bytes walked per check, {t_cpu:.1f} s",
         "us_per_row_step": 1e6 * t_cpu / max(1, row_steps),
+        "mask_token_checks_per_s": checks / t_mask if t_mask > 0 else None,
+        "sample_GBps": (row_steps * (2 * V + 8 * ((V + 63) // 64) + 8) / (t_cpu - t_mask) / 1e9
+                        if t_cpu > t_mask else None),
+        "mask_step20_token_checks_per_s": ({"threads": threads, "value": t1[0] / t1[2], "1_thread": t1[0] / t1[1]}
+                                          if t1 and t1[1] > 0 and t1[2] > 0 else None),
+        "nproc": os.cpu_count(),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def state_classes(g, cg, st0, pool, temp, seed, steps, ws, fws, B, V, stream, reps=30):
+    """The fill and the sample timed on two batches of one state class
+    each: every row in the state of the densest live row at the start of
+    the timed region (inside a string, where most tokens may follow) and
+    every row in the sparsest one's (a structural state).  Events on the
+    launch stream around each of `reps` calls; the states are not changed."""
+    import torch
+    mask = torch.empty((B, g.W), dtype=torch.int64, device=st0.device)
+    g.fill_bitmask(st0, mask, fws, stream)
+    torch.cuda.synchronize()
+    bits = np.unpackbits(mask.cpu().numpy().view(np.uint8), axis=1).sum(axis=1)
+    live = np.nonzero(bits > 0)[0]
+    if len(live) == 0:
+        return None
+    picks = {"string_interior": int(live[np.argmax(bits[live])]),
+             "structural": int(live[np.argmin(bits[live])])}
+    ids = torch.empty(B, dtype=torch.int32, device=st0.device)
+    lp = torch.empty(B, dtype=torch.float32, device=st0.device)
+    out = {}
+    for name, r in picks.items():
+        st = st0[r:r + 1].repeat(B, 1).contiguous()
+        g.fill_bitmask(st, mask, fws, stream)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ev[i][0].record(stream)
+            g.fill_bitmask(st, mask, fws, stream)
+            ev[i][1].record(stream)
+            cg.apply_mask_sample(pool[i % len(pool)], mask, temp, seed, steps, ws, ids, lp, stream=stream)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        f = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+        sm = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+        out[name] = {"row": r, "allowed_frac": round(float(bits[r]) / V, 4),
+                     "us_fill": round(float(f.mean()), 2), "us_sample": round(float(sm.mean()), 2)}
+    return out
 
 
 def inject_bench(args):
@@ -666,6 +729,24 @@ def main():
         "table_bytes": info["table_bytes"],
         "roofline": roofline,
     }
+    # a plain device-to-device copy of 256 MiB: what the memory system gives
+    # a stream here, beside the published peak
+    src = torch.empty(128 << 20, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 10 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    out["copy_GBps"] = round(copy_gbps, 1)
+    out["masked_sample_frac_copy"] = round(sample_gbps / copy_gbps, 4)
+    if not args.separate:
+        out["state_classes"] = state_classes(g, cg, st0, pool, temp, seed, steps0, ws, fws, B, V, stream)
     if args.calib_copy:
         src = torch.empty(32 << 20, dtype=torch.int16, device=dev).fill_(1)
         dst = torch.empty_like(src)
