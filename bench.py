@@ -536,6 +536,8 @@ def main():
     ap.add_argument("--plain-fill", action="store_true",
                     help="cg_fill_bitmask + cg_sample_advance per step, instead of cg_sample_advance_fill (the next "
                          "step's mask planned in the sampler's launch, then walked)")
+    ap.add_argument("--no-classes", action="store_true",
+                    help="skip the per-state-class timings (a kernel trace then holds the trajectory's launches only)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 64 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--config", type=int, default=CONFIG,
@@ -745,7 +747,7 @@ def main():
     del src, dst
     out["copy_GBps"] = round(copy_gbps, 1)
     out["masked_sample_frac_copy"] = round(sample_gbps / copy_gbps, 4)
-    if not args.separate:
+    if not (args.separate or args.no_classes):
         out["state_classes"] = state_classes(g, cg, st0, pool, temp, seed, steps0, ws, fws, B, V, stream)
     if args.calib_copy:
         src = torch.empty(32 << 20, dtype=torch.int16, device=dev).fill_(1)

@@ -105,7 +105,6 @@ __device__ __forceinline__ float wave_max_f(float v) {
     asm(CG_DPP_WAVE_REDUCE("v_max_f32_dpp") : "+v"(v));
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-__device__ inline double wave_max_d(double v) { return wave_reduce_d(v, [](double a, double b) { return fmax(a, b); }); }
 __device__ inline double wave_sum_d(double v) { return wave_reduce_d(v, [](double a, double b) { return a + b; }); }
 __device__ __forceinline__ float wave_sum_f(float v) {
     asm(CG_DPP_WAVE_REDUCE("v_add_f32_dpp") : "+v"(v));
@@ -321,14 +320,6 @@ static_assert(kWaves == 16, "slot reductions read one slot per lane of a 16-lane
 // Each wave reduces in registers, lane 0 parks the result in slot[wave];
 // after one barrier every wave reads the 16 slots with lanes 0..15 and
 // reduces that row of lanes with DPP.  One barrier, no second pass.
-__device__ __forceinline__ double slots_max_d(const double *slot) {
-    double v = slot[threadIdx.x & 15];
-    v = fmax(v, dpp_d<kQuadSwap1>(v));
-    v = fmax(v, dpp_d<kQuadSwap2>(v));
-    v = fmax(v, dpp_d<kRowRor4>(v));
-    v = fmax(v, dpp_d<kRowRor8>(v));
-    return readlane_d(v, 0);
-}
 __device__ __forceinline__ double slots_sum_d(const double *slot) {
     double v = slot[threadIdx.x & 15];
     v += dpp_d<kQuadSwap1>(v);
@@ -336,24 +327,6 @@ __device__ __forceinline__ double slots_sum_d(const double *slot) {
     v += dpp_d<kRowRor4>(v);
     v += dpp_d<kRowRor8>(v);
     return readlane_d(v, 0);
-}
-__device__ __forceinline__ void slots_argmax(const double *sv, const int *si, double &v, int &i) {
-    v = sv[threadIdx.x & 15];
-    i = si[threadIdx.x & 15];
-    arg_step<kQuadSwap1>(v, i);
-    arg_step<kQuadSwap2>(v, i);
-    arg_step<kRowRor4>(v, i);
-    arg_step<kRowRor8>(v, i);
-    v = readlane_d(v, 0);
-    i = __builtin_amdgcn_readlane(i, 0);
-}
-__device__ __forceinline__ int wave_min_i(int v) {
-    v = min(v, dpp_i<kQuadSwap1>(v));
-    v = min(v, dpp_i<kQuadSwap2>(v));
-    v = min(v, dpp_i<kRowRor4>(v));
-    v = min(v, dpp_i<kRowRor8>(v));
-    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 struct ChunkInfo {
@@ -400,15 +373,16 @@ __device__ double chunk_lse_exact(const void *logits, size_t rowbase, const uint
 // G(i) in float for screening, from v_log_f32 only, without branches: -ln u
 // for u <= 1/2; above, with v = 1 - u (from w): a 4-term series of
 // -ln(1 - v) for v < 2^-7, else -ln(1 - v) rounded from float (relative
-// error < 4e-6).  Absolute error of the result < 1e-5.
+// error < 4e-6).  Absolute error of the result < 1e-5.  The argument of the
+// first logarithm is selected before it is taken: two v_log_f32 per value.
 __device__ inline float gumbel32(uint32_t w) {
     constexpr float kLn2 = 0.6931471805599453f;
     const float u = ((float)w + 0.5f) * 2.3283064365386963e-10f;
     const float v = ((float)(0xFFFFFFFFu - w) + 0.5f) * 2.3283064365386963e-10f;
-    const float t_lo = -kLn2 * __builtin_amdgcn_logf(u);
+    const bool lo = w < 0x80000000u;
     const float t_ser = v * (1.f + v * (0.5f + v * (0.33333334f + v * 0.25f)));
-    const float t_log = -kLn2 * __builtin_amdgcn_logf(1.f - v);
-    const float t = (w < 0x80000000u) ? t_lo : (v < 0.0078125f ? t_ser : t_log);
+    const float t_log = -kLn2 * __builtin_amdgcn_logf(lo ? u : 1.f - v);
+    const float t = (!lo && v < 0.0078125f) ? t_ser : t_log;
     return -kLn2 * __builtin_amdgcn_logf(t);
 }
 
@@ -427,21 +401,6 @@ __device__ __forceinline__ void top2_merge(Top2 &a, float bv1, int bi1, float bv
         a.v2 = fmaxf(a.v2, bv1);
     }
 }
-template <int CTRL>
-__device__ __forceinline__ void top2_step(Top2 &a) {
-    const float v1 = __int_as_float(dpp_i<CTRL>(__float_as_int(a.v1)));
-    const float v2 = __int_as_float(dpp_i<CTRL>(__float_as_int(a.v2)));
-    const int i1 = dpp_i<CTRL>(a.i1);
-    top2_merge(a, v1, i1, v2);
-}
-// wave-wide top-2 (every lane of each 16-lane row holds the row's; the
-// caller combines rows)
-__device__ __forceinline__ void top2_rows(Top2 &a) {
-    top2_step<kQuadSwap1>(a);
-    top2_step<kQuadSwap2>(a);
-    top2_step<kRowRor4>(a);
-    top2_step<kRowRor8>(a);
-}
 // The same from two wave maxes: the best value, the lowest index holding it,
 // then the best of everything else.
 __device__ __forceinline__ Top2 top2_wave_fast(const Top2 &a) {
@@ -450,18 +409,6 @@ __device__ __forceinline__ Top2 top2_wave_fast(const Top2 &a) {
     r.i1 = wave_min_i_fast((a.i1 >= 0 && a.v1 == r.v1) ? a.i1 : 0x7FFFFFFF);
     if (r.i1 == 0x7FFFFFFF) r.i1 = -1;
     r.v2 = wave_max_f(a.i1 == r.i1 ? a.v2 : a.v1);
-    return r;
-}
-__device__ __forceinline__ Top2 top2_wave(Top2 a) {
-    top2_rows(a);
-    Top2 r;
-    r.v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v1), 0));
-    r.v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v2), 0));
-    r.i1 = __builtin_amdgcn_readlane(a.i1, 0);
-    for (int l = 16; l < 64; l += 16)
-        top2_merge(r, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v1), l)),
-                   __builtin_amdgcn_readlane(a.i1, l),
-                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v2), l)));
     return r;
 }
 // the same for chunk scores, in double (they can be large for heavy-tailed logits)
@@ -479,47 +426,6 @@ __device__ __forceinline__ void top2d_merge(Top2d &a, double bv1, int bi1, doubl
         a.v2 = fmax(a.v2, bv1);
     }
 }
-template <int CTRL>
-__device__ __forceinline__ void top2d_step(Top2d &a) {
-    const double v1 = dpp_d<CTRL>(a.v1), v2 = dpp_d<CTRL>(a.v2);
-    const int i1 = dpp_i<CTRL>(a.i1);
-    top2d_merge(a, v1, i1, v2);
-}
-__device__ __forceinline__ void top2d_rows(Top2d &a) {
-    top2d_step<kQuadSwap1>(a);
-    top2d_step<kQuadSwap2>(a);
-    top2d_step<kRowRor4>(a);
-    top2d_step<kRowRor8>(a);
-}
-__device__ __forceinline__ Top2d top2d_wave(Top2d a) {
-    top2d_rows(a);
-    Top2d r{readlane_d(a.v1, 0), readlane_d(a.v2, 0), __builtin_amdgcn_readlane(a.i1, 0)};
-    for (int l = 16; l < 64; l += 16)
-        top2d_merge(r, readlane_d(a.v1, l), __builtin_amdgcn_readlane(a.i1, l), readlane_d(a.v2, l));
-    return r;
-}
-__device__ __forceinline__ Top2d top2d_slots(const double *v1, const int *i1, const double *v2) {
-    const int k = threadIdx.x & 15;
-    Top2d a{v1[k], v2[k], i1[k]};
-    top2d_rows(a);
-    return Top2d{readlane_d(a.v1, 0), readlane_d(a.v2, 0), __builtin_amdgcn_readlane(a.i1, 0)};
-}
-
-// block-wide: slots of 16 waves, each wave reduces them with a 16-lane row
-__device__ __forceinline__ Top2 top2_slots(const float *v1, const int *i1, const float *v2) {
-    Top2 a;
-    const int k = threadIdx.x & 15;
-    a.v1 = v1[k];
-    a.i1 = i1[k];
-    a.v2 = v2[k];
-    top2_rows(a);
-    Top2 r;
-    r.v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v1), 0));
-    r.v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v2), 0));
-    r.i1 = __builtin_amdgcn_readlane(a.i1, 0);
-    return r;
-}
-
 // Per-wave copy of the best chunk seen so far (bf16 rows): the chunk's logits
 // in id order (4 KB) and each lane's four mask bytes, so the pick inside the
 // chosen chunk reads LDS instead of HBM.
