@@ -3,7 +3,9 @@
 //
 //   k_sample      one workgroup per row streams the logits once: masked max
 //                 and sum of exp((x - max) / T) per 2048-id chunk, then the
-//                 greedy pick or the two-level Philox Gumbel-max draw
+//                 greedy pick or the two-level Philox Gumbel-max draw; fused,
+//                 also the advance over the picked token and the plan of the
+//                 row's next mask
 //
 // Bound by HBM bandwidth and the per-logit VALU work; no MFMA (nothing here
 // is a dense contraction).
@@ -460,15 +462,17 @@ __host__ __device__ inline size_t stash_offset(int K) { return ((size_t)K * size
 constexpr int kStageRegs = 4;
 
 // One workgroup per row.  Its 16 waves stream the row's 2048-id chunks (wave
-// w takes chunks w, w + 16, ...; the next chunk's loads are in flight while
-// one is reduced), leave one summary
-// per chunk in LDS and fold each chunk into a running per-wave summary.  After
-// one barrier every wave merges the 16 wave summaries into the row's decision
-// and the workgroup picks the token inside the chosen chunk.  No state crosses
-// workgroups, so no device-wide fence is ever needed.
-// plan_next (with the fused advance): after the commit, the workgroup plans
-// its row's next mask from the committed state (fill_plan.hpp), rewriting
-// the row's mask words it has finished reading (mask is not restrict).
+// w takes chunks w, w + 16, ...; three chunks' loads in flight while one is
+// reduced) and leave one summary per chunk in LDS (masked max, sum of
+// exponentials, the chunk's screening noise); each wave also keeps a copy
+// of its best chunk so far in an LDS stash.  After one barrier three waves
+// reduce the chunk summaries at once (log-normaliser, greedy chunk, best two
+// chunk scores), then eight waves pick the token inside the chosen chunk,
+// read from the stash.  No state crosses workgroups, so no device-wide fence
+// is ever needed.  With the fused advance the first thread commits the
+// token; with plan_next the workgroup then plans its row's next mask from
+// the committed state (fill_plan.hpp), rewriting the row's mask words it
+// has finished reading (mask is not restrict).
 template <int DT, bool VEC>
 __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
                                                  const uint64_t *mask, int words_per_row,
