@@ -669,7 +669,20 @@ def main():
         fill_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
         samp_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     adv_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    assert np.array_equal(steps.cpu().numpy(), st_h), "replay diverged from the timed trajectory"
+    # and once more with one event at each step boundary only (an event
+    # between two launches stretches the step): the step's percentiles
+    st.copy_(st0)
+    steps.copy_(steps0)
+    mask.copy_(mask0)
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evb[0].record(stream)
+    for k in range(args.steps):
+        step(args.warmup + k)
+        evb[k + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([evb[k].elapsed_time(evb[k + 1]) for k in range(args.steps)])
     assert np.array_equal(steps.cpu().numpy(), st_h), "replay diverged from the timed trajectory"
 
     # masked sample: every logit (bf16) and mask word read once, id + logprob
