@@ -144,3 +144,95 @@ def test_fill_million_token_vocab():
     got = gpu_masks(g, st)
     want, _ = oracle_masks(og, rows, blob, off)
     assert np.array_equal(got[:, :want.shape[1]], want)
+
+
+def _stored(x, dt):
+    """float64 values rounded to dtype as the device stores them."""
+    import torch
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(dt).double().numpy()
+
+
+def _lse64(v):
+    m = np.max(v)
+    return float(m + np.log(np.sum(np.exp(v - m))))
+
+
+def _token_contended_row(rng, dt, Tf, seed, step, V, x, bits, r):
+    """Only chunk 3 has allowed ids (64 of them); two of them get token scores
+    x/T + G(0, i) between 2e-6 and 4e-5 apart, the rest score 6 lower.  The
+    ids are drawn again on every attempt: on a bf16 grid the rounding of the
+    second value is what lands the gap, and it depends on the noise."""
+    for attempt in range(4000):
+        ids = 3 * 2048 + np.sort(rng.choice(2048, 64, replace=False))
+        G = O.gumbel(O.philox_words(seed, step, 0, ids))
+        xi = _stored([Tf * (4.0 - G[0])], dt)[0]
+        S = xi / Tf + G[0]
+        for k in range(1, len(ids)):
+            xj = _stored([Tf * (S + 1e-5 - G[k])], dt)[0]
+            d = xj / Tf + G[k] - S
+            if 2e-6 < abs(d) < 4e-5:
+                xs = _stored(Tf * (S - 6.0 - G - rng.random(len(ids))), dt)
+                xs[0], xs[k] = xi, xj
+                x[r, ids] = xs
+                bits[r, ids] = True
+                return
+    raise AssertionError("no contended token pair found")
+
+
+def _chunk_contended_row(rng, dt, Tf, seed, step, V, x, bits, r):
+    """Two chunks hold one dominant allowed id and three companions 2-6
+    lower (in x / T) each; their chunk scores L_c + G(1, c) are between 2e-6
+    and 2e-5 apart (inside the screening window), every other chunk is
+    masked.  The companions are drawn again on every attempt (they move the
+    chunk's log-mass, and with it where the rounding lands the gap)."""
+    K = V // 2048
+    G1 = O.gumbel(O.philox_words(seed, step, 1, np.arange(K)))
+    def chunk_vals(c, score):
+        # dominant + companions whose log-sum-exp of x / T is close to score
+        o = 2.0 + 4.0 * rng.random(3)
+        top_z = score - np.log1p(np.exp(-o).sum())
+        top = _stored([Tf * top_z], dt)[0]
+        v = _stored(np.concatenate([[top], top - Tf * o]), dt)
+        pos = c * 2048 + np.sort(rng.choice(2048, 4, replace=False))
+        return pos, v
+    for attempt in range(4000):
+        pa, va = chunk_vals(0, 4.0 - G1[0])
+        S = _lse64(va / Tf) + G1[0]
+        for c in range(1, K):
+            pb, vb = chunk_vals(c, S + 1e-5 - G1[c])
+            d = _lse64(vb / Tf) + G1[c] - S
+            if 2e-6 < abs(d) < 2e-5:
+                x[r, pa], x[r, pb] = va, vb
+                bits[r, pa] = bits[r, pb] = True
+                return
+    raise AssertionError("no contended chunk pair found")
+
+
+@pytest.mark.parametrize("dtype_name", ["float32", "bfloat16"])
+def test_sample_contended_picks(dtype_name):
+    """Rows whose two best candidates are closer than the float screening
+    can order, so the sampler must decide in double: two tokens of one chunk
+    (the pick inside the chunk, from the stash for bf16 and from memory for
+    float32), or two chunks (their log-masses recomputed exactly).  Each
+    row's oracle margin at that level is checked to lie between the near-tie
+    bound (1e-6) and the screening window, so every row takes the exact
+    path, and every pick must equal the oracle's."""
+    import torch
+    say("contended", dtype_name)
+    dt = getattr(torch, dtype_name)
+    T, step = 0.7, 7
+    Tf = float(np.float32(T))
+    rng = np.random.default_rng(21)
+    B, V = 16, 16 * 2048
+    x = np.full((B, V), -30.0)
+    bits = np.zeros((B, V), dtype=bool)
+    seeds = [int(s) for s in rng.integers(0, 2**63, size=B)]
+    for r in range(B):
+        (_token_contended_row if r % 2 == 0 else _chunk_contended_row)(rng, dt, Tf, seeds[r], step, V, x, bits, r)
+    xs, ids, lp = _run_sample(x, bits, T, seeds, step, dt)
+    for r in range(B):
+        i, l, info = O.sample_row(xs[r], bits[r], T, seeds[r], step)
+        margin = info["margin_token"] if r % 2 == 0 else info["margin_chunk"]
+        assert NEAR_TIE < margin < 5e-5, (r, info)
+        assert ids[r] == i, (r, ids[r], i, info)
+        assert abs(lp[r] - l) < 1e-5, (r, lp[r], l)
