@@ -179,12 +179,14 @@ def _token_contended_row(rng, dt, Tf, seed, step, V, x, bits, r):
     raise AssertionError("no contended token pair found")
 
 
-def _chunk_contended_row(rng, dt, Tf, seed, step, V, x, bits, r):
+def _chunk_contended_row(rng, dt, Tf, seed, step, V, x, bits, r, same_wave=False):
     """Two chunks hold one dominant allowed id and three companions 2-6
     lower (in x / T) each; their chunk scores L_c + G(1, c) are between 2e-6
     and 2e-5 apart (inside the screening window), every other chunk is
     masked.  The companions are drawn again on every attempt (they move the
-    chunk's log-mass, and with it where the rounding lands the gap)."""
+    chunk's log-mass, and with it where the rounding lands the gap).
+    same_wave: the second chunk is 16 or 32, reduced by the same wave as
+    chunk 0, whose copy of its best chunk then holds only one of the two."""
     K = V // 2048
     G1 = O.gumbel(O.philox_words(seed, step, 1, np.arange(K)))
     def chunk_vals(c, score):
@@ -198,7 +200,7 @@ def _chunk_contended_row(rng, dt, Tf, seed, step, V, x, bits, r):
     for attempt in range(4000):
         pa, va = chunk_vals(0, 4.0 - G1[0])
         S = _lse64(va / Tf) + G1[0]
-        for c in range(1, K):
+        for c in (range(16, K, 16) if same_wave else range(1, K)):
             pb, vb = chunk_vals(c, S + 1e-5 - G1[c])
             d = _lse64(vb / Tf) + G1[c] - S
             if 2e-6 < abs(d) < 2e-5:
@@ -213,7 +215,9 @@ def test_sample_contended_picks(dtype_name):
     """Rows whose two best candidates are closer than the float screening
     can order, so the sampler must decide in double: two tokens of one chunk
     (the pick inside the chunk, from the stash for bf16 and from memory for
-    float32), or two chunks (their log-masses recomputed exactly).  Each
+    float32), or two chunks (their log-masses recomputed exactly; half of
+    these pairs are reduced by the same wave, so for bf16 the winner may be
+    the one its stash does not hold, and is read from memory).  Each
     row's oracle margin at that level is checked to lie between the near-tie
     bound (1e-6) and the screening window, so every row takes the exact
     path, and every pick must equal the oracle's."""
@@ -223,12 +227,15 @@ def test_sample_contended_picks(dtype_name):
     T, step = 0.7, 7
     Tf = float(np.float32(T))
     rng = np.random.default_rng(21)
-    B, V = 16, 16 * 2048
+    B, V = 16, 48 * 2048
     x = np.full((B, V), -30.0)
     bits = np.zeros((B, V), dtype=bool)
     seeds = [int(s) for s in rng.integers(0, 2**63, size=B)]
     for r in range(B):
-        (_token_contended_row if r % 2 == 0 else _chunk_contended_row)(rng, dt, Tf, seeds[r], step, V, x, bits, r)
+        if r % 2 == 0:
+            _token_contended_row(rng, dt, Tf, seeds[r], step, V, x, bits, r)
+        else:
+            _chunk_contended_row(rng, dt, Tf, seeds[r], step, V, x, bits, r, same_wave=r % 4 == 1)
     xs, ids, lp = _run_sample(x, bits, T, seeds, step, dt)
     for r in range(B):
         i, l, info = O.sample_row(xs[r], bits[r], T, seeds[r], step)
