@@ -243,3 +243,58 @@ def test_sample_contended_picks(dtype_name):
         assert NEAR_TIE < margin < 5e-5, (r, info)
         assert ids[r] == i, (r, ids[r], i, info)
         assert abs(lp[r] - l) < 1e-5, (r, lp[r], l)
+
+
+def test_fill_many_row_blocks():
+    """A batch of 16,421 rows (the walk scans its rows' tile counts in blocks
+    of 8192 rows: two full blocks and a ragged third), made of 48 rows at
+    random legal prefixes repeated in a seeded order: every row's mask
+    equals its prototype's oracle mask, bit-exact.  One fused step over the
+    whole batch (sample, advance, next mask) then equals the separate calls."""
+    import torch
+    say("row blocks")
+    cfg = 3
+    blob, off = W.make_vocab(cfg, 20000)
+    V = len(off) - 1
+    toks = [blob[off[i]:off[i + 1]] for i in range(V)]
+    g = cg.Grammar(W.spec_json(cfg), blob, off)
+    og = O.load_spec(W.spec_json(cfg))
+    rng = W.SplitMix(0xB10C)
+    seqs, orows = [], []
+    for _ in range(48):
+        s, row = random_walk(og, toks, rng.below(40), rng)
+        seqs.append(s)
+        orows.append(row)
+    st_p, steps_p, _ = device_rows(g, seqs)
+    want, _ = oracle_masks(og, orows, blob, off)
+    B = 2 * 8192 + 37
+    pick = np.random.default_rng(3).integers(0, 48, size=B)
+    pick_t = torch.from_numpy(pick).cuda()
+    st = st_p.index_select(0, pick_t).contiguous()
+    got = gpu_masks(g, st)
+    assert np.array_equal(got[:, :want.shape[1]], want[pick])
+    # one fused step over the whole batch against the separate calls
+    steps = steps_p.index_select(0, pick_t).contiguous()
+    temp = torch.full((B,), 0.7, dtype=torch.float32, device="cuda")
+    seed = torch.from_numpy(np.array(W.row_seeds(cfg, B), dtype=np.uint64).view(np.int64)).cuda()
+    ws = cg.new_workspace(B, V)
+    fws = g.new_fill_workspace(B)
+    logits = W.make_logits(cfg, 0, B, V, "cuda")
+    out = []
+    for fused in (False, True):
+        s_st, s_steps = st.clone(), steps.clone()
+        status = torch.zeros(B, dtype=torch.int32, device="cuda")
+        ids = torch.empty(B, dtype=torch.int32, device="cuda")
+        lp = torch.empty(B, dtype=torch.float32, device="cuda")
+        mask = torch.empty((B, g.W), dtype=torch.int64, device="cuda")
+        g.fill_bitmask(s_st, mask, fws)
+        if fused:
+            g.sample_advance_fill(logits, mask, temp, seed, s_steps, ws, ids, lp, s_st, status, fws)
+        else:
+            g.sample_advance(logits, mask, temp, seed, s_steps, ws, ids, lp, s_st, status)
+            g.fill_bitmask(s_st, mask, fws)
+        torch.cuda.synchronize()
+        out.append((ids, lp.view(torch.int32), s_st, s_steps, status, mask))
+    for a, b in zip(*out):
+        assert torch.equal(a, b)
+    assert int((out[0][4] == cg.ROW_OK).sum()) + int((out[0][4] == cg.ROW_DONE).sum()) > B // 2
