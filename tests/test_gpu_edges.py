@@ -298,3 +298,39 @@ def test_fill_many_row_blocks():
     for a, b in zip(*out):
         assert torch.equal(a, b)
     assert int((out[0][4] == cg.ROW_OK).sum()) + int((out[0][4] == cg.ROW_DONE).sum()) > B // 2
+
+
+@pytest.mark.parametrize("max_len", [4, 12, 28])
+def test_fill_token_length_classes(max_len):
+    """The walk is specialised by the longest token's length in 4-byte words;
+    vocabularies whose longest token is 4, 12 or 28 bytes (the tool-call
+    vocabulary cut to that length, duplicates dropped, one token padded to
+    the full length) reach the word counts the workloads do not: masks of
+    rows at random legal prefixes against the oracle, bit-exact."""
+    say("token length", max_len)
+    cfg = 3
+    blob0, off0 = W.make_vocab(cfg, 6000)
+    toks, seen = [], set()
+    for i in range(len(off0) - 1):
+        t = blob0[off0[i]:off0[i + 1]][:max_len]
+        if t not in seen:
+            seen.add(t)
+            toks.append(t)
+    longest = b'"' + b"a" * (max_len - 1)
+    if longest not in seen:
+        toks.append(longest)
+    assert max(len(t) for t in toks) == max_len
+    blob = b"".join(toks)
+    off = np.concatenate([[0], np.cumsum([len(t) for t in toks])]).tolist()
+    g = cg.Grammar(W.spec_json(cfg), blob, off)
+    og = O.load_spec(W.spec_json(cfg))
+    rng = W.SplitMix(0x1E7 + max_len)
+    seqs, rows = [], []
+    for _ in range(32):
+        s, row = random_walk(og, toks, rng.below(40), rng)
+        seqs.append(s)
+        rows.append(row)
+    st, _, _ = device_rows(g, seqs)
+    want, _ = oracle_masks(og, rows, blob, off)
+    got = gpu_masks(g, st)
+    assert np.array_equal(got[:, :want.shape[1]], want)
