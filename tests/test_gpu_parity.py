@@ -316,18 +316,25 @@ def test_sample_parity(torch_dev, cfg, B, V, T):
     assert ties <= max(1, B // 10)
 
 
-def test_sample_strided_and_wide_mask(torch_dev):
-    """row_stride > vocab, misaligned stride (scalar loads), extra mask words."""
-    for stride in (128256 + 64, 128256 + 3):
-        x, bits, seeds, ids, lp = _sample_case(torch_dev, 3, 8, 128256, 0.7, step=3, row_stride=stride,
-                                               mask_words=2010)
+@pytest.mark.parametrize("cfg,V,T,strides,mask_words", [
+    (3, 128256, 0.7, (128256 + 64, 128256 + 3), 2010),   # bf16
+    (3, 128256, 0.0, (128256 + 3,), 2004),
+    (2, 32000, 0.7, (32000 + 4, 32000 + 1), 505),       # float32
+])
+def test_sample_strided_and_wide_mask(torch_dev, cfg, V, T, strides, mask_words):
+    """row_stride > vocab, misaligned stride (rows not 16-byte aligned: the
+    bounds-checked loads), extra mask words."""
+    say("strided", cfg, T, strides)
+    for stride in strides:
+        x, bits, seeds, ids, lp = _sample_case(torch_dev, cfg, 8, V, T, step=3, row_stride=stride,
+                                               mask_words=mask_words)
         for r in range(8):
-            i, l, info = O.sample_row(x[r], bits[r], 0.7, int(seeds[r]), 3)
+            i, l, info = O.sample_row(x[r], bits[r], T, int(seeds[r]), 3)
             if i < 0:
                 assert ids[r] == -1
                 continue
-            if min(info["margin_chunk"], info["margin_token"]) >= NEAR_TIE:
-                assert ids[r] == i and abs(lp[r] - l) < LOGPROB_TOL
+            if T == 0 or min(info["margin_chunk"], info["margin_token"]) >= NEAR_TIE:
+                assert ids[r] == i and abs(lp[r] - l) < LOGPROB_TOL, (stride, r, ids[r], i)
 
 
 def test_sample_fp32_greedy_ties(torch_dev):
