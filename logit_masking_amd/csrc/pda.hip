@@ -380,8 +380,11 @@ __global__ __launch_bounds__(kWalkThreads) void k_fill_walk(FillArgs a) {
         if (tid == kWalkThreads - 1) prefix[nb] = run;
         __syncthreads();
         const uint32_t total = prefix[nb];
+        // tile g goes to wave g / gridDim.x of workgroup g % gridDim.x: a
+        // step's tiles spread over every CU, one wave per SIMD first,
+        // before any CU walks several at once
         const uint32_t stride = gridDim.x * kWalkWaves;
-        uint32_t g = blockIdx.x * kWalkWaves + wave;
+        uint32_t g = wave * gridDim.x + blockIdx.x;
         TileRef t0{}, t1{}, t2{};
         LaneTok<NW> cur{}, nxt{};
         fetch_ref(t0, g, total, prefix, nb, rb, a);
