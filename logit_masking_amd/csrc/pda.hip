@@ -314,15 +314,40 @@ struct TileRef {
 
 constexpr int kWalkRowBlock = 8192;  // rows whose tile counts are scanned at once
 
-// Row of the g-th listed tile of the block: the last r with prefix[r] <= g.
+// Row of the g-th listed tile of the block: the last r < nb with
+// prefix[r] <= g (prefix non-decreasing, prefix[0] = 0 <= g).  A 64-way
+// search by the whole wave: each lane tests one boundary of the current
+// span, the ballot's highest set lane narrows it (two rounds for 256 rows,
+// three up to 262,144).  Every lane of the wave must be active.
 __device__ __forceinline__ int row_of(const uint32_t *prefix, int nb, uint32_t g) {
-    int lo = 0, hi = nb;  // prefix[lo] <= g < prefix[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (prefix[mid] <= g) lo = mid;
-        else hi = mid;
+    const int lane = threadIdx.x & 63;
+    int lo = 0, span = nb;  // the row is in [lo, lo + span), prefix[lo] <= g
+    while (span > 1) {
+        const int step = (span + 63) >> 6;
+        const bool ok = lane * step < span && prefix[lo + lane * step] <= g;
+        const uint64_t m = __ballot(ok);  // lanes 0 .. k (lane 0 always)
+        const int k = 63 - __builtin_clzll(m);
+        lo += k * step;
+        span = min(step, span - k * step);
     }
     return lo;
+}
+
+// Inclusive sum over the lanes of a wave with DPP: shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then the last lane of rows 0 / 2 into rows
+// 1 / 3 and of row 1 into rows 2 and 3.  Every lane must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t v) {
+    return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31
+    return v;
 }
 
 __device__ __forceinline__ void fetch_ref(TileRef &t, uint32_t g, uint32_t total, const uint32_t *prefix, int nb,
@@ -362,16 +387,13 @@ __global__ __launch_bounds__(kWalkThreads) void k_fill_walk(FillArgs a) {
             prefix[i] = n;  // the count, until the scan below replaces it
             sum += n;
         }
-        uint32_t incl = sum;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
-        }
+        const uint32_t incl = wave_incl_sum(sum);
         if (lane == 63) wave_sum[wave] = incl;
         __syncthreads();
-        uint32_t run = incl - sum;
-        for (int w = 0; w < wave; w++) run += wave_sum[w];
+        // the totals of the waves before this one: lane w < wave reads wave
+        // w's, summed across the first row of lanes
+        const uint32_t before = wave_incl_sum(lane < wave ? wave_sum[lane] : 0u);
+        uint32_t run = incl - sum + (uint32_t)__builtin_amdgcn_readlane((int)before, 15);
         for (int i = r0; i < r1; i++) {
             const uint32_t n = prefix[i];
             prefix[i] = run;
