@@ -12,7 +12,7 @@ bench cap of "Constrained decoding", "What it is worth"), engine cap 2048.
 Logits for every step are generated before the timed region and stay in HBM.
 
 Prints one JSON line.  --gpus above 1 is refused: the path shards by rows
-with no exchange, and this build measures one GPU.
+with no exchange, and bench.py measures one GPU.
 """
 import argparse
 import json
@@ -550,8 +550,8 @@ def main():
                     help="measure result injection on text with calc spans instead (its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: rows shard across GPUs with no exchange, and multi-GPU runs are not "
-              "part of this build", file=sys.stderr)
+        print("bench.py measures one GPU: rows shard across GPUs with no exchange, and runs on more than one "
+              "GPU are not supported", file=sys.stderr)
         sys.exit(2)
 
     if args.inject:

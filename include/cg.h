@@ -264,7 +264,7 @@ size_t cg_sample_workspace_bytes(int32_t batch, int32_t vocab);
  * ("Constrained decoding", "The guarantee": sampling runs after masking.)
  * row_stride >= vocab elements; vocab <= 4,194,304 (2048 chunks).
  * d_workspace: cg_sample_workspace_bytes(batch, vocab) bytes, 16-byte
- *   aligned; may be NULL when that size is 0 (this build keeps every
+ *   aligned; may be NULL when that size is 0 (the sampler keeps every
  *   intermediate on chip, so it always is).
  * Outputs: d_out_ids[batch] int32, d_out_logprob[batch] float32.
  */
