@@ -86,3 +86,63 @@ def test_full_size_step_against_oracle(cfg):
     want1, _ = oracle_masks(og, rows1, blob, off)
     assert np.array_equal(mask1[:, :want1.shape[1]], want1)
     assert ties <= 2
+
+
+def test_full_size_trajectory_tool_call():
+    """The bench's own trajectory (tool-call grammar, vocab 128,256, batch
+    256, T = 0.7, every row from the start state) for 30 steps of
+    cg_sample_advance_fill, 16 rows followed in lock-step by the oracle:
+    every step's mask, pick and log-probability equal the oracle's (a
+    sampled near-tie adopts the device's pick on both sides)."""
+    import torch
+    say("full size trajectory")
+    cfg = 3
+    c = W.CONFIGS[cfg]
+    B, T = c["B"], float(c["T"])
+    blob, off = W.make_vocab(cfg)
+    V = len(off) - 1
+    toks = [blob[off[i]:off[i + 1]] for i in range(V)]
+    g = cg.Grammar(W.spec_json(cfg), blob, off)
+    og = O.load_spec(W.spec_json(cfg))
+    st = g.new_states(B)
+    g.init_state(st)
+    steps = torch.zeros(B, dtype=torch.int32, device="cuda")
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+    temp = torch.full((B,), T, dtype=torch.float32, device="cuda")
+    seeds = np.array(W.row_seeds(cfg, B), dtype=np.uint64)
+    seed = torch.from_numpy(seeds.view(np.int64)).cuda()
+    ws = cg.new_workspace(B, V)
+    fws = g.new_fill_workspace(B)
+    mask = torch.empty((B, g.W), dtype=torch.int64, device="cuda")
+    ids = torch.empty(B, dtype=torch.int32, device="cuda")
+    lp = torch.empty(B, dtype=torch.float32, device="cuda")
+    check = np.sort(np.random.default_rng(7).choice(B, 16, replace=False))
+    check_t = torch.from_numpy(check).cuda()
+    orows = [O.Row(og, W.GEN_CAP) for _ in check]
+    g.fill_bitmask(st, mask, fws)
+    ties = taken = 0
+    for s in range(30):
+        logits = W.make_logits(cfg, s, B, V, "cuda")
+        torch.cuda.synchronize()
+        got = mask.cpu().numpy().view(np.uint64)[check]
+        want, _ = oracle_masks(og, orows, blob, off)
+        assert np.array_equal(got[:, :want.shape[1]], want), s
+        g.sample_advance_fill(logits, mask, temp, seed, steps, ws, ids, lp, st, status, fws)
+        torch.cuda.synchronize()
+        x = logits.index_select(0, check_t).float().cpu().numpy().astype(np.float64)
+        ids_h, lp_h = ids.cpu().numpy()[check], lp.cpu().numpy()[check]
+        for k, r in enumerate(check):
+            bits = O.unpack_mask(want[k], V)
+            i, l, info = O.sample_row(x[k], bits, T, int(seeds[r]), orows[k].step)
+            if i >= 0 and min(info["margin_chunk"], info["margin_token"]) < NEAR_TIE:
+                ties += 1
+                assert bits[ids_h[k]]
+                i = int(ids_h[k])
+            else:
+                assert ids_h[k] == i, (s, r, ids_h[k], i, info)
+                if i >= 0:
+                    assert abs(lp_h[k] - l) < 1e-5, (s, r, lp_h[k], l)
+            if i >= 0:
+                orows[k].advance(toks[i])
+                taken += 1
+    assert ties <= 2 and taken > 100
