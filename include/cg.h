@@ -170,8 +170,8 @@ typedef struct {
  * Compiled grammars are cached: a compile with the same spec text,
  * vocabulary, options and device returns the same read-only handle with one
  * more reference (cg_free_grammar drops one); up to 8 handles no one holds
- * are kept for later identical compiles ("Evaluator aware decoding", "A
- * concrete prototype on llama.cpp": grammar caching keeps repeated grammars
+ * are kept for later identical compiles ("Evaluator aware decoding", "Where
+ * XGrammar-2 could take this": cross-grammar caching keeps repeated grammars
  * from costing compilation).  Thread-safe.
  */
 int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *tok_bytes,
@@ -233,8 +233,10 @@ size_t cg_draft_workspace_bytes(const cg_grammar *g, int32_t batch, int32_t k);
  * finished).  The target model's logits at position j are masked with mask j
  * and a verifier keeps a prefix of at most d_accept_len[r] tokens; the row
  * then takes d_path_states at the kept length (and d_step += that length).
- * The rows themselves are not changed.  "Constrained decoding", "The
- * guarantee": every position is masked by the automaton's state there.
+ * The rows themselves are not changed.  "Evaluator aware decoding", "Where
+ * XGrammar-2 could take this": speculative pipelines verify drafts along
+ * forced-token paths; every position is masked by the automaton's state
+ * there.
  * k <= CG_MAX_DRAFT; d_workspace: cg_draft_workspace_bytes(g, batch, k)
  * bytes, 16-byte aligned, scratch.
  */

@@ -468,8 +468,8 @@ int build_state_masks(cg_grammar *g, const FillHost &f) {
 
 // Compiled grammars are shared by (spec text, vocabulary, options, device):
 // an identical compile returns the same read-only handle with one more
-// reference ("Evaluator aware decoding", "A concrete prototype on
-// llama.cpp": cross-grammar caching keeps repeated grammars from blowing up
+// reference ("Evaluator aware decoding", "Where XGrammar-2 could take
+// this": cross-grammar caching keeps repeated grammars from blowing up
 // compilation).  Up to kCacheIdle handles no one holds any more are kept
 // for later identical compiles (least recently released first out).
 namespace {

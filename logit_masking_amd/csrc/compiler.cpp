@@ -260,7 +260,7 @@ struct Reader {
             const Json *mi = sch->get("maxItems");
             int64_t m = -1;
             if (mi) {
-                if (!is_plain_int(mi) || mi->i < -1) refuse(path, "maxItems must be a non-negative integer");
+                if (!is_plain_int(mi) || mi->i < 0) refuse(path, "maxItems must be a non-negative integer");
                 m = mi->i;
             }
             n.first = FC_ARR;

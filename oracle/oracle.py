@@ -270,8 +270,8 @@ class _Builder:
         if t == "array":
             if not keys <= {"type", "items", "maxItems"}:
                 raise Unsupported(path, f"unsupported keywords {sorted(keys - {'type', 'items', 'maxItems'})}")
-            mi = sch.get("maxItems", -1)
-            if not isinstance(mi, int) or isinstance(mi, bool) or mi < -1:
+            mi = sch.get("maxItems", -1)  # absent: no bound
+            if "maxItems" in sch and (not isinstance(mi, int) or isinstance(mi, bool) or mi < 0):
                 raise Unsupported(path, "maxItems must be a non-negative integer")
             if "items" in sch:
                 item = self.schema(sch["items"], f"{path}/items", depth + 1)

@@ -463,12 +463,14 @@ def _cat(parts_lists, budget):
     """All concatenations (one from each list) of total length <= budget."""
     res = [b""]
     for lst in parts_lists:
+        lst = sorted(lst, key=len)
         nxt = []
         for a in res:
             room = budget - len(a)
             for b in lst:
-                if len(b) <= room:
-                    nxt.append(a + b)
+                if len(b) > room:
+                    break
+                nxt.append(a + b)
         res = nxt
         if not res:
             break
@@ -484,11 +486,16 @@ class Enumerator:
         self.chars = closed_chars(sigma)
         self.cap = spec.get("open_string_cap", DEFAULTS["open_string_cap"])
         self.digits = _get(spec, "open_int_digits")
+        self._memo = {}
 
     def ok(self, b):
         return all(c in self.sigma for c in b)
 
     def strings(self, cap, budget):
+        """Every string of at most `cap` characters (None or < 0: any
+        number) spelled within `budget` bytes."""
+        if cap is None or cap < 0:
+            cap = budget
         out = [b'"' + b'"']
         cur = [b""]
         for _ in range(cap):
@@ -498,10 +505,81 @@ class Enumerator:
             out.extend(b'"' + a + b'"' for a in cur)
         return [s for s in out if len(s) <= budget]
 
+    # ---- open JSON values (RFC 8259), written from the grammar's productions:
+    # value = object / array / string / number / true / false / null;
+    # containers count against depth_cap (the root container is depth 1).
+    def numbers(self, budget):
+        """number = [ "-" ] int [ frac ] [ exp ]; int = "0" / [1-9] *DIGIT;
+        frac = "." 1*DIGIT; exp = ("e" / "E") [ "+" / "-" ] 1*DIGIT --
+        every spelling within `budget` bytes over the alphabet."""
+        sig = self.sigma
+        digits = [bytes([d]) for d in b"0123456789" if d in sig]
+        runs, cur = [], [b""]
+        while True:  # 1*DIGIT
+            cur = [a + d for a in cur for d in digits if len(a) + 1 <= budget]
+            if not cur:
+                break
+            runs += cur
+        ints = [b"0"] if b"0" in digits else []
+        ints += [r for r in runs if r[:1] != b"0"]
+        signs = [b""] + ([b"-"] if ord("-") in sig else [])
+        fracs = [b""] + ([b"." + r for r in runs] if ord(".") in sig else [])
+        exps = [b""]
+        for e in b"eE":
+            if e in sig:
+                for s in [b""] + [bytes([c]) for c in b"+-" if c in sig]:
+                    exps += [bytes([e]) + s + r for r in runs]
+        return _cat([signs, ints, fracs, exps], budget)
+
+    def any_values(self, budget, depth):
+        key = ("any", budget, depth)
+        if key in self._memo:
+            return self._memo[key]
+        out = self.strings(self.cap, budget) + self.numbers(budget)
+        out += [b for b in (b"true", b"false", b"null") if self.ok(b) and len(b) <= budget]
+        out += self.open_array(budget, depth) + self.open_object(budget, depth)
+        self._memo[key] = out
+        return out
+
+    def _members(self, first, budget):
+        """`first` (W member W) followed by any number of ("," W member W),
+        within `budget` bytes: the inside of a container."""
+        out, cur = list(first), list(first)
+        while cur:
+            nxt = []
+            for a in cur:
+                nxt += [a + b for b in _cat([[b","], first], budget - len(a))]
+            out += nxt
+            cur = nxt
+        return out
+
+    def open_array(self, budget, depth):
+        if depth + 1 > _get(self.spec, "depth_cap") or budget < 2:
+            return []
+        W = self.ws
+        out = _cat([[b"["], W, [b"]"]], budget)
+        elem = _cat([W, self.any_values(budget - 2, depth + 1), W], budget - 2)
+        out += [b"[" + s + b"]" for s in self._members(elem, budget - 2)]
+        return out
+
+    def open_object(self, budget, depth):
+        if depth + 1 > _get(self.spec, "depth_cap") or budget < 2:
+            return []
+        W = self.ws
+        out = _cat([[b"{"], W, [b"}"]], budget)
+        keys = self.strings(self.cap, budget - 2)
+        pair = _cat([W, keys, W, [b":"], W, self.any_values(budget - 2, depth + 1), W], budget - 2)
+        out += [b"{" + s + b"}" for s in self._members(pair, budget - 2)]
+        return out
+
     def values(self, sch, budget, depth=0):
         keys = set(sch) - {"title", "description"}
         if not keys:
-            raise ValueError("open values are not enumerable")
+            return self.any_values(budget, depth)
+        if keys == {"type"} and sch["type"] == "array":
+            return self.open_array(budget, depth)
+        if keys == {"type"} and sch["type"] == "object":
+            return self.open_object(budget, depth)
         if "anyOf" in sch:
             out = []
             for a in sch["anyOf"]:

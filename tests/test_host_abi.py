@@ -86,6 +86,11 @@ REFUSALS = [
     ({"type": "integer", "minimum": 5, "maximum": 4}, "$.schema"),
     ({"type": "integer"}, "$.schema"),
     ({}, "$.schema"),
+    # a negative bound is refused, not read as "no bound" (fail closed)
+    ({"type": "array", "items": {"type": "null"}, "maxItems": -1}, "$.schema"),
+    ({"type": "array", "maxItems": -1}, "$.schema"),
+    ({"type": "object", "properties": {"a": {"type": "array", "maxItems": -3}}, "required": [],
+      "additionalProperties": False}, "$.schema/properties/a"),
 ]
 
 
@@ -153,6 +158,46 @@ def test_tiny_languages_host(name, spec, sigma, budget):
         P = [P[rng.below(len(P))] for _ in range(3000)]
     for p in P:
         for b in set(sigma) | {0xFF, 0x20}:
+            _agree(og, hg, p + bytes([b]))
+
+
+def _open_json_cases():
+    from tests import test_open_json_pins as P
+    cases = [(c["input"].encode(), c["refused_at"], c["complete"]) for c in P._golden()]
+    return cases + P._deep_cases()
+
+
+@pytest.mark.parametrize("data,refused_at,complete", _open_json_cases(), ids=lambda x: str(x)[:16])
+def test_open_json_host(data, refused_at, complete, small_vocabs):
+    """The library's table walker on the recursive-JSON pins (RFC 8259 offsets,
+    the depth cap of 32)."""
+    blob, off = small_vocabs[5]
+    hg = cg.Grammar(W.spec_json(5), blob, off, host_only=True)
+    assert hg.try_input(data) == (len(data) if refused_at is None else refused_at, complete)
+
+
+@pytest.mark.parametrize("case", __import__("tests.test_open_json_pins", fromlist=["x"]).OPEN_TINY,
+                         ids=lambda c: c[0] if isinstance(c, tuple) else None)
+def test_open_tiny_languages_host(case):
+    """Open values under tiny caps: the table walker against the exact
+    prefix set of the enumerated language (every prefix with room for its
+    completion, each alphabet byte appended; bytes outside the alphabet
+    against the oracle)."""
+    name, spec, sigma, budget, room = case
+    hg = cg.Grammar(json.dumps(spec).encode(), b"a", [0, 1], host_only=True)
+    og = O.load_spec(spec)
+    M = langref.Enumerator(spec, sigma, budget).members()
+    P = langref.prefixes(M)
+    Ps = sorted(p for p in P if len(p) + 1 + room <= budget)
+    if len(Ps) > 3000:
+        rng = W.SplitMix(len(Ps))
+        Ps = [Ps[rng.below(len(Ps))] for _ in range(3000)]
+    for p in Ps:
+        assert hg.try_input(p) == (len(p), p in M), p
+        for b in set(sigma):
+            q = p + bytes([b])
+            assert (hg.try_input(q)[0] == len(q)) == (q in P), q
+        for b in {0xFF, 0x20, ord("x")} - set(sigma):  # outside the alphabet: the oracle
             _agree(og, hg, p + bytes([b]))
 
 

@@ -417,6 +417,9 @@ def test_finished_outputs_are_members(grammars):
     ({"type": "object", "properties": {"a": {"type": "string", "minLength": 1}}, "required": [],
       "additionalProperties": False}, "$.schema/properties/a"),
     ({"type": "integer", "minimum": 5, "maximum": 4}, "$.schema"),
+    # "Constrained Decoding Under Matched Conditions", "What exists beyond the
+    # experiment": refusals are typed and fail closed; a negative bound is one
+    ({"type": "array", "maxItems": -1}, "$.schema"),
 ])
 def test_unsupported_fail_closed(schema, path):
     with pytest.raises(O.Unsupported) as e:
@@ -479,14 +482,22 @@ def test_two_level_sampler_distribution():
 
 
 def test_sampled_logprob():
+    """The sampled pick's log-probability is torch's log_softmax of x / T over
+    the allowed tokens (float64), for bf16-valued and float logits."""
+    import torch
     rng = np.random.default_rng(2)
-    x = rng.standard_normal(5000)
-    allowed = rng.random(5000) < 0.5
-    i, lp, _ = O.sample_row(x, allowed, 0.7, 123, 4)
-    z = x / float(np.float32(0.7))
-    m = z[allowed].max()
-    want = z[i] - (m + np.log(np.exp(z[allowed] - m).sum()))
-    assert allowed[i] and abs(lp - want) < 1e-12
+    for V, T, scale in ((5000, 0.7, 1.0), (130000, 0.7, 3.0), (777, 1.0, 8.0), (4096, 0.05, 1.0)):
+        x = rng.standard_normal(V) * scale
+        if V == 130000:
+            x = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+        allowed = rng.random(V) < 0.5
+        for seed in (123, 9):
+            i, lp, _ = O.sample_row(x, allowed, T, seed, 4)
+            xt = torch.from_numpy(x)
+            z = torch.where(torch.from_numpy(allowed), xt / float(np.float32(T)),
+                            torch.tensor(-float("inf"), dtype=torch.float64))
+            want = float(torch.log_softmax(z, 0)[i])
+            assert allowed[i] and abs(lp - want) < 1e-12
 
 
 def test_gumbel_uniform_open_interval():
