@@ -90,7 +90,8 @@ def lib():
         L.cg_fill_walk.argtypes = [vp, vp, i32, vp, i32, vp, vp]
         L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
         L.cg_last_error.restype = ctypes.c_char_p
-        for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask", "cg_sample_advance",
+        for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask",
+                     "cg_sample_advance",
                      "cg_sample_advance_fill", "cg_sample_advance_plan", "cg_fill_walk",
                      "cg_force_bytes", "cg_eval_calc", "cg_fill_draft", "cg_contract_model_spec",
                      "cg_contract_reverse",
@@ -126,6 +127,15 @@ def _dev(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims")
+    return t
+
+
+def _states(t, name="states"):
+    """Rows of cg_state: a contiguous [B, 24] uint8 device tensor."""
+    import torch
+    _dev(t, torch.uint8, name, 2)
+    if t.shape[1] != STATE_BYTES:
+        raise ValueError(f"{name} must be [B, {STATE_BYTES}] (cg_state rows)")
     return t
 
 
@@ -174,7 +184,7 @@ class Grammar:
 
     def init_state(self, states, stream=None):
         import torch
-        _dev(states, torch.uint8, "states", 2)
+        _states(states)
         _check(lib().cg_init_state(self._h, _ptr(states), states.shape[0], _stream(stream)))
 
     def fill_workspace_bytes(self, B: int) -> int:
@@ -188,7 +198,7 @@ class Grammar:
     def fill_bitmask(self, states, mask, workspace=None, stream=None):
         """workspace: from new_fill_workspace(B); None allocates one for this call."""
         import torch
-        _dev(states, torch.uint8, "states", 2)
+        _states(states)
         _dev(mask, torch.int64, "mask", 2)
         if mask.shape[0] < states.shape[0]:
             raise ValueError("mask has fewer rows than states")
@@ -217,7 +227,7 @@ class Grammar:
         _dev(mask, torch.int64, "mask", 2)
         _dev(temperature, torch.float32, "temperature", 1)
         _dev(seed, torch.int64, "seed", 1)
-        _dev(states, torch.uint8, "states", 2)
+        _states(states)
         for t, n in ((steps, "steps"), (out_ids, "out_ids"), (status, "status")):
             _dev(t, torch.int32, n, 1)
         _dev(out_logprob, torch.float32, "out_logprob", 1)
@@ -250,7 +260,7 @@ class Grammar:
         _dev(mask, torch.int64, "mask", 2)
         _dev(temperature, torch.float32, "temperature", 1)
         _dev(seed, torch.int64, "seed", 1)
-        _dev(states, torch.uint8, "states", 2)
+        _states(states)
         for t, n in ((steps, "steps"), (out_ids, "out_ids"), (status, "status")):
             _dev(t, torch.int32, n, 1)
         _dev(out_logprob, torch.float32, "out_logprob", 1)
@@ -273,15 +283,20 @@ class Grammar:
         """cg_fill_walk: the second launch of sample_advance_fill (after
         split=True, with the same mask and fill workspace)."""
         import torch
-        _dev(states, torch.uint8, "states", 2)
+        _states(states)
         _dev(mask, torch.int64, "mask", 2)
         B = states.shape[0]
+        if mask.shape[0] < B:
+            raise ValueError("mask has fewer rows than states")
+        _dev(workspace, None, "workspace")
+        if workspace.numel() * workspace.element_size() < self.fill_workspace_bytes(B):
+            raise ValueError("fill workspace too small")
         _check(lib().cg_fill_walk(self._h, _ptr(states), B, _ptr(mask), mask.shape[1], _ptr(workspace),
                                   _stream(stream)))
 
     def advance(self, states, ids, steps, status, stream=None):
         import torch
-        _dev(states, torch.uint8, "states", 2)
+        _states(states)
         for t, n in ((ids, "ids"), (steps, "steps"), (status, "status")):
             _dev(t, torch.int32, n, 1)
             if t.shape[0] < states.shape[0]:
@@ -297,13 +312,15 @@ class Grammar:
         uint8; masks [B, k+1, W] int64; accept_len [B] int32; steps [B] int32
         or None."""
         import torch
-        _dev(states, torch.uint8, "states", 2)
+        _states(states)
         B = states.shape[0]
         _dev(draft, torch.int32, "draft", 2)
         k = draft.shape[1]
         if draft.shape[0] < B:
             raise ValueError("draft has fewer rows than states")
         _dev(path_states, torch.uint8, "path_states", 3)
+        if path_states.shape[2] != STATE_BYTES:
+            raise ValueError(f"path_states must be [B, k+1, {STATE_BYTES}]")
         _dev(masks, torch.int64, "masks", 3)
         _dev(accept_len, torch.int32, "accept_len", 1)
         if steps is not None:
@@ -322,7 +339,7 @@ class Grammar:
         """cg_force_bytes: row r walks data[offsets[r]:offsets[r+1]] (uint8 /
         int32 device tensors, offsets has B+1 entries)."""
         import torch
-        _dev(states, torch.uint8, "states", 2)
+        _states(states)
         B = states.shape[0]
         _dev(data, torch.uint8, "data", 1)
         _dev(offsets, torch.int32, "offsets", 1)

@@ -334,3 +334,31 @@ def test_fill_token_length_classes(max_len):
     want, _ = oracle_masks(og, rows, blob, off)
     got = gpu_masks(g, st)
     assert np.array_equal(got[:, :want.shape[1]], want)
+
+
+def test_binding_rejects_bad_shapes():
+    """The binding refuses buffers the kernels would read or write past:
+    rows of the wrong width, a mask or a fill workspace too small for the
+    batch (fill_walk included)."""
+    import torch
+    say("binding shapes")
+    blob, off = W.make_vocab(3, 4096)
+    g = cg.Grammar(W.spec_json(3), blob, off, gen_cap=W.GEN_CAP)
+    B = 8
+    st = g.new_states(B)
+    g.init_state(st)
+    mask = torch.zeros((B, g.W), dtype=torch.int64, device="cuda")
+    fws = g.new_fill_workspace(B)
+    g.fill_bitmask(st, mask, fws)
+    bad = torch.zeros((B, cg.STATE_BYTES + 8), dtype=torch.uint8, device="cuda")
+    for call in (lambda: g.fill_bitmask(bad, mask, fws), lambda: g.init_state(bad),
+                 lambda: g.fill_walk(bad, mask, fws)):
+        with pytest.raises(ValueError):
+            call()
+    with pytest.raises(ValueError):
+        g.fill_walk(st, mask[:B - 1], fws)
+    with pytest.raises(ValueError):
+        g.fill_walk(st, mask, g.new_fill_workspace(1)[:1])
+    with pytest.raises(ValueError):
+        g.fill_bitmask(st, mask, g.new_fill_workspace(1)[:1])
+    torch.cuda.synchronize()

@@ -291,3 +291,4 @@ def test_grammar_cache():
     assert cg.cache_stats()[0] <= e0 + 8
     cg.cache_clear()
     assert cg.cache_stats()[0] == e0
+
