@@ -215,6 +215,22 @@ size_t cg_fill_workspace_bytes(const cg_grammar *g, int32_t batch);
 int cg_fill_bitmask(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
                     int32_t words_per_row, void *d_workspace, void *stream);
 
+/*
+ * cg_fill_bitmask for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that forbid allocation): the same
+ * arguments without the workspace, the same masks.  The per-row tile lists
+ * live in a device array inside the library, one per device, of
+ * CG_FILL_NOALLOC_SCRATCH_BYTES; its address is taken when a grammar is
+ * first compiled on that device.  Every call on a device shares that array,
+ * so calls on one device must not overlap in time (two streams running
+ * them at once race); the array needs no initialisation.
+ * CG_E_LIMIT (nothing launched) when cg_fill_workspace_bytes(g, batch)
+ * exceeds the array; CG_E_DEVICE if its address could not be taken.
+ */
+#define CG_FILL_NOALLOC_SCRATCH_BYTES (16u << 20)
+int cg_fill_bitmask_noalloc(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
+                            int32_t words_per_row, void *stream);
+
 /* Longest draft cg_fill_draft takes. */
 #define CG_MAX_DRAFT 64
 

@@ -19,13 +19,14 @@ FLAG_DONE, FLAG_CAPPED = 1, 2
 HOST_ONLY = 1
 STATE_BYTES = 24
 DTYPE_F32, DTYPE_BF16 = 0, 1
+FILL_NOALLOC_SCRATCH_BYTES = 16 << 20  # CG_FILL_NOALLOC_SCRATCH_BYTES
 
 # Symbols the C ABI (include/cg.h) exports.
 EXPORTS = ["cg_compile_grammar", "cg_free_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_workspace_bytes",
            "cg_fill_bitmask", "cg_sample_advance", "cg_sample_advance_fill",
            "cg_sample_advance_plan", "cg_fill_walk", "cg_force_bytes", "cg_eval_calc", "cg_draft_workspace_bytes",
            "cg_fill_draft", "cg_contract_model_spec", "cg_contract_reverse", "cg_cache_stats", "cg_cache_clear",
-           "cg_eval_strop",
+           "cg_eval_strop", "cg_fill_bitmask_noalloc",
            "cg_sample_workspace_bytes", "cg_apply_mask_sample", "cg_advance", "cg_try_input", "cg_last_error"]
 
 
@@ -66,6 +67,7 @@ def lib():
         L.cg_fill_workspace_bytes.argtypes = [vp, i32]
         L.cg_fill_workspace_bytes.restype = sz
         L.cg_fill_bitmask.argtypes = [vp, vp, i32, vp, i32, vp, vp]
+        L.cg_fill_bitmask_noalloc.argtypes = [vp, vp, i32, vp, i32, vp]
         L.cg_sample_workspace_bytes.argtypes = [i32, i32]
         L.cg_sample_workspace_bytes.restype = sz
         L.cg_apply_mask_sample.argtypes = [vp, i32, i32, i32, i64, vp, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -91,7 +93,7 @@ def lib():
         L.cg_try_input.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_int)]
         L.cg_last_error.restype = ctypes.c_char_p
         for name in ("cg_compile_grammar", "cg_grammar_info", "cg_init_state", "cg_fill_bitmask",
-                     "cg_sample_advance",
+                     "cg_fill_bitmask_noalloc", "cg_sample_advance",
                      "cg_sample_advance_fill", "cg_sample_advance_plan", "cg_fill_walk",
                      "cg_force_bytes", "cg_eval_calc", "cg_fill_draft", "cg_contract_model_spec",
                      "cg_contract_reverse",
@@ -209,6 +211,18 @@ class Grammar:
             raise ValueError("fill workspace too small")
         _check(lib().cg_fill_bitmask(self._h, _ptr(states), B, _ptr(mask), mask.shape[1], _ptr(workspace),
                                      _stream(stream)))
+
+    def fill_bitmask_noalloc(self, states, mask, stream=None):
+        """cg_fill_bitmask_noalloc: fill_bitmask with the library's own
+        per-device scratch (no workspace; calls on one device must not
+        overlap)."""
+        import torch
+        _states(states)
+        _dev(mask, torch.int64, "mask", 2)
+        if mask.shape[0] < states.shape[0]:
+            raise ValueError("mask has fewer rows than states")
+        _check(lib().cg_fill_bitmask_noalloc(self._h, _ptr(states), states.shape[0], _ptr(mask), mask.shape[1],
+                                             _stream(stream)))
 
     def sample_advance(self, logits, mask, temperature, seed, steps, workspace, out_ids, out_logprob, states,
                        status, stream=None):

@@ -20,6 +20,9 @@ int launch_force(const cg_grammar *g, cg_state *states, int B, const uint8_t *by
                  const uint32_t *offsets, int32_t *status, hipStream_t st);
 int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws,
                 hipStream_t st);
+int noalloc_setup(int dev);
+int launch_fill_noalloc(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr,
+                        hipStream_t st);
 int launch_draft(const cg_grammar *g, const cg_state *states, const int32_t *steps, int B, const int32_t *draft,
                  int kd, cg_state *path, int32_t *accept_len, hipStream_t st);
 int fill_plan_stride(const cg_grammar *g);
@@ -556,6 +559,9 @@ int compile_uncached(const char *spec_json, size_t spec_len, const uint8_t *tok_
             return CG_E_DEVICE;
         }
         g->device = dev;
+        // the address of cg_fill_bitmask_noalloc's scratch array on this
+        // device, taken once (a failure is reported by that call)
+        (void)noalloc_setup(dev);
         if (hipDeviceGetAttribute(&g->n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || g->n_cu < 1)
             g->n_cu = 256;
         const size_t V = (size_t)vocab_size;
@@ -727,6 +733,14 @@ int cg_fill_bitmask(const cg_grammar *g, const cg_state *d_states, int32_t batch
     if (batch > 0 && (!d_workspace || (uintptr_t)d_workspace % 16))
         return arg_error("workspace must be a 16-byte aligned device buffer of cg_fill_workspace_bytes bytes");
     return launch_fill(g, d_states, batch, d_mask, words_per_row, d_workspace, (hipStream_t)stream);
+}
+
+int cg_fill_bitmask_noalloc(const cg_grammar *g, const cg_state *d_states, int32_t batch, uint64_t *d_mask,
+                            int32_t words_per_row, void *stream) {
+    if (!on_device(g)) return arg_error("grammar has no device tables");
+    if (batch < 0 || (batch > 0 && (!d_states || !d_mask))) return arg_error("bad states / mask / batch");
+    if (words_per_row < (g->V + 63) / 64) return arg_error("words_per_row < ceil(vocab_size / 64)");
+    return launch_fill_noalloc(g, d_states, batch, d_mask, words_per_row, (hipStream_t)stream);
 }
 
 size_t cg_draft_workspace_bytes(const cg_grammar *g, int32_t batch, int32_t k) {

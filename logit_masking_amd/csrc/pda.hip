@@ -14,6 +14,7 @@
 // Nothing here is a dense contraction, so there is no MFMA: the work is
 // table lookups, integer ALU and latency.
 #include <algorithm>
+#include <mutex>
 
 #include "cg_internal.hpp"
 #include "fill_plan.hpp"
@@ -584,6 +585,71 @@ int launch_fill_walk(const cg_grammar *g, const FillArgs &a, hipStream_t st) {
     case 7: return launch_walk_nw<7>(g, a, st);
     default: return launch_walk_nw<8>(g, a, st);
     }
+}
+
+// ---------------------------------------------------------------------------
+// The fill's per-row tile lists in a file-scope device array, for callers
+// that cannot allocate (code under graph capture, serving loops that forbid
+// allocation): cg_fill_bitmask_noalloc.  Every device the library runs on
+// holds one copy for the life of the process; every call on a device shares
+// it, so such calls must not overlap in time on one device.  Nothing in it
+// needs clearing: the plan writes each row's count and list before the walk
+// reads them.  In host code the array's name is not a device address: the
+// address is taken once per device with hipGetSymbolAddress and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)CG_FILL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / sizeof(uint32_t)];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void *scratch_ptr[kMaxDevices];  // per device; null until set up
+static bool scratch_tried[kMaxDevices];
+
+// Called with device `dev` current (cg_compile_grammar uploads a grammar's
+// tables there).  Returns CG_OK once the device's address is known.
+int noalloc_setup(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("fill_bitmask_noalloc: device %d out of range", dev);
+        return CG_E_DEVICE;
+    }
+    std::lock_guard<std::mutex> lk(scratch_mu);
+    if (scratch_ptr[dev]) return CG_OK;
+    if (!scratch_tried[dev]) {
+        scratch_tried[dev] = true;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e == hipSuccess && p) scratch_ptr[dev] = p;
+        else (void)hipGetLastError();
+    }
+    if (!scratch_ptr[dev]) {
+        set_error("fill_bitmask_noalloc: no address for the scratch array on device %d", dev);
+        return CG_E_DEVICE;
+    }
+    return CG_OK;
+}
+
+int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws,
+                hipStream_t st);
+
+int launch_fill_noalloc(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr,
+                        hipStream_t st) {
+    if (B == 0) return CG_OK;
+    const size_t need = (size_t)B * (size_t)fill_plan_stride(g) * sizeof(uint32_t);
+    if (need > kScratchBytes) {
+        set_error("fill_bitmask_noalloc: %d rows need %zu bytes of scratch, the limit is %zu (use cg_fill_bitmask "
+                  "with a workspace)", B, need, kScratchBytes);
+        return CG_E_LIMIT;
+    }
+    void *p = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(scratch_mu);
+        if (g->device >= 0 && g->device < kMaxDevices) p = scratch_ptr[g->device];
+    }
+    if (!p) {
+        set_error("fill_bitmask_noalloc: the scratch array of device %d is not set up", g->device);
+        return CG_E_DEVICE;
+    }
+    return launch_fill(g, states, B, mask, wpr, p, st);
 }
 
 int launch_fill(const cg_grammar *g, const cg_state *states, int B, uint64_t *mask, int wpr, void *ws,

@@ -352,7 +352,7 @@ def test_binding_rejects_bad_shapes():
     g.fill_bitmask(st, mask, fws)
     bad = torch.zeros((B, cg.STATE_BYTES + 8), dtype=torch.uint8, device="cuda")
     for call in (lambda: g.fill_bitmask(bad, mask, fws), lambda: g.init_state(bad),
-                 lambda: g.fill_walk(bad, mask, fws)):
+                 lambda: g.fill_walk(bad, mask, fws), lambda: g.fill_bitmask_noalloc(bad, mask)):
         with pytest.raises(ValueError):
             call()
     with pytest.raises(ValueError):

@@ -292,3 +292,9 @@ def test_grammar_cache():
     cg.cache_clear()
     assert cg.cache_stats()[0] == e0
 
+
+def test_noalloc_scratch_constant():
+    """The binding's scratch size is the header's."""
+    src = open(os.path.join(ROOT, "include", "cg.h")).read()
+    m = re.search(r"#define CG_FILL_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == cg.FILL_NOALLOC_SCRATCH_BYTES
