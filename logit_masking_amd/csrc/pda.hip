@@ -562,13 +562,26 @@ int fill_check(const cg_grammar *g, int B) {
     return CG_OK;
 }
 
+// The walk kernels' dynamic-LDS limit per device as last raised (0: the
+// default): raised only when a launch needs more, so the per-step path makes
+// no attribute call.
+constexpr int kWalkMaxDevices = 64;
+static std::mutex walk_attr_mu;
+static int walk_lds_attr[kWalkMaxDevices][8];
+
 template <int NW>
 static int launch_walk_nw(const cg_grammar *g, const FillArgs &a, hipStream_t st) {
     const size_t lds = fill_lds_bytes(g, a.B);
-    if (lds > 64 * 1024 &&
-        hipFuncSetAttribute((const void *)k_fill_walk<NW>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-            hipSuccess)
-        return launch_status("fill_bitmask (LDS attribute)");
+    if (lds > 64 * 1024) {
+        std::lock_guard<std::mutex> lk(walk_attr_mu);
+        const bool known = g->device >= 0 && g->device < kWalkMaxDevices;
+        if (!known || (size_t)walk_lds_attr[g->device][NW - 1] < lds) {
+            if (hipFuncSetAttribute((const void *)k_fill_walk<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)lds) != hipSuccess)
+                return launch_status("fill_bitmask (LDS attribute)");
+            if (known) walk_lds_attr[g->device][NW - 1] = (int)lds;
+        }
+    }
     hipLaunchKernelGGL(k_fill_walk<NW>, dim3(g->n_cu), dim3(kWalkThreads), lds, st, a);
     return launch_status("fill_bitmask (walk)");
 }

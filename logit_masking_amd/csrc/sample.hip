@@ -12,6 +12,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "cg_internal.hpp"
 #include "fill_plan.hpp"
@@ -359,12 +360,25 @@ struct Slots {
 };
 
 // log-mass of chunk c recomputed entirely in double by the whole workgroup
+// (kWaves waves).  Every thread's mask bytes and logits are loaded before any
+// is used: one round trip, not one per id (a loop that loads the logit only
+// under its mask bit waits out two dependent round trips per id).
 template <int DT>
 __device__ double chunk_lse_exact(const void *logits, size_t rowbase, const uint8_t *mrow, int V, int c, double T,
                                   double m, double *slot) {
+    constexpr int kPer = kChunk / (kWaves * 64);
+    float x[kPer];
+    uint32_t mb[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+        const int e = c * kChunk + (int)threadIdx.x + j * kWaves * 64;
+        mb[j] = e < V ? (mrow[e >> 3] >> (e & 7)) & 1u : 0u;
+        x[j] = e < V ? load_logit<DT>(logits, rowbase + e) : 0.f;
+    }
     double s = 0.0;
-    for (int e = c * kChunk + (int)threadIdx.x; e < min(V, (c + 1) * kChunk); e += blockDim.x)
-        if ((mrow[e >> 3] >> (e & 7)) & 1u) s += exp(((double)load_logit<DT>(logits, rowbase + e) - m) / T);
+#pragma unroll
+    for (int j = 0; j < kPer; j++)
+        if (mb[j]) s += exp(((double)x[j] - m) / T);
     s = wave_sum_d(s);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = s;
@@ -477,7 +491,7 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
                                                  const uint64_t *mask, int words_per_row,
                                                  const float *__restrict__ temp, const uint64_t *__restrict__ seed,
-                                                 const int32_t *__restrict__ step, int K, int use_stash,
+                                                 const int32_t *step, int K, int use_stash,
                                                  int32_t *__restrict__ out_id, float *__restrict__ out_lp,
                                                  AdvanceArgs adv, FillArgs pa, int plan_next) {
     extern __shared__ uint64_t dyn[];
@@ -908,6 +922,39 @@ size_t sample_workspace_bytes(int B, int V) {
     return 0;  // partials live in LDS
 }
 
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex dev_mu;
+int dev_lds_max[kMaxDevices];         // 0: not asked yet
+int sample_lds_attr[kMaxDevices][4];  // k_sample<dtype, vec>'s dynamic-LDS limit as raised (0: default)
+
+// LDS a workgroup may use on a device, asked once per device
+int lds_max_of(int dev) {
+    std::lock_guard<std::mutex> lk(dev_mu);
+    if (dev < 0 || dev >= kMaxDevices) return 65536;
+    if (!dev_lds_max[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+            v = 65536;
+        dev_lds_max[dev] = v;
+    }
+    return dev_lds_max[dev];
+}
+
+// Raise a kernel's dynamic-LDS limit on a device only when a launch needs
+// more than it was last raised to (a grammar's launches all need the same
+// amount): no host call on the per-step path.
+int raise_lds_limit(const void *kern, int dev, int which, size_t lds) {
+    std::lock_guard<std::mutex> lk(dev_mu);
+    const bool known = dev >= 0 && dev < kMaxDevices;
+    if (known && (size_t)sample_lds_attr[dev][which] >= lds) return CG_OK;
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return launch_status("apply_mask_sample (LDS attribute)");
+    if (known) sample_lds_attr[dev][which] = (int)lds;
+    return CG_OK;
+}
+}  // namespace
+
 int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, const uint64_t *mask, int wpr,
                   const float *temp, const uint64_t *seed, const int32_t *step, void *ws, int32_t *out_id,
                   float *out_lp, const cg_grammar *g, cg_state *states, int32_t *steps_rw, int32_t *status,
@@ -921,10 +968,16 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
         set_error("apply_mask_sample: vocab above %d", kMaxChunks * kChunk);
         return CG_E_ARG;
     }
+    // the device and its LDS size: the grammar's (asked when it was compiled),
+    // else asked once per device
     int dev = 0, lds_max = 65536;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        lds_max = 65536;
+    if (g) {
+        dev = g->device;
+        lds_max = g->lds_max;
+    } else {
+        if (hipGetDevice(&dev) != hipSuccess) return launch_status("apply_mask_sample (device)");
+        lds_max = lds_max_of(dev);
+    }
     const size_t static_lds =
         4 * sizeof(Slots) + 256 * sizeof(uint4) + sizeof(RowDecision) + sizeof(PlanShared) + sizeof(cg_state) + 256;
     const size_t table = g ? (size_t)g->comb_len * 8 : 0;
@@ -960,9 +1013,10 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
     const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * es) % 16 == 0);
 #define CG_LAUNCH_SAMPLE(D, VV)                                                                                  \
     do {                                                                                                         \
-        if (lds > 64 * 1024 && hipFuncSetAttribute((const void *)k_sample<D, VV>,                                \
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) \
-            return launch_status("apply_mask_sample (LDS attribute)");                                           \
+        if (lds > 64 * 1024) {                                                                                   \
+            const int rc = raise_lds_limit((const void *)k_sample<D, VV>, dev, 2 * (D) + ((VV) ? 1 : 0), lds);    \
+            if (rc != CG_OK) return rc;                                                                          \
+        }                                                                                                        \
         hipLaunchKernelGGL((k_sample<D, VV>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask, wpr, \
                            temp, seed, step, K, use_stash, out_id, out_lp, adv, pa, plan_next);              \
     } while (0)

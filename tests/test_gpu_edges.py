@@ -72,7 +72,7 @@ def test_sample_vocab_over_limit():
     logits = torch.zeros((1, V), dtype=torch.bfloat16, device="cuda")
     mask = torch.zeros((1, (V + 63) // 64), dtype=torch.int64, device="cuda")
     one = lambda dt, v: torch.full((1,), v, dtype=dt, device="cuda")
-    ws = torch.zeros(2, dtype=torch.float64, device="cuda")
+    ws = cg.new_workspace(1, V)
     with pytest.raises(cg.CgError) as e:
         cg.apply_mask_sample(logits, mask, one(torch.float32, 0.7), one(torch.int64, 1), one(torch.int32, 0), ws,
                              one(torch.int32, 0), one(torch.float32, 0))
