@@ -72,65 +72,104 @@ def pct(a, q):
     return float(np.percentile(np.asarray(a), q))
 
 
-def cpu_baseline(ids_hist, B, V, blob, off, budget_s, cfg=CONFIG):
-    """The oracle as it stands, on a bounded sample of the same workload:
-    the first rows of the measured trajectory replayed on the host; at every
-    step each row still generating gets a full-vocabulary mask and a
-    float64 two-level sample, until the time budget is spent."""
+def cpu_baseline(rec, B, V, blob, off, budget_s, cfg=CONFIG):
+    """The oracle as it stands, on a bounded sample of the same workload, and
+    the run's own parity check: the checked rows of the measured trajectory
+    (rec["rows"]) are replayed on the host from the GPU's own logits.  At
+    every step each row still generating gets a full-vocabulary oracle mask
+    (compared word by word with the mask the device used) and a float64
+    two-level sample (compared with the device's pick and log-probability;
+    a pick whose oracle margin at either level is below 1e-6 is a near-tie,
+    counted apart); the row then takes the device's pick, whose status must
+    equal the oracle's.  Finished rows must have an empty mask and id -1.
+    Only the oracle's mask and sample work is timed, until the budget is
+    spent ("Constrained Decoding Under Matched Conditions", "The artifact
+    validator does not trust the remote summary": the run recounts its own
+    results)."""
     import logit_masking_amd.workloads as W
     from oracle import oracle as O
     og = O.load_spec(W.spec_json(cfg))
     toks = [blob[off[i]:off[i + 1]] for i in range(V)]
     threads = min(16, os.cpu_count() or 1)
-    nrows = threads
-    rows = [O.Row(og, W.GEN_CAP) for _ in range(nrows)]
+    chk = rec["rows"]
+    rows = [O.Row(og, W.GEN_CAP) for _ in chk]
     seeds = W.row_seeds(cfg, B)
     T = W.CONFIGS[cfg]["T"]
-    checks = walked = row_steps = 0
+    Wv = (V + 63) // 64
+    par = {"rows_checked": len(chk), "row_steps": 0, "steps_checked": 0, "mask_word_mismatches": 0,
+           "pick_mismatches": 0, "near_ties": 0, "max_logprob_err": 0.0, "status_mismatches": 0,
+           "finished_row_violations": 0, "blank_live_rows": 0}
+    checks = walked = 0
     t_cpu = t_mask = 0.0
-    last = 0
     t1 = None
-    for s in range(ids_hist.shape[0]):
-        live = [r for r in range(nrows) if not rows[r].done]
+    # the warmup steps before the measured trajectory: the rows follow the
+    # device's picks unchecked
+    for s in range(rec["pre_ids"].shape[0]):
+        for k in range(len(chk)):
+            i = int(rec["pre_ids"][s, chk[k]])
+            rows[k].advance(None if i < 0 else toks[i])
+    for s in range(rec["ids"].shape[0]):
+        live = [k for k in range(len(chk)) if not rows[k].done]
+        for k in range(len(chk)):
+            if rows[k].done and (rec["masks"][s, k, :Wv].any() or rec["ids"][s, chk[k]] != -1):
+                par["finished_row_violations"] += 1
         if not live or t_cpu >= budget_s:
             break
-        logits = W.make_logits(cfg, s, nrows, V, "cpu")
-        x = logits.float().numpy().astype(np.float64)
+        x = rec["x"][s]  # the checked rows' logits at this step, float32
         t0 = time.perf_counter()
-        words, w = og.mask_rows([rows[r].conf for r in live], [False] * len(live), blob, off, threads)
+        words, w = og.mask_rows([rows[k].conf for k in live], [False] * len(live), blob, off, threads)
         tm = time.perf_counter()
-        for k, r in enumerate(live):
-            O.sample_row(x[r], O.unpack_mask(words[k], V), T, seeds[r], rows[r].step)
+        res = [O.sample_row(x[k].astype(np.float64), O.unpack_mask(words[j], V), T, seeds[chk[k]], rows[k].step)
+               for j, k in enumerate(live)]
         t_cpu += time.perf_counter() - t0
         t_mask += tm - t0
         if s == 20:  # the same masks again on one thread (rows in mixed states by now)
             u0 = time.perf_counter()
-            og.mask_rows([rows[r].conf for r in live], [False] * len(live), blob, off, 1)
+            og.mask_rows([rows[k].conf for k in live], [False] * len(live), blob, off, 1)
             t1 = (len(live) * V, time.perf_counter() - u0, tm - t0)
         checks += len(live) * V
         walked += w
-        row_steps += len(live)
-        last = s
-        for r in range(nrows):
-            i = int(ids_hist[s, r])
-            rows[r].advance(None if i < 0 else toks[i])
-    return {
+        par["row_steps"] += len(live)
+        par["steps_checked"] = s + 1
+        for j, k in enumerate(live):
+            r = chk[k]
+            par["mask_word_mismatches"] += int(np.count_nonzero(rec["masks"][s, k, :Wv] != words[j][:Wv]))
+            if not words[j].any():
+                par["blank_live_rows"] += 1
+            i, lp, info = res[j]
+            gi, glp = int(rec["ids"][s, r]), float(rec["lp"][s, r])
+            near = T > 0 and min(info["margin_chunk"], info["margin_token"]) < 1e-6
+            par["near_ties"] += int(near)
+            if gi != i:
+                par["pick_mismatches"] += int(not near)
+            else:
+                par["max_logprob_err"] = max(par["max_logprob_err"], abs(glp - lp))
+            # the oracle row follows the device's pick
+            st = rows[k].advance(None if gi < 0 else toks[gi])
+            par["status_mismatches"] += int(st != int(rec["status"][s, r]))
+    par["rows_done"] = sum(int(r.complete) for r in rows)
+    par["rows_capped"] = sum(int(r.done and not r.complete) for r in rows)
+    par["max_logprob_err"] = float(f"{par['max_logprob_err']:.3g}")
+    base = {
         "value": checks / t_cpu if t_cpu > 0 else None,
         "unit": "token-checks/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"rows 0-{nrows - 1} of the measured trajectory, steps 0-{last}, every row still generating: "
-                  f"full-vocabulary mask + float64 two-level sample per row-step; {row_steps} row-steps, "
-                  f"{checks} token checks, {walked / max(1, checks):.2f} bytes walked per check, {t_cpu:.1f} s",
-        "us_per_row_step": 1e6 * t_cpu / max(1, row_steps),
+        "sample": f"rows {chk[0]}-{chk[-1]} of the measured trajectory on the device's own logits, steps "
+                  f"0-{par['steps_checked'] - 1}, every row still generating: full-vocabulary mask + float64 "
+                  f"two-level sample per row-step; {par['row_steps']} row-steps, {checks} token checks, "
+                  f"{walked / max(1, checks):.2f} bytes walked per check, {t_cpu:.1f} s",
+        "us_per_row_step": 1e6 * t_cpu / max(1, par["row_steps"]),
         "mask_token_checks_per_s": checks / t_mask if t_mask > 0 else None,
-        "sample_GBps": (row_steps * (2 * V + 8 * ((V + 63) // 64) + 8) / (t_cpu - t_mask) / 1e9
+        "sample_GBps": (par["row_steps"] * (2 * V + 8 * ((V + 63) // 64) + 8) / (t_cpu - t_mask) / 1e9
                         if t_cpu > t_mask else None),
         "mask_step20_token_checks_per_s": ({"threads": threads, "value": t1[0] / t1[2], "1_thread": t1[0] / t1[1]}
                                           if t1 and t1[1] > 0 and t1[2] > 0 else None),
+        "bytes_walked_per_check": walked / max(1, checks),
         "nproc": os.cpu_count(),
         "cpu_model": cpu_model(),
     }
+    return base, par
 
 
 def cpu_model():
@@ -523,6 +562,38 @@ def overlap_bench(args):
     print(json.dumps(out))
 
 
+def compile_times(args):
+    """--compile-times: cg_compile_grammar for every workload, the grammar
+    cache cleared first: the spec-to-automaton part and the whole call
+    (vocabulary tables, precomputed masks, upload), host wall-clock.  The
+    pages keep compilation out of latency with warm-up and ask that caching
+    keep it from blowing up ("Constrained Decoding Under Matched Conditions";
+    "Evaluator aware decoding", "Where XGrammar-2 could take this").  Prints
+    one JSON line."""
+    import torch
+    import logit_masking_amd as cg
+    from logit_masking_amd import workloads as W
+    torch.cuda.set_device(0)
+    res = {}
+    for cfg in sorted(W.SPECS):
+        blob, off = W.make_vocab(cfg)
+        cg.cache_clear()
+        t0 = time.perf_counter()
+        g = cg.Grammar(W.spec_json(cfg), blob, off, gen_cap=W.GEN_CAP)
+        wall = 1e3 * (time.perf_counter() - t0)
+        info = g.info()
+        t1 = time.perf_counter()
+        g2 = cg.Grammar(W.spec_json(cfg), blob, off, gen_cap=W.GEN_CAP)  # answered from the cache
+        cached = 1e3 * (time.perf_counter() - t1)
+        res[str(cfg)] = {"vocab": len(off) - 1, "automaton_ms": round(info["compile_ms"], 2),
+                         "total_ms": round(info["total_ms"], 2), "binding_wall_ms": round(wall, 2),
+                         "cached_ms": round(cached, 3), "table_bytes": info["table_bytes"],
+                         "state_masks": info["state_masks"]}
+        del g, g2
+    print(json.dumps({"metric": "cg_compile_grammar time per workload (ms)", "unit": "ms", "n_gpus": 1,
+                      "higher_is_better": False, "data": "synthetic", "configs": res}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -548,6 +619,8 @@ def main():
                     help="measure the fill on a second stream behind a stand-in lm_head product (its own JSON line)")
     ap.add_argument("--inject", action="store_true",
                     help="measure result injection on text with calc spans instead (its own JSON line)")
+    ap.add_argument("--compile-times", action="store_true",
+                    help="time cg_compile_grammar for every workload instead (its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: rows shard across GPUs with no exchange, and runs on more than one "
@@ -556,6 +629,9 @@ def main():
 
     if args.inject:
         inject_bench(args)
+        return
+    if args.compile_times:
+        compile_times(args)
         return
     if args.draft:
         draft_bench(args)
@@ -685,6 +761,39 @@ def main():
     step_ms = np.array([evb[k].elapsed_time(evb[k + 1]) for k in range(args.steps)])
     assert np.array_equal(steps.cpu().numpy(), st_h), "replay diverged from the timed trajectory"
 
+    # and once more, recording for the parity check (the checked rows' masks
+    # as the sampler reads them, every row's pick, log-probability and
+    # status) with cg_fill_bitmask timed on the same states before each step
+    # (the fill's own rate; in the fused step its plan runs inside the
+    # sampler's launch)
+    st.copy_(st0)
+    steps.copy_(steps0)
+    mask.copy_(mask0)
+    chk = list(range(min(16, B)))
+    chk_t = torch.tensor(chk, dtype=torch.long, device=dev)
+    rec_mask = torch.empty((args.steps, len(chk), g.W), dtype=torch.int64, device=dev)
+    rec_lp = torch.empty((args.steps, B), dtype=torch.float32, device=dev)
+    rec_status = torch.empty((args.steps, B), dtype=torch.int32, device=dev)
+    fmask = torch.empty_like(mask)
+    fused_mask_diff = torch.zeros((), dtype=torch.int64, device=dev)
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        evf[k][0].record(stream)
+        g.fill_bitmask(st, fmask, fws, stream)
+        evf[k][1].record(stream)
+        if fused_fill:
+            rec_mask[k].copy_(mask.index_select(0, chk_t))
+            fused_mask_diff += (fmask[:, :g.W] != mask[:, :g.W]).sum()
+        else:
+            rec_mask[k].copy_(fmask.index_select(0, chk_t))
+        step(args.warmup + k)
+        rec_lp[k].copy_(lp)
+        rec_status[k].copy_(status)
+    torch.cuda.synchronize()
+    assert np.array_equal(steps.cpu().numpy(), st_h), "replay diverged from the timed trajectory"
+    fillb_ms = np.array([e[0].elapsed_time(e[1]) for e in evf])
+
     # masked sample: every logit (bf16) and mask word read once, id + logprob
     # written; fused, also each row's state, step and status
     sample_bytes = B * V * es + B * g.W * 8 + B * 8
@@ -693,7 +802,7 @@ def main():
     if fused_fill:
         sample_bytes += B * g.W * 8  # the next mask's words, written once by the plan
     sample_gbps = sample_bytes / (samp_ms.mean() * 1e-3) / 1e9
-    fill_checks = B * V / (fill_ms.mean() * 1e-3)
+    fill_checks = B * V / (fillb_ms.mean() * 1e-3)
     dominant = "fill_bitmask" if fill_ms.mean() >= samp_ms.mean() else "mask_softmax_sample"
     kernel_name = ("k_sample (mask_softmax_sample)" if args.separate
                    else "k_sample (mask_softmax_sample + advance, one launch)" if not fused_fill
@@ -725,7 +834,11 @@ def main():
         "step": ("cg_sample_advance_fill (sample + advance + next plan; walk)" if fused_fill
                  else "cg_fill_bitmask; cg_apply_mask_sample; cg_advance" if args.separate
                  else "cg_fill_bitmask; cg_sample_advance"),
-        "fill_token_checks_per_s": None if fused_fill else round(fill_checks, 1),
+        "fill_token_checks_per_s": round(fill_checks, 1),
+        "us_fill_bitmask": {"mean": round(1e3 * fillb_ms.mean(), 2), "p50": round(1e3 * pct(fillb_ms, 50), 2),
+                            "p99": round(1e3 * pct(fillb_ms, 99), 2),
+                            "note": "cg_fill_bitmask (plan + walk launches) on the trajectory's states before each "
+                                    "step, events around the call"},
         "masked_sample_GBps": round(sample_gbps, 1),
         "masked_sample_frac_hbm": round(sample_gbps / HBM_PEAK_GBPS, 4),
         "us_per_step": {"mean": round(1e3 * ms_per_step, 2), "p50": round(1e3 * pct(step_ms, 50), 2),
@@ -741,6 +854,7 @@ def main():
         "rows_capped": int(((flags & 2) > 0).sum()),
         "tokens_accepted_mean": float(st_h.mean()),
         "compile_ms": round(info["compile_ms"], 2),
+        "compile_total_ms": round(info["total_ms"], 2),
         "table_bytes": info["table_bytes"],
         "roofline": roofline,
     }
@@ -769,8 +883,24 @@ def main():
             torch.neg(src, out=dst)  # an elementwise kernel: reads and writes 64 MiB
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = src.numel() * 2
+    if fused_fill:
+        out["fused_mask_equals_fill_bitmask"] = int(fused_mask_diff.item()) == 0
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(ids_hist.cpu().numpy(), B, V, blob, off, args.cpu_budget, cfg)
+        xs = {}
+        for k in range(args.steps):  # the checked rows' logits of every pool buffer the trajectory used
+            i = (args.warmup + k) % npool
+            if i not in xs:
+                xs[i] = pool[i].index_select(0, chk_t).float().cpu().numpy()
+        rec = {"rows": chk, "masks": rec_mask.cpu().numpy().view(np.uint64),
+               "pre_ids": ids_hist[:args.warmup].cpu().numpy(), "ids": ids_hist[args.warmup:].cpu().numpy(),
+               "lp": rec_lp.cpu().numpy(), "status": rec_status.cpu().numpy(),
+               "x": [xs[(args.warmup + k) % npool] for k in range(args.steps)]}
+        base, par = cpu_baseline(rec, B, V, blob, off, args.cpu_budget, cfg)
+        out["cpu_baseline"] = base
+        out["parity"] = par
+        # the fill's byte-steps: the oracle's mean bytes walked per token check
+        # on the checked rows times the fill's token-checks/s
+        out["fill_byte_steps_per_s"] = round(base["bytes_walked_per_check"] * fill_checks, 1)
     print(json.dumps(out))
 
 

@@ -111,6 +111,9 @@ typedef struct {
     int32_t state_masks;    /* states whose plain-configuration mask was computed once at
                                compile time (0: none, or the table would exceed 64 MiB) */
     int32_t pad;
+    double total_ms;        /* the whole cg_compile_grammar call that built the handle: the
+                               automaton, the vocabulary tables, the precomputed masks and
+                               the upload (a cached handle keeps its first compile's time) */
 } cg_info;
 
 /*

@@ -44,7 +44,8 @@ class Info(ctypes.Structure):
     _fields_ = [("vocab_size", ctypes.c_int32), ("words_per_row", ctypes.c_int32),
                 ("max_token_len", ctypes.c_int32), ("n_states", ctypes.c_int32),
                 ("table_entries", ctypes.c_int32), ("table_bytes", ctypes.c_int32),
-                ("compile_ms", ctypes.c_double), ("state_masks", ctypes.c_int32), ("pad", ctypes.c_int32)]
+                ("compile_ms", ctypes.c_double), ("state_masks", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
 
 
 _lib = None

@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <functional>
 #include <mutex>
 #include <string>
@@ -660,8 +661,10 @@ int cg_compile_grammar(const char *spec_json, size_t spec_len, const uint8_t *to
             }
     }
     g_misses++;
+    const auto t0 = std::chrono::steady_clock::now();
     const int rc = compile_uncached(spec_json, spec_len, tok_bytes, tok_offsets, vocab_size, opts, out);
     if (rc != CG_OK) return rc;
+    (*out)->total_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     g_cache.push_back(CacheEntry{std::string(spec_json, spec_len), h1, h2, vocab_size, gen_cap, flags, device, *out, 0});
     return CG_OK;
 }
@@ -709,6 +712,7 @@ int cg_grammar_info(const cg_grammar *g, cg_info *info) {
     info->table_entries = (int32_t)g->comb_len;
     info->table_bytes = (int32_t)(g->comb_len * sizeof(uint64_t));
     info->compile_ms = g->compile_ms;
+    info->total_ms = g->total_ms;
     info->state_masks = g->n_smask;
     info->pad = 0;
     return CG_OK;

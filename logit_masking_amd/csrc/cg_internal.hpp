@@ -285,7 +285,8 @@ struct cg_grammar {
     int lds_max = 65536;     // LDS bytes a workgroup may use on that device
     int32_t lex_tiles = 0;   // candidate tiles of the lexicographic list
     int32_t q_tiles = 0;     // and of the string-closing list
-    double compile_ms = 0;
+    double compile_ms = 0;   // spec -> automaton (parse, build, trim, pack)
+    double total_ms = 0;     // the whole cg_compile_grammar call that built the handle
     uint64_t *host_comb = nullptr;
     std::vector<uint32_t> host_forced;  // bit q: state q is inside an engine-written region
     bool has_forced = false;

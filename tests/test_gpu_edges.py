@@ -49,6 +49,7 @@ def _check(x, bits, T, seeds, step, ids, lp):
             continue
         assert ids[r] == i, (r, ids[r], i)
         assert abs(lp[r] - l) < 1e-5, (r, lp[r], l)
+    say("near-ties", ties, "of", x.shape[0], "rows")
     return ties
 
 

@@ -85,6 +85,7 @@ def test_full_size_step_against_oracle(cfg):
         rows1.append(row)
     want1, _ = oracle_masks(og, rows1, blob, off)
     assert np.array_equal(mask1[:, :want1.shape[1]], want1)
+    say("near-ties", ties)
     assert ties <= 2
 
 
@@ -145,4 +146,5 @@ def test_full_size_trajectory_tool_call():
             if i >= 0:
                 orows[k].advance(toks[i])
                 taken += 1
+    say("near-ties", ties, "of", taken, "sampled picks")
     assert ties <= 2 and taken > 100

@@ -322,6 +322,7 @@ def test_decode_loop_with_injection(fused, T, cfg):
     assert stepc.cpu().numpy().tolist() == [r.step for r in orows]
     assert [bytes(t) for t in dev_text] == [bytes(r.text) for r in orows]
     assert injections >= B // 2, injections
+    say("near-ties", ties)
     assert ties <= 2
     say("inject loop", fused, T, "injections", injections, "done", sum(r.done for r in orows))
 

@@ -313,6 +313,7 @@ def test_sample_parity(torch_dev, cfg, B, V, T):
             continue
         assert ids[r] == i, (r, ids[r], i, info)
         assert abs(lp[r] - l) < LOGPROB_TOL, (r, lp[r], l)
+    say("near-ties", cfg, B, V, T, ties)
     assert ties <= max(1, B // 10)
 
 
@@ -421,4 +422,5 @@ def test_design_mask_parity(torch_dev, design):
             else:
                 assert ids_dev[r] == i and (i < 0 or abs(lp_dev[r] - l) < LOGPROB_TOL)
             assert stat[r] == rows[r].advance(None if ids_dev[r] < 0 else toks[ids_dev[r]])
+    say("near-ties (trajectory)", ties)
     assert ties <= 2
