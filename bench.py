@@ -115,7 +115,9 @@ def cpu_baseline(rec, B, V, blob, off, budget_s, cfg=CONFIG):
                 par["finished_row_violations"] += 1
         if not live or t_cpu >= budget_s:
             break
-        x = rec["x"][s]  # the checked rows' logits at this step, float32
+        x = rec["x"][s]  # the checked rows' logits at this step (bf16 bits or float32)
+        if x.dtype == np.uint16:
+            x = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
         t0 = time.perf_counter()
         words, w = og.mask_rows([rows[k].conf for k in live], [False] * len(live), blob, off, threads)
         tm = time.perf_counter()
@@ -722,6 +724,7 @@ def main():
     for k in range(args.steps):
         step(args.warmup + k)
     end_ev.record(stream)
+    t_enq = time.perf_counter() - t0  # host time to enqueue the K steps (no synchronisation inside)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region_ms = start_ev.elapsed_time(end_ev)
@@ -761,15 +764,15 @@ def main():
     step_ms = np.array([evb[k].elapsed_time(evb[k + 1]) for k in range(args.steps)])
     assert np.array_equal(steps.cpu().numpy(), st_h), "replay diverged from the timed trajectory"
 
-    # and once more, recording for the parity check (the checked rows' masks
-    # as the sampler reads them, every row's pick, log-probability and
-    # status) with cg_fill_bitmask timed on the same states before each step
-    # (the fill's own rate; in the fused step its plan runs inside the
+    # and once more, recording for the parity check (the masks of rows 0-63
+    # as the sampler reads them; every row's pick, log-probability and
+    # status), with cg_fill_bitmask timed on the same states before each
+    # step (the fill's own rate; in the fused step its plan runs inside the
     # sampler's launch)
     st.copy_(st0)
     steps.copy_(steps0)
     mask.copy_(mask0)
-    chk = list(range(min(16, B)))
+    chk = list(range(min(64, B)))
     chk_t = torch.tensor(chk, dtype=torch.long, device=dev)
     rec_mask = torch.empty((args.steps, len(chk), g.W), dtype=torch.int64, device=dev)
     rec_lp = torch.empty((args.steps, B), dtype=torch.float32, device=dev)
@@ -849,6 +852,7 @@ def main():
                       "p99": round(1e3 * pct(samp_ms, 99), 2)},
         "us_advance": {"mean": round(1e3 * adv_ms.mean(), 2)} if args.separate else "fused into us_sample",
         "wall_us_per_step": round(1e6 * wall / args.steps, 2),
+        "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
         "dominant_kernel": dominant,
         "rows_done": int((flags & 1).sum()),
         "rows_capped": int(((flags & 2) > 0).sum()),
@@ -889,8 +893,10 @@ def main():
         xs = {}
         for k in range(args.steps):  # the checked rows' logits of every pool buffer the trajectory used
             i = (args.warmup + k) % npool
-            if i not in xs:
-                xs[i] = pool[i].index_select(0, chk_t).float().cpu().numpy()
+            if i not in xs:  # bf16 as its bits (uint16), float32 as is
+                x = pool[i].index_select(0, chk_t)
+                xs[i] = (x.view(torch.int16).cpu().numpy().view(np.uint16) if x.dtype == torch.bfloat16
+                         else x.cpu().numpy())
         rec = {"rows": chk, "masks": rec_mask.cpu().numpy().view(np.uint64),
                "pre_ids": ids_hist[:args.warmup].cpu().numpy(), "ids": ids_hist[args.warmup:].cpu().numpy(),
                "lp": rec_lp.cpu().numpy(), "status": rec_status.cpu().numpy(),
