@@ -165,13 +165,14 @@ __device__ inline void wave_argmax(double &v, int &i) {
 
 // Lane l holds, in group g = 0..3, the ids c*2048 + g*512 + 8l + j (j =
 // 0..7): every load instruction covers a contiguous 1 KB (bf16) or 2 KB
-// (float32, two instructions per group) of the row, and group g's mask
-// bits are the byte c*256 + 64g + l of the row's mask, one byte load per
-// group, also contiguous across the lanes.
+// (float32, two instructions per group) of the row.  The chunk's 256 mask
+// bytes come in one dword load per lane (lane l: bytes 4l .. 4l + 3), so a
+// chunk in flight holds 17 (bf16) or 33 registers; group g's byte for lane
+// l, 64g + l, is fetched from lane 16g + l/4 when the chunk is reduced.
 template <int DT>
 struct ChunkRegs {
     uint32_t d[DT == 1 ? 16 : 32];
-    uint32_t mb[4];
+    uint32_t mw;
 };
 
 // Bounds-checked load (rows whose storage is not 16-byte aligned): ids past
@@ -179,11 +180,17 @@ struct ChunkRegs {
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_chunk(ChunkRegs<DT> &R, const void *logits, size_t rowbase,
                                            const uint8_t *mrow, int V, int c, int lane) {
+    R.mw = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int f0 = c * kChunk + lane * 32 + 8 * i;  // the ids of mask byte 4 lane + i
+        uint32_t b = (f0 < V) ? mrow[f0 >> 3] : 0u;
+        if (f0 + 8 > V) b &= (f0 >= V) ? 0u : ((1u << (V - f0)) - 1u);
+        R.mw |= b << (8 * i);
+    }
 #pragma unroll
     for (int g = 0; g < 4; g++) {
         const int e0 = c * kChunk + g * 512 + lane * 8;
-        R.mb[g] = (e0 < V) ? mrow[e0 >> 3] : 0u;
-        if (e0 + 8 > V) R.mb[g] &= (e0 >= V) ? 0u : ((1u << (V - e0)) - 1u);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const float x = (e0 + j < V) ? load_logit<DT>(logits, rowbase + e0 + j) : 0.f;
@@ -222,9 +229,16 @@ __device__ __forceinline__ void load_buf(ChunkRegs<DT> &R, const RowBufs &rb, in
             d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
         }
     }
+    R.mw = __builtin_amdgcn_raw_buffer_load_b32(rb.m, c * 256 + lane * 4, 0, 0);
+}
+
+// Group g's mask byte for this lane (chunk byte 64g + lane) from the lane
+// that loaded it: one cross-lane read per group, no LDS memory.
+__device__ __forceinline__ void mask_bytes(uint32_t mw, int lane, uint32_t (&mb)[4]) {
+    const int sh = 8 * (lane & 3);
 #pragma unroll
     for (int g = 0; g < 4; g++)
-        R.mb[g] = __builtin_amdgcn_raw_buffer_load_b8(rb.m, c * 256 + g * 64 + lane, 0, 0);
+        mb[g] = ((uint32_t)__builtin_amdgcn_ds_bpermute(64 * g + (lane & ~3), (int)mw) >> sh) & 0xFFu;
 }
 
 
@@ -241,8 +255,8 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // float32 logit j of group g, or -inf where the mask bit is clear (a
 // sign-extended 1-bit field selects between the value and -inf)
 template <int DT>
-__device__ __forceinline__ float masked_x(const ChunkRegs<DT> &R, int g, int j) {
-    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)R.mb[g], j, 1);
+__device__ __forceinline__ float masked_x(const ChunkRegs<DT> &R, const uint32_t (&mb)[4], int g, int j) {
+    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)mb[g], j, 1);
     const uint32_t u = R.d[g * 8 + j];
     return __uint_as_float((sel & u) | (~sel & 0xFF800000u));
 }
@@ -269,9 +283,9 @@ __device__ __forceinline__ void init_pair_lut(uint4 *lut) {
 // error ~1e-6.  Groups of 8 ids with no allowed id skip the exponentials
 // (most of a structural row).
 template <int DT>
-__device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4 *lut, float kk, float &m_out,
-                                             float &s_out, bool &any_out) {
-    any_out = __any(R.mb[0] | R.mb[1] | R.mb[2] | R.mb[3]);
+__device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint32_t (&mb)[4], const uint4 *lut,
+                                             float kk, float &m_out, float &s_out, bool &any_out) {
+    any_out = __any(mb[0] | mb[1] | mb[2] | mb[3]);
     m_out = -INFINITY;
     s_out = 0.f;
     if (!any_out) return;
@@ -280,7 +294,9 @@ __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4
 #pragma unroll
     for (int g = 0; g < 4; g++) {
         if (DT == 1) {
-            const uint4 sel = lut[R.mb[g]];
+            // one bit-select per bf16 pair (allowed halves keep their logit,
+            // the others become -inf), then one shift and one and
+            const uint4 sel = lut[mb[g]];
             const uint32_t sp[4] = {sel.x, sel.y, sel.z, sel.w};
 #pragma unroll
             for (int p = 0; p < 4; p++) {
@@ -291,7 +307,7 @@ __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 8; j++) xm[g * 8 + j] = masked_x<DT>(R, g, j);
+            for (int j = 0; j < 8; j++) xm[g * 8 + j] = masked_x<DT>(R, mb, g, j);
         }
 #pragma unroll
         for (int j = 0; j < 8; j += 2) m = max3f(m, xm[g * 8 + j], xm[g * 8 + j + 1]);
@@ -303,7 +319,7 @@ __device__ __forceinline__ void reduce_chunk(const ChunkRegs<DT> &R, const uint4
     float s = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; g++) {
-        if (R.mb[g]) {
+        if (mb[g]) {
             float sg = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; j++) sg += __builtin_amdgcn_exp2f(__builtin_fmaf(xm[g * 8 + j], kk, -mk));
@@ -472,21 +488,24 @@ struct AdvanceArgs {
 // byte offset of the stash in dynamic LDS: after the chunk summaries, 16-byte aligned
 __host__ __device__ inline size_t stash_offset(int K) { return ((size_t)K * sizeof(ChunkInfo) + 15) / 16 * 16; }
 
-// table slots fetched into registers ahead of the logits (the rest, if any, after them)
-constexpr int kStageRegs = 4;
+// table slots each thread fetches into registers at the start, ahead of the
+// logits (a table beyond kStageRegs * 1024 slots stages its rest after the
+// stream)
+constexpr int kStageRegs = 3;
 
 // One workgroup per row.  Its 16 waves stream the row's 2048-id chunks (wave
-// w takes chunks w, w + 16, ...; three chunks' loads in flight while one is
-// reduced) and leave one summary per chunk in LDS (masked max, sum of
-// exponentials, the chunk's screening noise); each wave also keeps a copy
-// of its best chunk so far in an LDS stash.  After one barrier three waves
-// reduce the chunk summaries at once (log-normaliser, greedy chunk, best two
-// chunk scores), then eight waves pick the token inside the chosen chunk,
-// read from the stash.  No state crosses workgroups, so no device-wide fence
-// is ever needed.  With the fused advance the first thread commits the
-// token; with plan_next the workgroup then plans its row's next mask from
-// the committed state (fill_plan.hpp), rewriting the row's mask words it
-// has finished reading (mask is not restrict).
+// w takes chunks w, w + 16, ...; one bf16 or two float32 chunks' loads in
+// flight per wave, the next load issued as each chunk is reduced) and leave
+// one summary per chunk in LDS (masked max, sum of exponentials, the
+// chunk's screening noise); each wave also keeps a copy of its best chunk
+// so far in an LDS stash.  After one barrier three waves reduce the chunk
+// summaries (log-normaliser, greedy chunk, best two chunk scores) while
+// eight waves pick the token inside the chunk they choose with the same
+// code, read from the stash.  No state crosses workgroups, so no
+// device-wide fence is ever needed.  With the fused advance the first
+// thread commits the token; with plan_next the workgroup then plans its
+// row's next mask from the committed state (fill_plan.hpp), rewriting the
+// row's mask words it has finished reading (mask is not restrict).
 template <int DT, bool VEC>
 __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
                                                  const uint64_t *mask, int words_per_row,
@@ -506,6 +525,45 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     // every chunk index derived from it) is uniform, and branches on scalars
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = blockIdx.x;
+    const uint8_t *mrow = (const uint8_t *)(mask + (size_t)r * words_per_row);
+    const size_t rowbase = (size_t)r * (size_t)stride;
+    // Each wave streams its chunks (c = wave, wave + 16, ...) through a ring
+    // of NB chunk buffers: the next load into a buffer is issued as soon as
+    // its chunk is reduced.  One bf16 chunk (4 KB) per wave in flight keeps
+    // the memory queues shallow: deeper rings (all of a 128K-id row requested
+    // at once) leave every chunk waiting behind the whole chip's requests and
+    // bunch the arrivals, and the reductions, at the end of the stream.
+    // Rows whose storage is not 16-byte aligned are read one chunk at a time
+    // with bounds-checked loads instead.
+    constexpr int NB = DT == 1 ? 1 : 2;
+    const int Kf = VEC ? K : 0;  // chunks read through buffer loads
+    RowBufs rb;
+    rb.x = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)logits + rowbase * (DT == 1 ? 2 : 4)), (short)0,
+                                             (V * (DT == 1 ? 2 : 4) + 3) & ~3, kRsrcWord3);
+    rb.m = __builtin_amdgcn_make_buffer_rsrc((void *)mrow, (short)0, words_per_row * 8, kRsrcWord3);
+    // (a scheduling barrier after each chunk's loads keeps the compiler from
+    // regrouping loads across chunks, which would make the first chunk wait
+    // for the others)
+    auto load = [&](ChunkRegs<DT> &R, int cc) {
+        load_buf<DT>(R, rb, min(cc, Kf), lane);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    ChunkRegs<DT> buf[NB];
+    // The first loads go out before anything else is read (a scalar read of
+    // the row's temperature, seed or step ahead of them would hold them back
+    // for its own round trip: scalar loads are waited for all together).
+    // Every wave issues them (clamped, even with no chunk of its own)
+    // whenever the row has pipelined chunks at all.
+    if (Kf > 0) {
+#pragma unroll
+        for (int b = 0; b < NB; b++) load(buf[b], wave + b * kWaves);
+    }
+    // fused: wave 0's lanes 0..5 fetch the row's 24-byte state now; thread
+    // 0 assembles it after the pick, long after it has arrived
+    const bool fuse = adv.comb != nullptr;
+    uint32_t stw = 0;
+    if (fuse && wave == 0 && lane < 6) stw = ((const uint32_t *)(adv.states + r))[lane];
+    __builtin_amdgcn_sched_barrier(0);
     const float Tf = temp[r];
     const uint64_t sd = seed[r];
     const uint32_t stp = (uint32_t)step[r];
@@ -514,68 +572,42 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const double invT = 1.0 / T;
     const float kk = greedy ? kLog2e : kLog2e / Tf;
     const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
-    const uint8_t *mrow = (const uint8_t *)(mask + (size_t)r * words_per_row);
-    const size_t rowbase = (size_t)r * (size_t)stride;
     constexpr double kLn2d = 0.6931471805599453, kLog2ed = 1.4426950408889634;
     const bool stash = DT == 1 && use_stash;
-    // fused advance: the transition table is fetched after the stream (into
-    // registers, in flight across the decision) and staged in LDS before the
-    // pick; the walk of the chosen token reads it there
-    const bool fuse = adv.comb != nullptr;
+    // fused advance: the transition table is fetched into registers at the
+    // start, right behind the first chunk, so its round trip is over long
+    // before the stream ends; it is stored to LDS after the stream and the
+    // walk of the chosen token reads it there
     uint64_t *lds_comb = (uint64_t *)((char *)dyn + adv.comb_off);
     const uint32_t tn = fuse ? adv.comb_len : 0u;
     // the pick (thread 0): every exit path below leaves it here
     int pick = -1;
     float pick_lp = 0.f;
     Decision dc;
+    const uint32_t treg = min(tn, (uint32_t)(kStageRegs * blockDim.x));
+    uint64_t tv[kStageRegs];
     {
-        // Chunks stream in groups of four per wave, as straight-line code:
-        // three chunks' loads in flight, each chunk reduced as soon as its
-        // own loads are in, the fourth load issued into the first buffer once
-        // it is free.  A wave with fewer chunks still issues every load, for
-        // the chunk one past the row's last (wholly outside both buffer
-        // resources: zeros, no memory traffic), so every path issues the
-        // same loads and the compiler's waits count exactly the loads behind
-        // each chunk.  Rows whose storage is not 16-byte aligned are read one
-        // chunk at a time with bounds-checked loads instead.
-        const int Kf = VEC ? K : 0;  // chunks read through buffer loads
-        RowBufs rb;
-        rb.x = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)logits + rowbase * (DT == 1 ? 2 : 4)), (short)0,
-                                                 (V * (DT == 1 ? 2 : 4) + 3) & ~3, kRsrcWord3);
-        rb.m = __builtin_amdgcn_make_buffer_rsrc((void *)mrow, (short)0, words_per_row * 8, kRsrcWord3);
-        // (a scheduling barrier after each chunk's loads keeps the compiler
-        // from regrouping loads across chunks, which would make the first
-        // chunk wait for the others)
-        auto load = [&](ChunkRegs<DT> &R, int cc) {
-            load_buf<DT>(R, rb, min(cc, Kf), lane);
-            __builtin_amdgcn_sched_barrier(0);
-        };
+        // (indices clamped rather than guarded: a fixed number of loads
+        // keeps the waits exact)
+        if (fuse) {
+#pragma unroll
+            for (int j = 0; j < kStageRegs; j++) tv[j] = adv.comb[min(j * blockDim.x + threadIdx.x, treg - 1)];
+        }
         // clears the mask bits of ids past V in the last chunk (a caller's
         // mask may carry set bits there)
-        auto clear_tail = [&](ChunkRegs<DT> &R) {
+        auto clear_tail = [&](uint32_t (&mb)[4]) {
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const int n = V - ((K - 1) * kChunk + g * 512 + lane * 8);
-                R.mb[g] &= n >= 8 ? 0xFFu : n <= 0 ? 0u : ((1u << n) - 1u);
+                mb[g] &= n >= 8 ? 0xFFu : n <= 0 ? 0u : ((1u << n) - 1u);
             }
         };
+        int c = wave;
         if (DT == 1) init_pair_lut(lut);
         if (stash && lane == 0) st->c[wave] = -1;
-        __syncthreads();  // the mask table
-        // The barrier comes before the loads: a wave whose loads are issued
-        // starts reducing without waiting for the others to issue theirs.
-        ChunkRegs<DT> b0, b1, b2;
-        auto start_group = [&](int c0) {
-            load(b0, c0);
-            load(b1, c0 + kWaves);
-            if (DT == 1) load(b2, c0 + 2 * kWaves);
-        };
-        // The first group's loads: every wave issues them (clamped, even with
-        // no chunk of its own) whenever the row has pipelined chunks at all,
-        // so that the loads before the first reduction are the same on every
-        // path.
-        int c = wave;
-        if (Kf > 0) start_group(c);
+        // (the loads stay in flight across the barrier: a workgroup barrier
+        // waits for LDS operations, not for loads from memory)
+        __syncthreads();  // the pair table
         // screening noise G(1, c) of this wave's chunks (c = wave + 16 lane +
         // 1024 j; written and read by the same wave), while the loads fly
         if (!greedy)
@@ -591,10 +623,12 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         float best = -INFINITY;
         const float invTf = (float)invT;
         auto process = [&](ChunkRegs<DT> &R, int cc) {
-            if (VEC && cc == K - 1) clear_tail(R);
+            uint32_t mb[4];
+            mask_bytes(R.mw, lane, mb);
+            if (VEC && cc == K - 1) clear_tail(mb);
             float m, s;
             bool any;
-            reduce_chunk<DT>(R, lut, kk, m, s, any);
+            reduce_chunk<DT>(R, mb, lut, kk, m, s, any);
             if (lane == 0) {
                 ci[cc].s = s;
                 ci[cc].m = m;
@@ -609,132 +643,212 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
                 for (int g = 0; g < 4; g++)
                     *(uint4 *)&st->d[wave][g * 256 + lane * 4] =
                         make_uint4(R.d[g * 4], R.d[g * 4 + 1], R.d[g * 4 + 2], R.d[g * 4 + 3]);
-                st->mb[wave][lane] = R.mb[0] | R.mb[1] << 8 | R.mb[2] << 16 | R.mb[3] << 24;
+                st->mb[wave][lane] = mb[0] | mb[1] << 8 | mb[2] << 16 | mb[3] << 24;
                 if (lane == 0) st->c[wave] = cc;
             }
         };
-        // a group of four chunks whose loads start_group issued
-        auto group = [&](int c0) {
-            if (DT == 1) {
-                process(b0, c0);
-                load(b0, c0 + 3 * kWaves);
-                if (c0 + kWaves < Kf) process(b1, c0 + kWaves);
-                if (c0 + 2 * kWaves < Kf) process(b2, c0 + 2 * kWaves);
-                if (c0 + 3 * kWaves < Kf) process(b0, c0 + 3 * kWaves);
-            } else {
-                // float32 chunks take twice the registers: two in flight
-                process(b0, c0);
-                load(b0, c0 + 2 * kWaves);
-                if (c0 + kWaves < Kf) process(b1, c0 + kWaves);
-                load(b1, c0 + 3 * kWaves);
-                if (c0 + 2 * kWaves < Kf) process(b0, c0 + 2 * kWaves);
-                if (c0 + 3 * kWaves < Kf) process(b1, c0 + 3 * kWaves);
+        // (with two or more buffers every path issues the same loads, past
+        // the row's end included, so the compiler's waits count exactly the
+        // loads behind each chunk; a single buffer waits for everything it
+        // has and skips the load past the end)
+        for (; c < Kf; c += NB * kWaves) {
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                if (b == 0 || c + b * kWaves < Kf) process(buf[b], c + b * kWaves);
+                if (NB > 1 || c + (b + NB) * kWaves < Kf) load(buf[b], c + (b + NB) * kWaves);
             }
-        };
-        // The first group runs outside any loop, so that no merge of loop
-        // paths blurs the compiler's count of loads in flight (a vocabulary
-        // of up to 131072 ids is one group per wave); later groups loop.
-        if (c < Kf) group(c);
-        for (c += 4 * kWaves; c < Kf; c += 4 * kWaves) {
-            start_group(c);
-            group(c);
         }
         // rows not 16-byte aligned: every chunk, bounds-checked
         for (c = wave < Kf ? wave + ((Kf - 1 - wave) / kWaves + 1) * kWaves : wave; c < K; c += kWaves) {
-            load_chunk<DT, VEC>(b0, logits, rowbase, mrow, V, c, lane);
-            process(b0, c);
+            load_chunk<DT, VEC>(buf[0], logits, rowbase, mrow, V, c, lane);
+            process(buf[0], c);
         }
     }
-    // fused: the table's first slots into registers now, stored after the
-    // decision (indices clamped rather than guarded: a fixed number of loads
-    // keeps the wait before the stores exact)
-    const uint32_t treg = min(tn, (uint32_t)(kStageRegs * blockDim.x));
-    uint64_t tv[kStageRegs];
-    if (fuse) {
-#pragma unroll
-        for (int j = 0; j < kStageRegs; j++) tv[j] = adv.comb[min(j * blockDim.x + threadIdx.x, treg - 1)];
-    }
-    __syncthreads();
-    // ---- the row's decision: three independent reductions over the chunk
-    // summaries (lane j takes chunks j, j + 64, ...) on three waves at once:
-    // (0) the log-normaliser over the chunk log-masses L_c = m/T + ln s (ln
-    // from v_log_f32: the chunk sums carry ~1e-6 of float rounding anyway),
-    // (1) the largest allowed logit and the lowest chunk holding it, (2) the
-    // two best chunk scores L_c + G(1, c).  The other waves stage the table.
-    if (wave < 3) {
-        auto lmass = [&](const ChunkInfo &x) -> double {
-            return (x.any && x.s > 0.f) ? (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf(x.s) : -INFINITY;
-        };
-        if (wave == 0) {
-            double lmax = -INFINITY;
-            float lsum = 0.f;
-            for (int cc = lane; cc < K; cc += 64) {
-                const double l = lmass(ci[cc]);
-                if (!(l > -INFINITY)) continue;
-                if (l > lmax) {
-                    lsum = lsum * __builtin_amdgcn_exp2f((float)((lmax - l) * kLog2ed)) + 1.f;
-                    lmax = l;
-                } else {
-                    lsum += __builtin_amdgcn_exp2f((float)((l - lmax) * kLog2ed));
-                }
-            }
-            const double L = wave_max_d_fast(lmax);
-            const float t =
-                wave_sum_f(lmax > -INFINITY ? lsum * __builtin_amdgcn_exp2f((float)((lmax - L) * kLog2ed)) : 0.f);
-            if (lane == 0) wdec.lse_all = L > -INFINITY ? L + kLn2d * (double)__builtin_amdgcn_logf(t) : -INFINITY;
-        } else if (wave == 1) {
-            float mv = -INFINITY;
-            int mc = -1;
-            for (int cc = lane; cc < K; cc += 64) {
-                const ChunkInfo x = ci[cc];
-                if (x.any && x.m > mv) {  // chunks in increasing order: ties keep the lowest
-                    mv = x.m;
-                    mc = cc;
-                }
-            }
-            const float m = wave_max_f(mv);
-            const int c = wave_min_i_fast((mc >= 0 && mv == m) ? mc : 0x7FFFFFFF);
-            if (lane == 0) {
-                wdec.mv = m;
-                wdec.mc = m > -INFINITY ? c : -1;  // allowed tokens all at -inf: nothing to draw
-            }
-        } else if (!greedy) {
-            Top2d cs{-INFINITY, -INFINITY, -1};
-            for (int cc = lane; cc < K; cc += 64) {
-                const double l = lmass(ci[cc]);
-                if (l > -INFINITY) top2d_merge(cs, l + (double)ci[cc].g, cc, -INFINITY);
-            }
-            // best score, the lowest chunk holding it, the best of the rest
-            const double v1 = wave_max_d_fast(cs.v1);
-            int c1 = wave_min_i_fast((cs.i1 >= 0 && cs.v1 == v1) ? cs.i1 : 0x7FFFFFFF);
-            if (c1 == 0x7FFFFFFF) c1 = -1;
-            const double v2 = wave_max_d_fast(cs.i1 == c1 ? cs.v2 : cs.v1);
-            if (lane == 0) {
-                wdec.c1 = c1;
-                wdec.cs1 = v1;
-                wdec.cs2 = v2;
-            }
-        }
-    }
-    // the table to LDS (made visible by the next barrier)
+    // the table to LDS, made visible by the barrier after the decision
     if (fuse) {
 #pragma unroll
         for (int j = 0; j < kStageRegs; j++) {
             const uint32_t i = j * blockDim.x + threadIdx.x;
             if (i < treg) lds_comb[i] = tv[j];
         }
-        if (tn > treg) stage_table(lds_comb, adv.comb, tn, treg);
     }
-    __syncthreads();  // the decision (and the table)
+    __syncthreads();
+    // ---- the row's decision: three independent reductions over the chunk
+    // summaries (lane j takes chunks j, j + 64, ...) on waves 13..15 at once:
+    // (0) the log-normaliser over the chunk log-masses L_c = m/T + ln s (ln
+    // from v_log_f32: the chunk sums carry ~1e-6 of float rounding anyway),
+    // (1) the largest allowed logit and the lowest chunk holding it, (2) the
+    // two best chunk scores L_c + G(1, c).  Meanwhile the eight token waves
+    // (0..7) work out the chunk choice themselves, with the same code on the
+    // same summaries ((1) for greedy rows, (2) for sampled ones), and start
+    // the pick inside that chunk; the decision's barrier is also the pick's.
+    // Only when the exact recheck of two close chunks moves the choice (or
+    // the waves' choices differ) is the pick made again.
+    constexpr int kTokWaves = kChunk / 4 / 64;  // 4 ids (one Philox block) per thread
+    constexpr int kDecWave = kWaves - 3;
+    static_assert(kDecWave >= kTokWaves, "the reducing waves are not token waves");
+    const bool tok = wave < kTokWaves;
+    const int t = threadIdx.x;
+    auto lmass = [&](const ChunkInfo &x) -> double {
+        return (x.any && x.s > 0.f) ? (double)x.m * invT + kLn2d * (double)__builtin_amdgcn_logf(x.s) : -INFINITY;
+    };
+    // (1): the largest allowed logit and the lowest chunk holding it (-1:
+    // nothing allowed, or every allowed logit is -inf)
+    auto chunk_max = [&](float &mv_out, int &mc_out) {
+        float mv = -INFINITY;
+        int mc = -1;
+        for (int cc = lane; cc < K; cc += 64) {
+            const ChunkInfo x = ci[cc];
+            if (x.any && x.m > mv) {  // chunks in increasing order: ties keep the lowest
+                mv = x.m;
+                mc = cc;
+            }
+        }
+        const float m = wave_max_f(mv);
+        const int c = wave_min_i_fast((mc >= 0 && mv == m) ? mc : 0x7FFFFFFF);
+        mv_out = m;
+        mc_out = m > -INFINITY ? c : -1;
+    };
+    // (2): the best chunk score, the lowest chunk holding it, the best of the rest
+    auto chunk_top2 = [&](double &v1_out, int &c1_out, double &v2_out) {
+        Top2d cs{-INFINITY, -INFINITY, -1};
+        for (int cc = lane; cc < K; cc += 64) {
+            const double l = lmass(ci[cc]);
+            if (l > -INFINITY) top2d_merge(cs, l + (double)ci[cc].g, cc, -INFINITY);
+        }
+        const double v1 = wave_max_d_fast(cs.v1);
+        int c1 = wave_min_i_fast((cs.i1 >= 0 && cs.v1 == v1) ? cs.i1 : 0x7FFFFFFF);
+        if (c1 == 0x7FFFFFFF) c1 = -1;
+        v1_out = v1;
+        c1_out = c1;
+        v2_out = wave_max_d_fast(cs.i1 == c1 ? cs.v2 : cs.v1);
+    };
+    if (wave == kDecWave) {
+        double lmax = -INFINITY;
+        float lsum = 0.f;
+        for (int cc = lane; cc < K; cc += 64) {
+            const double l = lmass(ci[cc]);
+            if (!(l > -INFINITY)) continue;
+            if (l > lmax) {
+                lsum = lsum * __builtin_amdgcn_exp2f((float)((lmax - l) * kLog2ed)) + 1.f;
+                lmax = l;
+            } else {
+                lsum += __builtin_amdgcn_exp2f((float)((l - lmax) * kLog2ed));
+            }
+        }
+        const double L = wave_max_d_fast(lmax);
+        const float tt =
+            wave_sum_f(lmax > -INFINITY ? lsum * __builtin_amdgcn_exp2f((float)((lmax - L) * kLog2ed)) : 0.f);
+        if (lane == 0) wdec.lse_all = L > -INFINITY ? L + kLn2d * (double)__builtin_amdgcn_logf(tt) : -INFINITY;
+    } else if (wave == kDecWave + 1) {
+        float m;
+        int c;
+        chunk_max(m, c);
+        if (lane == 0) {
+            wdec.mv = m;
+            wdec.mc = c;
+        }
+    } else if (wave == kDecWave + 2 && !greedy) {
+        double v1, v2;
+        int c1;
+        chunk_top2(v1, c1, v2);
+        if (lane == 0) {
+            wdec.c1 = c1;
+            wdec.cs1 = v1;
+            wdec.cs2 = v2;
+        }
+    }
+    // (3) inside a chunk: the token waves' threads take 4 ids each, e = 4t ..
+    // 4t + 3 (one Philox block), from the stash of the wave that reduced the
+    // chunk, else from HBM.  Eight waves, not sixteen: the Philox rounds
+    // dominate and cost per wave, whatever the ids per lane.  Each token
+    // wave leaves its best id (greedy: the lowest id holding the largest
+    // logit mv; sampled: the top two of x/T + G(0, i) screened in float) in
+    // its slot, and the chunk it worked on.
+    int e = 0, ws = 0;
+    bool from_stash = false;
+    float xq[4] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t mb4 = 0;  // mask bits of e .. e + 3
+    uint32_t wq[4] = {0u, 0u, 0u, 0u};
+    const float it = greedy ? 0.f : 1.0f / Tf;
+    auto tok_phase = [&](int ch, float mv) {  // token waves only
+        e = ch * kChunk + 4 * t;
+        ws = ch % kWaves;
+        from_stash = stash && st->c[ws] == ch;
+        mb4 = 0;
+        if (from_stash) {
+            const uint2 dw = *(const uint2 *)&st->d[ws][2 * t];
+            xq[0] = __uint_as_float(dw.x << 16);
+            xq[1] = __uint_as_float(dw.x & 0xFFFF0000u);
+            xq[2] = __uint_as_float(dw.y << 16);
+            xq[3] = __uint_as_float(dw.y & 0xFFFF0000u);
+            const int li = 4 * t;
+            mb4 = (st->mb[ws][(li & 511) >> 3] >> (8 * (li >> 9) + (li & 7))) & 15u;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                xq[j] = 0.f;
+                if (e + j < V) {
+                    xq[j] = load_logit<DT>(logits, rowbase + e + j);
+                    mb4 |= ((mrow[(e + j) >> 3] >> ((e + j) & 7)) & 1u) << j;
+                }
+            }
+        }
+        if (greedy) {
+            int im = 0x7FFFFFFF;
+#pragma unroll
+            for (int j = 3; j >= 0; j--)
+                if (((mb4 >> j) & 1u) && xq[j] == mv) im = e + j;
+            im = wave_min_i_fast(im);
+            if (lane == 0) sl[2].i[wave] = im;
+        } else {
+            uint4 o = make_uint4(0, 0, 0, 0);
+            if (mb4) o = philox4x32_10(make_uint4((uint32_t)e >> 2, stp, 0u, 0u), k0, k1);
+            wq[0] = o.x;
+            wq[1] = o.y;
+            wq[2] = o.z;
+            wq[3] = o.w;
+            Top2 ts{-INFINITY, -INFINITY, -1};
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                if ((mb4 >> j) & 1u) top2_merge(ts, xq[j] * it + gumbel32(wq[j]), e + j, -INFINITY);
+            ts = top2_wave_fast(ts);
+            if (lane == 0) {
+                sl[2].f[wave] = ts.v1;
+                sl[2].h[wave] = ts.v2;
+                sl[2].i[wave] = ts.i1;
+            }
+        }
+        if (lane == 0) sl[2].j[wave] = ch;
+    };
+    if (tok) {
+        float smv = 0.f;
+        int spec;
+        if (greedy) {
+            chunk_max(smv, spec);
+        } else {
+            double v1, v2;
+            chunk_top2(v1, spec, v2);
+        }
+        if (spec >= 0) tok_phase(spec, smv);
+        else if (lane == 0) sl[2].j[wave] = -1;
+    }
+    if (tn > treg) stage_table(lds_comb, adv.comb, tn, treg);
+    __syncthreads();  // the decision, the table and the token waves' slots
     dc.lse_all = wdec.lse_all;
     dc.mv = wdec.mv;
     dc.mc = wdec.mc;
     dc.chosen = greedy ? wdec.mc : wdec.c1;
     dc.exact_chunk = !greedy && wdec.c1 >= 0 && !(wdec.cs1 - wdec.cs2 > kContendChunk);
     dc.cs1 = wdec.cs1;
-    // fused: the row's state is fetched now, its round trip hidden by the pick
+    // fused: the row's state, fetched at the start
     cg_state row_state{};
-    if (fuse && threadIdx.x == 0) row_state = adv.states[r];
+    if (fuse && threadIdx.x == 0) {
+        uint32_t w6[6];
+#pragma unroll
+        for (int j = 0; j < 6; j++) w6[j] = (uint32_t)__builtin_amdgcn_readlane((int)stw, j);
+        __builtin_memcpy(&row_state, w6, sizeof(w6));
+    }
     do {
     if (dc.mc < 0) break;  // nothing allowed: a finished row
     if (dc.exact_chunk) {
@@ -757,37 +871,15 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     }
     const int chosen = dc.chosen;
     if (chosen < 0) break;  // every allowed logit is -inf: no distribution to draw from
-    // (3) inside the chunk: threads 0..511 take 4 ids each, e = 4t .. 4t + 3
-    // (one Philox block), from the stash of the wave that reduced the chunk,
-    // else from HBM.  Eight waves, not sixteen: the Philox rounds dominate
-    // and cost per wave, whatever the ids per lane.
-    const int t = threadIdx.x;
-    constexpr int kTokWaves = kChunk / 4 / 64;
-    const bool tok = wave < kTokWaves;
-    const int e = chosen * kChunk + 4 * t;
-    const int ws = chosen % kWaves;
-    const bool from_stash = stash && st->c[ws] == chosen;
-    float xq[4] = {0.f, 0.f, 0.f, 0.f};
-    uint32_t mb4 = 0;  // mask bits of e .. e + 3
-    if (tok) {
-        if (from_stash) {
-            const uint2 dw = *(const uint2 *)&st->d[ws][2 * t];
-            xq[0] = __uint_as_float(dw.x << 16);
-            xq[1] = __uint_as_float(dw.x & 0xFFFF0000u);
-            xq[2] = __uint_as_float(dw.y << 16);
-            xq[3] = __uint_as_float(dw.y & 0xFFFF0000u);
-            const int li = 4 * t;
-            mb4 = (st->mb[ws][(li & 511) >> 3] >> (8 * (li >> 9) + (li & 7))) & 15u;
-        } else {
+    bool again = false;  // (the same for every thread: read from LDS)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                if (e + j < V) {
-                    xq[j] = load_logit<DT>(logits, rowbase + e + j);
-                    mb4 |= ((mrow[(e + j) >> 3] >> ((e + j) & 7)) & 1u) << j;
-                }
-        }
+    for (int k = 0; k < kTokWaves; k++) again |= sl[2].j[k] != chosen;
+    if (again) {
+        __syncthreads();  // every slot read above
+        if (tok) tok_phase(chosen, dc.mv);
+        __syncthreads();
     }
-    auto x_of = [&](int id) -> float {  // logit of an id of the chosen chunk
+    auto x_of = [&](int id) -> float {  // logit of an id of the chosen chunk (thread 0)
         const int li = id - chosen * kChunk;
         if (from_stash) {
             const uint32_t dw = st->d[ws][li >> 1];
@@ -796,16 +888,6 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         return load_logit<DT>(logits, rowbase + id);
     };
     if (greedy) {
-        // the lowest id of the chunk holding the largest logit
-        int im = 0x7FFFFFFF;
-#pragma unroll
-        for (int j = 3; j >= 0; j--)
-            if (((mb4 >> j) & 1u) && xq[j] == dc.mv) im = e + j;
-        if (tok) {
-            im = wave_min_i_fast(im);
-            if (lane == 0) sl[2].i[wave] = im;
-        }
-        __syncthreads();
         if (threadIdx.x == 0) {
             int best = sl[2].i[0];
 #pragma unroll
@@ -817,25 +899,9 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     }
     // sampled: argmax_i x_i / T + G(0, i) screened in float; the winner is
     // exact unless the best two are within the screening error (x/T rounding
-    // < 1e-6 |x/T|, G < 1e-5), in which case the contenders are recomputed
-    const float it = 1.0f / Tf;
-    uint4 o = make_uint4(0, 0, 0, 0);
-    if (mb4) o = philox4x32_10(make_uint4((uint32_t)e >> 2, stp, 0u, 0u), k0, k1);
-    const uint32_t wq[4] = {o.x, o.y, o.z, o.w};
-    if (tok) {
-        Top2 ts{-INFINITY, -INFINITY, -1};
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            if ((mb4 >> j) & 1u) top2_merge(ts, xq[j] * it + gumbel32(wq[j]), e + j, -INFINITY);
-        ts = top2_wave_fast(ts);
-        if (lane == 0) {
-            sl[2].f[wave] = ts.v1;
-            sl[2].h[wave] = ts.v2;
-            sl[2].i[wave] = ts.i1;
-        }
-    }
-    __syncthreads();
-    // every wave merges the token waves' top two (slot loads first, then the merges)
+    // < 1e-6 |x/T|, G < 1e-5), in which case the contenders are recomputed.
+    // Every wave merges the token waves' top two (slot loads first, then the
+    // merges).
     float sv1[kTokWaves], sv2[kTokWaves];
     int si1[kTokWaves];
 #pragma unroll
