@@ -68,6 +68,39 @@ def recorded_traffic():
         return None
 
 
+def read_floor(pool, mask, B, V, es, W, stream, reps=72):
+    """The memory floor of the masked-sample launch: libcg_floor.so's
+    read-only kernel (the sampler's grid, chunk walk and bytes, no
+    arithmetic) over the same logits pool, an event pair around each launch
+    as for the sampler.  None when that library is not built."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "logit_masking_amd", "libcg_floor.so")
+    if not os.path.exists(path):
+        return None
+    f = ctypes.CDLL(path).cg_floor_read_rows
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    out_mask = torch.empty_like(mask)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        x = pool[i % len(pool)]
+        e0.record(stream)
+        assert f(x.data_ptr(), es, B, V, x.stride(0), mask.data_ptr(), W, out_mask.data_ptr(), stream.cuda_stream) == 0
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs[8:]])
+    nbytes = B * V * es + 2 * B * W * 8
+    return {"kernel": "k_read_floor (the sampler's grid, chunk walk and bytes: logits and mask read, a mask "
+                      "written; no arithmetic)",
+            "bytes": nbytes, "us": round(1e3 * ms.mean(), 2), "p50_us": round(1e3 * pct(ms, 50), 2),
+            "GBps": round(nbytes / (ms.mean() * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def pct(a, q):
     return float(np.percentile(np.asarray(a), q))
 
@@ -764,7 +797,7 @@ def main():
     step_ms = np.array([evb[k].elapsed_time(evb[k + 1]) for k in range(args.steps)])
     assert np.array_equal(steps.cpu().numpy(), st_h), "replay diverged from the timed trajectory"
 
-    # and once more, recording for the parity check (the masks of rows 0-63
+    # and once more, recording for the parity check (the masks of rows 0-127
     # as the sampler reads them; every row's pick, log-probability and
     # status), with cg_fill_bitmask timed on the same states before each
     # step (the fill's own rate; in the fused step its plan runs inside the
@@ -772,7 +805,7 @@ def main():
     st.copy_(st0)
     steps.copy_(steps0)
     mask.copy_(mask0)
-    chk = list(range(min(64, B)))
+    chk = list(range(min(128, B)))
     chk_t = torch.tensor(chk, dtype=torch.long, device=dev)
     rec_mask = torch.empty((args.steps, len(chk), g.W), dtype=torch.int64, device=dev)
     rec_lp = torch.empty((args.steps, B), dtype=torch.float32, device=dev)
@@ -878,6 +911,11 @@ def main():
     del src, dst
     out["copy_GBps"] = round(copy_gbps, 1)
     out["masked_sample_frac_copy"] = round(sample_gbps / copy_gbps, 4)
+    floor = read_floor(pool, mask, B, V, es, g.W, stream)
+    out["read_floor"] = floor
+    if floor is not None:
+        # the sampler's time against the floor's, both event pairs around one launch
+        out["masked_sample_frac_floor"] = round(floor["us"] / (1e3 * samp_ms.mean()), 4)
     if not (args.separate or args.no_classes):
         out["state_classes"] = state_classes(g, cg, st0, pool, temp, seed, steps0, ws, fws, B, V, stream)
     if args.calib_copy:

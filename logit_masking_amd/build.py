@@ -47,7 +47,22 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, OUT)
+    build_floor(cc, bdir)
     return OUT
+
+
+def build_floor(cc: str, bdir: str) -> str:
+    """libcg_floor.so: the bench's read-only reference kernel (read_floor.hip),
+    a library of its own that libcg does not link."""
+    out = os.path.join(HERE, "libcg_floor.so")
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [cc] + FLAGS + ["-shared", "-Wl,--no-undefined", "-x", "hip", os.path.join(CSRC, "read_floor.hip"),
+                          "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on read_floor.hip:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -44,6 +44,17 @@ def test_library_names_no_framework():
         assert bad not in out.lower()
 
 
+def test_floor_library_is_apart():
+    """The bench's read-only reference kernel lives in a library of its own:
+    one export, not linked by libcg (whose exports stay those of cg.h)."""
+    floor = os.path.join(ROOT, "logit_masking_amd", "libcg_floor.so")
+    if not os.path.exists(floor):
+        pytest.skip("libcg_floor.so is built by logit_masking_amd/build.py")
+    out = subprocess.check_output(["nm", "-D", "--defined-only", floor], text=True)
+    assert {l.split()[-1] for l in out.splitlines() if " T " in l} == {"cg_floor_read_rows"}
+    assert "libcg_floor" not in subprocess.check_output(["ldd", cg.LIB_PATH], text=True)
+
+
 @pytest.fixture(scope="module")
 def small_vocabs():
     return {c: (W.make_vocab(c, 4096) if c != 1 else W.make_vocab(1)) for c in W.SPECS}
