@@ -181,17 +181,23 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
         for (uint32_t b = 0; b < 256; b++)
             if ((g->host_comb[q + b] & 0xFFFFu) == q) f.legal[(size_t)q * 4 + (b >> 6)] |= 1ull << (b & 63);
     auto pad = [&](std::vector<uint32_t> &order) { order.resize((order.size() + kTile - 1) / kTile * kTile, kPad); };
-    auto pack = [&](const std::vector<uint32_t> &order, std::vector<uint32_t> &idlen, std::vector<uint32_t> &w) {
+    // a list's walk data: per token, id | bytes to walk << 24 | 1 << 31 (0 marks
+    // padding) and those bytes, from(t) on, nw words per token
+    auto pack = [&](const std::vector<uint32_t> &order, std::vector<uint32_t> &idlen, std::vector<uint32_t> &w,
+                    auto from) {
         const size_t n = order.size();
         idlen.assign(std::max<size_t>(n, 1), 0u);
         w.assign(std::max<size_t>(nw * n, 1), 0u);
         for (size_t i = 0; i < n; i++) {
             const uint32_t t = order[i];
             if (t == kPad) continue;
-            idlen[i] = t | len(t) << 24;
-            for (uint32_t j = 0; j < len(t); j++) w[(j >> 2) * n + i] |= (uint32_t)bytes(t)[j] << (8 * (j & 3));
+            const uint32_t f0 = from(t);
+            idlen[i] = t | (len(t) - f0) << 24 | 1u << 31;
+            for (uint32_t j = f0; j < len(t); j++)
+                w[((j - f0) >> 2) * n + i] |= (uint32_t)bytes(t)[j] << (8 * ((j - f0) & 3));
         }
     };
+    auto whole = [](uint32_t) { return 0u; };
     // key span of each tile over its real tokens (keys never decrease along a list)
     auto spans = [&](const std::vector<uint32_t> &order, auto key, std::vector<uint2> &tile) {
         tile.clear();
@@ -213,8 +219,8 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
     std::sort(q.begin(), q.end(), [&](uint32_t a, uint32_t b) { return less_from(a, qoff(a), b, qoff(b)); });
     pad(lex);
     pad(q);
-    pack(lex, f.lex_idlen, f.lex_w);
-    pack(q, f.q_idlen, f.q_w);
+    pack(lex, f.lex_idlen, f.lex_w, whole);
+    pack(q, f.q_idlen, f.q_w, qoff);  // the bytes after the closing quote
     spans(lex, [&](uint32_t t) { return lead_key(bytes(t)[0], len(t) > 1 ? bytes(t)[1] : 0u, len(t)); }, f.lex_tile);
     spans(q, [&](uint32_t t) { return qoff(t) == len(t) ? 0u : bytes(t)[qoff(t)] + 1u; }, f.q_tile);
     // the jump: where the token's first quote is, and how the bytes after it
@@ -246,7 +252,7 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
     }
     std::sort(cl.begin(), cl.end(), [&](uint32_t a, uint32_t b) { return less_from(a, 0, b, 0); });
     pad(cl);
-    pack(cl, f.c_idlen, f.c_w);
+    pack(cl, f.c_idlen, f.c_w, whole);
     spans(cl, [&](uint32_t t) { return lead_key(bytes(t)[0], len(t) > 1 ? bytes(t)[1] : 0u, len(t)); }, f.c_tile);
     jumps(cl, f.c_jump);
     f.q_posch.assign(std::max<size_t>(q.size(), 1), 0u);
@@ -332,7 +338,7 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
                 }
     }
     pad(qc);
-    pack(qc, f.qc_idlen, f.qc_w);
+    pack(qc, f.qc_idlen, f.qc_w, qoff);
     spans(qc, [&](uint32_t t) { return qoff(t) == len(t) ? 0u : bytes(t)[qoff(t)] + 1u; }, f.qc_tile);
     f.qc_posch.assign(std::max<size_t>(qc.size(), 1), 0u);
     for (size_t i = 0; i < qc.size(); i++)

@@ -228,46 +228,75 @@ constexpr int kWalkWaves = kWalkThreads / 64;
 // Byte Bi of the token (compile-time index: the walk is fully unrolled, so
 // the token words stay in registers with no dynamic indexing).  A lane walks
 // bytes [start, end) of its token while alive; the wave leaves as soon as no
-// lane has bytes left.  `jump` (kNoQuote: none) is the token's first quote
-// position and the string summary of the bytes after it.
+// lane has bytes left.  The step follows step_byte's rules, arranged for
+// this loop: moves and whitespace, nearly every byte a walk reads, take the
+// straight-line path; a string's code point, its quotes and the container
+// pushes and pops take the branch.  `jump` (kNoQuote: none) is the token's
+// first quote position and the string summary of the bytes after it: when
+// that quote opens a string, the walk jumps over the string's content.
 template <int Bi, int NB, int NW>
 __device__ __forceinline__ void walk_bytes(Walker &wk, bool &alive, const uint32_t (&w)[NW], int &start, int &end,
                                            uint32_t jump, const uint64_t *lds_comb, const WalkConsts &k) {
     if constexpr (Bi < NB) {
-        if (!__any(alive && Bi < end)) return;
-        if (alive && Bi >= start && Bi < end) {
-            alive = step_byte(wk, (w[Bi >> 2] >> ((Bi & 3) * 8)) & 0xFFu, lds_comb, k);
-            if (alive && (jump & 63u) == (uint32_t)Bi && wk.q == k.s_body) {
-                // the quote opened a string: the rest of the token is string
-                // content up to its closing quote, if any
-                const uint32_t kind = tok_kind(jump), nch = tok_chars(jump);
-                alive = kind != STR_DEAD && nch <= wk.cnt;
-                if (kind == STR_QUOTE) {
-                    wk.q = wk.ret;
-                    wk.ws = 0;
-                    wk.cnt -= nch;
-                    start = Bi + 2 + (int)tok_pos(jump);
+        const bool left = alive && Bi < end;
+        if (!__builtin_amdgcn_ballot_w64(left)) return;
+        if (left && Bi >= start) {
+            const uint32_t b = (w[Bi >> 2] >> ((Bi & 3) * 8)) & 0xFFu;
+            const uint64_t e = lds_comb[wk.q + b];
+            const uint32_t lo = (uint32_t)e, hi = (uint32_t)(e >> 32);
+            bool ok = (lo & 0xFFFFu) == wk.q;
+            uint32_t nq = lo >> 16;
+            const uint32_t op = hi & 0xFu;
+            uint32_t ws1 = __umul24(op, wk.ws) + op;  // OP_NONE: 0, OP_WS: the run + 1
+            if (op >= OP_CHAR) {
+                const uint32_t arg = hi >> 4;
+                ws1 = 0;
+                if (op == OP_CHAR) {
+                    ok = ok && wk.cnt != 0;
+                    wk.cnt -= 1;
+                } else if (op == OP_STR_OPEN) {
+                    wk.ret = nq;
+                    nq = k.s_body;
+                    wk.cnt = arg;
+                    if ((jump & 63u) == (uint32_t)Bi) {
+                        // the token's first quote opened the string: the rest
+                        // of the token is string content up to its closing
+                        // quote, if any
+                        const uint32_t kind = tok_kind(jump), nch = tok_chars(jump);
+                        ok = ok && kind != STR_DEAD && nch <= arg;
+                        if (kind == STR_QUOTE) {
+                            nq = wk.ret;
+                            wk.cnt = arg - nch;
+                            start = Bi + 2 + (int)tok_pos(jump);
+                        } else {
+                            end = 0;
+                        }
+                    }
+                } else if (op == OP_STR_CLOSE) {
+                    nq = wk.ret;
+                } else if (op == OP_PUSH) {
+                    ok = ok && wk.depth < (arg >> 1);
+                    wk.stk = (wk.stk << 1) | (arg & 1u);
+                    wk.depth += 1;
                 } else {
-                    end = 0;
+                    wk.stk >>= 1;
+                    wk.depth -= 1;
+                    nq = (wk.depth == 0) ? nq : ((wk.stk & 1u) ? (arg >> 14) : (arg & 0x3FFFu));
                 }
             }
+            alive = ok && ws1 <= k.ws_max;
+            wk.ws = ws1;
+            wk.q = nq;
         }
         walk_bytes<Bi + 1, NB, NW>(wk, alive, w, start, end, jump, lds_comb, k);
     }
 }
 
-template <int NW>
-__device__ __forceinline__ uint32_t byte_at(const uint32_t (&w)[NW], uint32_t i) {
-    uint32_t x = 0;
-#pragma unroll
-    for (int j = 0; j < NW; j++) x = (uint32_t)j == (i >> 2) ? w[j] : x;
-    return (x >> (8 * (i & 3))) & 0xFFu;
-}
-
 // One tile's worth of a lane: its token (or padding) and where its walk starts.
 template <int NW>
 struct LaneTok {
-    uint32_t il, aux;  // id | len << 24; jump (lexicographic list) or quote position | chars (string list)
+    uint32_t il, aux;  // id | bytes to walk << 24 | 1 << 31 (0: padding); jump (lexicographic lists)
+                       // or quote position | code points before it << 8 (string lists)
     uint32_t w[NW];
 };
 
@@ -419,12 +448,12 @@ __global__ __launch_bounds__(kWalkThreads) void k_fill_walk(FillArgs a) {
             const bool in_str = (t0.tile >> 30) >= LIST_QSTR;
             const Walker w0 = load_walker(t0.s);
             const uint32_t id = cur.il & 0xFFFFFFu;
-            int end = (int)(cur.il >> 24), start = 0;
-            bool alive = end > 0;
+            int end = (int)((cur.il >> 24) & 0x3Fu), start = 0;
+            bool alive = (int32_t)cur.il < 0;
             uint32_t jump = kNoQuote;
             Walker wk = w0;
             if (in_str) {
-                start = (int)(cur.aux & 0xFFu) + 1;
+                // a string list holds the bytes after the closing quote
                 const uint32_t nch = cur.aux >> 8;
                 alive = alive && nch <= w0.cnt;
                 wk.q = w0.ret;
