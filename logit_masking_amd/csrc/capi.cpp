@@ -74,7 +74,7 @@ void release(cg_grammar *g) {
         (void)hipFree(g->dev.c_tile);
         (void)hipFree(g->dev.retmask2);
         (void)hipFree(g->dev.qc_idlen);
-        (void)hipFree(g->dev.qc_posch);
+        (void)hipFree(g->dev.qc_jump);
         (void)hipFree(g->dev.qc_w);
         (void)hipFree(g->dev.qc_tile);
         (void)hipFree(g->dev.retmask);
@@ -85,7 +85,7 @@ void release(cg_grammar *g) {
         (void)hipFree(g->dev.lex_w);
         (void)hipFree(g->dev.lex_tile);
         (void)hipFree(g->dev.q_idlen);
-        (void)hipFree(g->dev.q_posch);
+        (void)hipFree(g->dev.q_jump);
         (void)hipFree(g->dev.q_w);
         (void)hipFree(g->dev.q_tile);
         (void)hipFree(g->dev.strbits);
@@ -123,11 +123,11 @@ struct FillHost {
     std::vector<int32_t> rq_idx;
     std::vector<uint64_t> s0;  // tokens that stay inside the container a row is in (bit per id)
     std::vector<uint64_t> retmask2;  // [resume][kind of the open container][Wv]
-    std::vector<uint32_t> qc_idlen, qc_posch, qc_w;
+    std::vector<uint32_t> qc_idlen, qc_jump, qc_w;
     std::vector<uint2> qc_tile;
     std::vector<uint32_t> c_idlen, c_jump, c_w;
     std::vector<uint2> c_tile;
-    std::vector<uint32_t> lex_idlen, lex_jump, lex_w, q_idlen, q_posch, q_w;
+    std::vector<uint32_t> lex_idlen, lex_jump, lex_w, q_idlen, q_jump, q_w;
     std::vector<uint2> lex_tile, q_tile;
 };
 
@@ -225,19 +225,27 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
     spans(q, [&](uint32_t t) { return qoff(t) == len(t) ? 0u : bytes(t)[qoff(t)] + 1u; }, f.q_tile);
     // the jump: where the token's first quote is, and how the bytes after it
     // read as string content
-    auto jumps = [&](const std::vector<uint32_t> &order, std::vector<uint32_t> &jump) {
+    // read from where the list's walk starts (from(t))
+    auto jumps = [&](const std::vector<uint32_t> &order, std::vector<uint32_t> &jump, auto from) {
         jump.assign(std::max<size_t>(order.size(), 1), kNoQuote);
         for (size_t i = 0; i < order.size(); i++) {
             const uint32_t t = order[i];
             if (t == kPad || g->k.s_body >= g->k.q_limit) continue;
-            const uint8_t *b = bytes(t);
-            const uint8_t *qp = (const uint8_t *)memchr(b, '"', len(t));
+            const uint8_t *b = bytes(t) + from(t);
+            const uint32_t n = len(t) - from(t);
+            const uint8_t *qp = (const uint8_t *)memchr(b, '"', n);
             if (!qp) continue;
             const uint32_t at = (uint32_t)(qp - b);
-            jump[i] = at | string_summary(g, b + at + 1, len(t) - at - 1);
+            jump[i] = at | string_summary(g, b + at + 1, n - at - 1);
         }
     };
-    jumps(lex, f.lex_jump);
+    // a string list's tokens also carry the code points before their closing
+    // quote (bits 21..26)
+    auto with_chars = [&](const std::vector<uint32_t> &order, std::vector<uint32_t> &jump) {
+        for (size_t i = 0; i < order.size(); i++)
+            if (order[i] != kPad) jump[i] |= tok_chars(tokinfo[order[i]]) << 21;
+    };
+    jumps(lex, f.lex_jump, whole);
     // tokens that stay inside the container a row is in (s0) and the rest,
     // kept as a lexicographic tile list of their own
     f.s0.assign(Wv, 0ull);
@@ -254,10 +262,9 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
     pad(cl);
     pack(cl, f.c_idlen, f.c_w, whole);
     spans(cl, [&](uint32_t t) { return lead_key(bytes(t)[0], len(t) > 1 ? bytes(t)[1] : 0u, len(t)); }, f.c_tile);
-    jumps(cl, f.c_jump);
-    f.q_posch.assign(std::max<size_t>(q.size(), 1), 0u);
-    for (size_t i = 0; i < q.size(); i++)
-        if (q[i] != kPad) f.q_posch[i] = tok_pos(tokinfo[q[i]]) | tok_chars(tokinfo[q[i]]) << 8;
+    jumps(cl, f.c_jump, whole);
+    jumps(q, f.q_jump, qoff);
+    with_chars(q, f.q_jump);
     // tokens that end inside the string, per budget
     f.strbits.assign((size_t)kStrBitsets * Wv, 0ull);
     for (uint32_t t = 0; t < V; t++) {
@@ -340,9 +347,8 @@ void build_fill_tables(const cg_grammar *g, const uint8_t *tok_bytes, const uint
     pad(qc);
     pack(qc, f.qc_idlen, f.qc_w, qoff);
     spans(qc, [&](uint32_t t) { return qoff(t) == len(t) ? 0u : bytes(t)[qoff(t)] + 1u; }, f.qc_tile);
-    f.qc_posch.assign(std::max<size_t>(qc.size(), 1), 0u);
-    for (size_t i = 0; i < qc.size(); i++)
-        if (qc[i] != kPad) f.qc_posch[i] = tok_pos(tokinfo[qc[i]]) | tok_chars(tokinfo[qc[i]]) << 8;
+    jumps(qc, f.qc_jump, qoff);
+    with_chars(qc, f.qc_jump);
 }
 
 }  // namespace
@@ -602,7 +608,7 @@ int compile_uncached(const char *spec_json, size_t spec_len, const uint8_t *tok_
             upload(&g->dev.lex_w, f.lex_w.data(), f.lex_w.size()) ||
             upload(&g->dev.lex_tile, f.lex_tile.data(), f.lex_tile.size()) ||
             upload(&g->dev.q_idlen, f.q_idlen.data(), f.q_idlen.size()) ||
-            upload(&g->dev.q_posch, f.q_posch.data(), f.q_posch.size()) ||
+            upload(&g->dev.q_jump, f.q_jump.data(), f.q_jump.size()) ||
             upload(&g->dev.q_w, f.q_w.data(), f.q_w.size()) ||
             upload(&g->dev.q_tile, f.q_tile.data(), f.q_tile.size()) ||
             upload(&g->dev.strbits, f.strbits.data(), f.strbits.size()) ||
@@ -613,7 +619,7 @@ int compile_uncached(const char *spec_json, size_t spec_len, const uint8_t *tok_
             upload(&g->dev.c_tile, f.c_tile.data(), f.c_tile.size()) ||
             (!f.retmask2.empty() && (upload(&g->dev.retmask2, f.retmask2.data(), f.retmask2.size()) ||
                                      upload(&g->dev.qc_idlen, f.qc_idlen.data(), f.qc_idlen.size()) ||
-                                     upload(&g->dev.qc_posch, f.qc_posch.data(), f.qc_posch.size()) ||
+                                     upload(&g->dev.qc_jump, f.qc_jump.data(), f.qc_jump.size()) ||
                                      upload(&g->dev.qc_w, f.qc_w.data(), f.qc_w.size()) ||
                                      upload(&g->dev.qc_tile, f.qc_tile.data(), f.qc_tile.size()))) ||
             (!f.retmask.empty() && (upload(&g->dev.retmask, f.retmask.data(), f.retmask.size()) ||

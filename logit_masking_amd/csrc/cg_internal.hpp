@@ -244,7 +244,7 @@ struct DeviceTables {
     // holds the closing tokens whose bytes after the quote stay inside it
     // (null: no table); the other closing tokens are the qc list.
     uint64_t *retmask2 = nullptr;    // [n_resume * 2][Wv]
-    uint32_t *qc_idlen = nullptr, *qc_posch = nullptr, *qc_w = nullptr;
+    uint32_t *qc_idlen = nullptr, *qc_jump = nullptr, *qc_w = nullptr;
     uint2 *qc_tile = nullptr;
     // Tokens that close a string: closebits[c] = the content before the
     // quote fits a budget of c code points; retmask[rq_idx[R]] = the bytes
@@ -255,15 +255,16 @@ struct DeviceTables {
     int32_t *rq_idx = nullptr;       // [q_limit]
     // Fill candidates: the non-empty tokens in lexicographic order, padded
     // with empty entries (idlen 0) to whole 64-token tiles.
-    uint32_t *lex_idlen = nullptr;   // [lex_tiles * 64] id | len << 24
+    uint32_t *lex_idlen = nullptr;   // [lex_tiles * 64] id | len << 24 | 1 << 31 (0: padding)
     uint32_t *lex_jump = nullptr;    // [lex_tiles * 64] first quote position (kNoQuote: none) | string
                                      //       summary of the bytes after it (tokinfo layout, bits 8..20)
     uint32_t *lex_w = nullptr;       // [nw][lex_tiles * 64] token bytes
     uint2 *lex_tile = nullptr;       // [lex_tiles] first and last key of each tile
     // Tokens that close a string opened before them, sorted by the bytes
     // after the quote, padded the same way.
-    uint32_t *q_idlen = nullptr;     // [q_tiles * 64] id | len << 24
-    uint32_t *q_posch = nullptr;     // [q_tiles * 64] quote position | code points before it << 8
+    uint32_t *q_idlen = nullptr;     // [q_tiles * 64] id | bytes after the quote << 24 | 1 << 31
+    uint32_t *q_jump = nullptr;      // [q_tiles * 64] the first quote after the closing one, as in
+                                     //       lex_jump, | code points before the closing one << 21
     uint32_t *q_w = nullptr;         // [nw][q_tiles * 64]
     uint2 *q_tile = nullptr;         // [q_tiles] first and last after-quote key of each tile
     uint64_t *strbits = nullptr;     // [33][ceil(V / 64)] tokens that stay inside a string from a

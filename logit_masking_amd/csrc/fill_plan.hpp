@@ -22,7 +22,7 @@ struct FillArgs {
     const uint32_t *lex_idlen, *lex_jump, *lex_w;
     const uint2 *lex_tile;
     int lex_tiles;
-    const uint32_t *q_idlen, *q_posch, *q_w;
+    const uint32_t *q_idlen, *q_jump, *q_w;
     const uint2 *q_tile;
     int q_tiles;
     const uint64_t *strbits;
@@ -39,7 +39,7 @@ struct FillArgs {
     const uint2 *c_tile;
     int c_tiles;
     const uint64_t *retmask2;                 // string rows inside a container (null: none)
-    const uint32_t *qc_idlen, *qc_posch, *qc_w;
+    const uint32_t *qc_idlen, *qc_jump, *qc_w;
     const uint2 *qc_tile;
     int qc_tiles;
     const uint64_t *closebits, *retmask;  // string rows with no open container (rq_idx null: none)

@@ -229,11 +229,11 @@ constexpr int kWalkWaves = kWalkThreads / 64;
 // the token words stay in registers with no dynamic indexing).  A lane walks
 // bytes [start, end) of its token while alive; the wave leaves as soon as no
 // lane has bytes left.  The step follows step_byte's rules, arranged for
-// this loop: moves and whitespace, nearly every byte a walk reads, take the
-// straight-line path; a string's code point, its quotes and the container
-// pushes and pops take the branch.  `jump` (kNoQuote: none) is the token's
-// first quote position and the string summary of the bytes after it: when
-// that quote opens a string, the walk jumps over the string's content.
+// this loop: moves, whitespace and string code points take the
+// straight-line path; the quotes and the container pushes and pops take the
+// branch.  `jump` (kNoQuote in its low 6 bits: none) is the position of the
+// first quote the walk meets and the string summary of the bytes after it:
+// when that quote opens a string, the walk jumps over the string's content.
 template <int Bi, int NB, int NW>
 __device__ __forceinline__ void walk_bytes(Walker &wk, bool &alive, const uint32_t (&w)[NW], int &start, int &end,
                                            uint32_t jump, const uint64_t *lds_comb, const WalkConsts &k) {
@@ -247,14 +247,15 @@ __device__ __forceinline__ void walk_bytes(Walker &wk, bool &alive, const uint32
             bool ok = (lo & 0xFFFFu) == wk.q;
             uint32_t nq = lo >> 16;
             const uint32_t op = hi & 0xFu;
-            uint32_t ws1 = __umul24(op, wk.ws) + op;  // OP_NONE: 0, OP_WS: the run + 1
-            if (op >= OP_CHAR) {
+            const uint32_t is_ws = op & 1u;  // OP_WS (OP_STR_OPEN takes the branch)
+            uint32_t ws1 = __umul24(is_ws, wk.ws) + is_ws;
+            const bool ch = op == OP_CHAR;
+            ok = ok && !(ch && wk.cnt == 0);
+            wk.cnt -= ch ? 1u : 0u;
+            if (op > OP_CHAR) {
                 const uint32_t arg = hi >> 4;
                 ws1 = 0;
-                if (op == OP_CHAR) {
-                    ok = ok && wk.cnt != 0;
-                    wk.cnt -= 1;
-                } else if (op == OP_STR_OPEN) {
+                if (op == OP_STR_OPEN) {
                     wk.ret = nq;
                     nq = k.s_body;
                     wk.cnt = arg;
@@ -295,8 +296,8 @@ __device__ __forceinline__ void walk_bytes(Walker &wk, bool &alive, const uint32
 // One tile's worth of a lane: its token (or padding) and where its walk starts.
 template <int NW>
 struct LaneTok {
-    uint32_t il, aux;  // id | bytes to walk << 24 | 1 << 31 (0: padding); jump (lexicographic lists)
-                       // or quote position | code points before it << 8 (string lists)
+    uint32_t il, aux;  // id | bytes to walk << 24 | 1 << 31 (0: padding); jump, and in the string
+                       // lists | code points before the closing quote << 21
     uint32_t w[NW];
 };
 
@@ -305,13 +306,13 @@ __device__ __forceinline__ void load_lane(LaneTok<NW> &x, uint32_t list, int i, 
     if (list == LIST_QSTR) {
         const int n = a.q_tiles * kTile;
         x.il = a.q_idlen[i];
-        x.aux = a.q_posch[i];
+        x.aux = a.q_jump[i];
 #pragma unroll
         for (int j = 0; j < NW; j++) x.w[j] = a.q_w[(size_t)j * n + i];
     } else if (list == LIST_QCLOSE) {
         const int n = a.qc_tiles * kTile;
         x.il = a.qc_idlen[i];
-        x.aux = a.qc_posch[i];
+        x.aux = a.qc_jump[i];
 #pragma unroll
         for (int j = 0; j < NW; j++) x.w[j] = a.qc_w[(size_t)j * n + i];
     } else if (list == LIST_CLOSE) {
@@ -450,18 +451,16 @@ __global__ __launch_bounds__(kWalkThreads) void k_fill_walk(FillArgs a) {
             const uint32_t id = cur.il & 0xFFFFFFu;
             int end = (int)((cur.il >> 24) & 0x3Fu), start = 0;
             bool alive = (int32_t)cur.il < 0;
-            uint32_t jump = kNoQuote;
             Walker wk = w0;
             if (in_str) {
                 // a string list holds the bytes after the closing quote
-                const uint32_t nch = cur.aux >> 8;
+                const uint32_t nch = cur.aux >> 21;
                 alive = alive && nch <= w0.cnt;
                 wk.q = w0.ret;
                 wk.ws = 0;
                 wk.cnt = w0.cnt - nch;
-            } else {
-                jump = cur.aux;
             }
+            const uint32_t jump = cur.aux;
             walk_bytes<0, NW * 4, NW>(wk, alive, cur.w, start, end, jump, lds_comb, k);
             if (alive) atomicOr(&a.mask[(size_t)t0.r * a.words_per_row + (id >> 6)], 1ull << (id & 63));
             cur = nxt;
@@ -547,7 +546,7 @@ FillArgs make_fill_args(const cg_grammar *g, const cg_state *states, int B, uint
     a.lex_tile = g->dev.lex_tile;
     a.lex_tiles = g->lex_tiles;
     a.q_idlen = g->dev.q_idlen;
-    a.q_posch = g->dev.q_posch;
+    a.q_jump = g->dev.q_jump;
     a.q_w = g->dev.q_w;
     a.q_tile = g->dev.q_tile;
     a.q_tiles = g->q_tiles;
@@ -568,7 +567,7 @@ FillArgs make_fill_args(const cg_grammar *g, const cg_state *states, int B, uint
     a.c_tiles = g->c_tiles;
     a.retmask2 = g->dev.retmask ? g->dev.retmask2 : nullptr;
     a.qc_idlen = g->dev.qc_idlen;
-    a.qc_posch = g->dev.qc_posch;
+    a.qc_jump = g->dev.qc_jump;
     a.qc_w = g->dev.qc_w;
     a.qc_tile = g->dev.qc_tile;
     a.qc_tiles = g->qc_tiles;
