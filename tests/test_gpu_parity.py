@@ -154,6 +154,62 @@ def test_mask_parity_inside_strings(torch_dev, cfg):
     _compare_masks(got, want, len(toks), f"config {cfg} in strings")
 
 
+# Tokens for the walk's string paths: after a closing quote a second string
+# opened and closed (or left open) inside the token, escapes, multi-byte code
+# points and brackets in it; quotes escaped, first or not; code points around
+# the cap.
+WALK_TOKENS = [
+    b'":"abc', b'":"a', b'":"', b'":"ab",', b'":"ab"', b'":"a\\"b', b'":"a\\\\"', b'":"\xc3\xa9x"',
+    b'":"\xe2\x82\xac"}', b'","x"', b'","x":"y"', b'"],"a"', b'"}', b'"},{"k":"v"', b'":["a","b"]',
+    b'":{"x":"y"}', b'" : "z"', b'":""', b'":"\\u00e9"', b'":"\\u00', b'":"' + b"a" * 20,
+    b'":"' + b"a" * 25 + b'"', b'":"abcde"', b'":"abcdef"', b'":"abcdefg"', b'x":"y', b'ab","c',
+    b'\xc3\xa9":"x', b'\\\\":"q"', b'"abc"', b'"ab"c', b'"x"y"z"', b'"a":"b"', b'{"a":"b","c":"d"}',
+    b'["x","y"]', b'"\\"q"', b'"\\u0041"', b'"a\\nb"', b' "a"', b'"' + b"q" * 28 + b'"', b'"abc',
+    b'"', b'"":"', b'\xa9"', b'\xa9":"x"', b'\x82\xac', b'\x82\xac"}', b'abcdef"', b'abcdefg"',
+    b'[{"a":["b",{"c":"d"}]}]', b'"]]]', b'"}}', b'":[[["x"', b'":1,"b":"c"',
+]
+WALK_PREFIXES = [b"", b"{", b"[", b'{"', b'{"ab', b'{"abcde', b'{"a":"', b'{"a":"xy', b'["', b'["a\\',
+                 b'["\xc3', b'["\xe2\x82', b'{"a":["b","', b'[[{"k":"', b'{"a":"\\u00', b'{"a":1,"',
+                 b'[[["', b'{"a":{"b":[', b'["\\', b'{"a\\']
+
+
+@pytest.mark.parametrize("cap", [None, 6])
+def test_walk_string_paths(torch_dev, cap):
+    """The walk's string paths against the oracle, word for word: tokens whose
+    bytes after a closing quote open a second string (jumped with that
+    string's summary, closed or left open, escapes and multi-byte code points
+    inside), escaped quotes (walked byte by byte), code points before and at
+    a cap of 6; rows inside strings (at a code-point boundary, after a
+    backslash, mid UTF-8) and outside them, in objects and arrays up to the
+    depth cap ("Constrained decoding", "The guarantee")."""
+    import json
+    say("walk string paths", cap)
+    spec = json.dumps({"kind": "json_schema", "ws_max": 2, "open_string_cap": cap, "depth_cap": 4,
+                       "schema": {"anyOf": [{"type": "object"}, {"type": "array"}]}}).encode()
+    og = O.load_spec(spec)
+    toks = [bytes([i]) for i in range(256)] + WALK_TOKENS
+    blob = b"".join(toks)
+    off = np.cumsum([0] + [len(t) for t in toks]).tolist()
+    g = cg.Grammar(spec, blob, off)
+    seqs, rows = [], []
+    for pre in WALK_PREFIXES:
+        row = O.Row(og, W.GEN_CAP)
+        if og.feed(og.clone(row.conf), pre) != len(pre):
+            continue
+        for b in pre:
+            row.advance(bytes([b]))
+        seqs.append(list(pre))
+        rows.append(row)
+    assert len(rows) >= 15, len(rows)
+    st, steps, status = device_rows(g, seqs)
+    got = gpu_masks(g, st)
+    want, _ = oracle_masks(og, rows, blob, off)
+    _compare_masks(got, want, len(toks), f"walk string paths, cap {cap}")
+    # the crafted tokens must take part: some allowed, some refused
+    allowed = np.unpackbits(want.view(np.uint8), axis=1, bitorder="little")[:, 256:len(toks)]
+    assert allowed.any() and not allowed.all()
+
+
 def test_calc_prefix_sweep(torch_dev):
     """Config 1 over 2048 random valid prefixes (byte ids through cg_advance)."""
     say("calc sweep")
