@@ -91,7 +91,7 @@ __device__ __forceinline__ void append_tiles(bool act, uint32_t t, uint32_t *lis
     const int lane = threadIdx.x & 63;
     uint32_t base = 0;
     if (lane == 0) base = atomicAdd(count, (uint32_t)__popcll(m));
-    base = __shfl(base, 0);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);  // no LDS round trip
     if (act) list[base + __popcll(m & ((1ull << lane) - 1ull))] = t;
 }
 
@@ -199,6 +199,7 @@ __device__ inline void plan_row(const FillArgs &a, int r, const cg_state &s, con
         }
 #pragma unroll
         for (int i = 0; i < kPlanKeys; i++) {
+            if (c0 + i * kPlanThreads >= n_all) break;  // no key of this round left (the same for every thread)
             const int t = c0 + tid + i * kPlanThreads;
             bool act = false;
             if (t < n_all) {
