@@ -494,8 +494,9 @@ __host__ __device__ inline size_t stash_offset(int K) { return ((size_t)K * size
 constexpr int kStageRegs = 3;
 
 // One workgroup per row.  Its 16 waves stream the row's 2048-id chunks (wave
-// w takes chunks w, w + 16, ...; one bf16 or two float32 chunks' loads in
-// flight per wave, the next load issued as each chunk is reduced) and leave
+// w starts with chunk w and then takes the next unclaimed one from a counter
+// in LDS; one bf16 or two float32 chunks' loads in flight per wave, the next
+// load issued as each chunk is reduced) and leave
 // one summary per chunk in LDS (masked max, sum of exponentials, the
 // chunk's screening noise); each wave also keeps a copy of its best chunk
 // so far in an LDS stash.  After one barrier three waves reduce the chunk
@@ -521,15 +522,16 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     __shared__ RowDecision wdec;
     __shared__ PlanShared psh;
     __shared__ cg_state next_state;
+    __shared__ int next_chunk;  // the next chunk to deal to a wave
     // the wave index through readfirstlane: the compiler then knows it (and
     // every chunk index derived from it) is uniform, and branches on scalars
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = blockIdx.x;
     const uint8_t *mrow = (const uint8_t *)(mask + (size_t)r * words_per_row);
     const size_t rowbase = (size_t)r * (size_t)stride;
-    // Each wave streams its chunks (c = wave, wave + 16, ...) through a ring
-    // of NB chunk buffers: the next load into a buffer is issued as soon as
-    // its chunk is reduced.  One bf16 chunk (4 KB) per wave in flight keeps
+    // Each wave streams its chunks through a ring of NB chunk buffers (the
+    // first ones wave, wave + 16, ...): the next load into a buffer is
+    // issued as soon as its chunk is reduced.  One bf16 chunk (4 KB) per wave in flight keeps
     // the memory queues shallow: deeper rings (all of a 128K-id row requested
     // at once) leave every chunk waiting behind the whole chip's requests and
     // bunch the arrivals, and the reductions, at the end of the stream.
@@ -605,16 +607,17 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         int c = wave;
         if (DT == 1) init_pair_lut(lut);
         if (stash && lane == 0) st->c[wave] = -1;
-        // (the loads stay in flight across the barrier: a workgroup barrier
-        // waits for LDS operations, not for loads from memory)
-        __syncthreads();  // the pair table
-        // screening noise G(1, c) of this wave's chunks (c = wave + 16 lane +
-        // 1024 j; written and read by the same wave), while the loads fly
+        if (threadIdx.x == 0) next_chunk = NB * kWaves;
+        // screening noise G(1, c) of every chunk (wave w: c = w + 16 lane +
+        // 1024 j), while the loads fly; any wave may reduce any chunk
         if (!greedy)
             for (int cg = wave + kWaves * lane; cg < K; cg += kWaves * 64) {
                 const uint4 o = philox4x32_10(make_uint4((uint32_t)cg >> 2, stp, 1u, 0u), k0, k1);
                 ci[cg].g = gumbel32(pick_word(o, cg & 3));
             }
+        // (the loads stay in flight across the barrier: a workgroup barrier
+        // waits for LDS operations, not for loads from memory)
+        __syncthreads();  // the pair table, the noise and the chunk counter
         // reduce chunk cc into its summary; the wave's best chunk so far (by
         // the chunk score in float: m for greedy rows, m/T + ln s + G(1, c)
         // for sampled ones) is copied to the stash.  A near-tie that the
@@ -647,19 +650,39 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
                 if (lane == 0) st->c[wave] = cc;
             }
         };
-        // (with two or more buffers every path issues the same loads, past
-        // the row's end included, so the compiler's waits count exactly the
-        // loads behind each chunk; a single buffer waits for everything it
-        // has and skips the load past the end)
-        for (; c < Kf; c += NB * kWaves) {
+        // Each wave's first NB chunks are w, w + 16, ...; after that a wave
+        // takes the next chunk from the counter in LDS as it starts reducing
+        // one (the ticket's round trip hides behind the reduction), so the
+        // row's last chunks go to the waves that are ahead rather than
+        // queueing behind a wave that drew slow loads.  (With two or more
+        // buffers every path issues the same loads, past the row's end
+        // included -- clamped, read as zeros without touching memory -- so
+        // the compiler's waits count exactly the loads behind each chunk; a
+        // single buffer waits for everything it has and skips the load past
+        // the end.)
+        int cur[NB];
+#pragma unroll
+        for (int b = 0; b < NB; b++) cur[b] = wave + b * kWaves;
+        auto pending = [&]() {
+            bool p = false;
+#pragma unroll
+            for (int b = 0; b < NB; b++) p |= cur[b] < Kf;
+            return p;
+        };
+        while (pending()) {
 #pragma unroll
             for (int b = 0; b < NB; b++) {
-                if (b == 0 || c + b * kWaves < Kf) process(buf[b], c + b * kWaves);
-                if (NB > 1 || c + (b + NB) * kWaves < Kf) load(buf[b], c + (b + NB) * kWaves);
+                if (NB > 1 && cur[b] >= Kf) continue;  // this buffer is done; the others are not
+                int nxt = 0;
+                if (lane == 0) nxt = atomicAdd(&next_chunk, 1);
+                process(buf[b], cur[b]);
+                nxt = __builtin_amdgcn_readfirstlane(nxt);
+                if (NB > 1 || nxt < Kf) load(buf[b], nxt);
+                cur[b] = nxt;
             }
         }
         // rows not 16-byte aligned: every chunk, bounds-checked
-        for (c = wave < Kf ? wave + ((Kf - 1 - wave) / kWaves + 1) * kWaves : wave; c < K; c += kWaves) {
+        for (c = Kf > 0 ? K : wave; c < K; c += kWaves) {
             load_chunk<DT, VEC>(buf[0], logits, rowbase, mrow, V, c, lane);
             process(buf[0], c);
         }
@@ -773,8 +796,11 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const float it = greedy ? 0.f : 1.0f / Tf;
     auto tok_phase = [&](int ch, float mv) {  // token waves only
         e = ch * kChunk + 4 * t;
-        ws = ch % kWaves;
-        from_stash = stash && st->c[ws] == ch;
+        // the wave whose stash holds the chunk, if any (lanes 0..15 read one
+        // stash tag each)
+        const uint64_t held = stash ? __ballot(lane < kWaves && st->c[lane & (kWaves - 1)] == ch) : 0ull;
+        ws = held ? (int)__builtin_ctzll(held) : 0;
+        from_stash = held != 0ull;
         mb4 = 0;
         if (from_stash) {
             const uint2 dw = *(const uint2 *)&st->d[ws][2 * t];
