@@ -623,7 +623,8 @@ def compile_times(args):
         res[str(cfg)] = {"vocab": len(off) - 1, "automaton_ms": round(info["compile_ms"], 2),
                          "total_ms": round(info["total_ms"], 2), "binding_wall_ms": round(wall, 2),
                          "cached_ms": round(cached, 3), "table_bytes": info["table_bytes"],
-                         "state_masks": info["state_masks"]}
+                         "state_masks": info["state_masks"],
+                         "max_bytes": info["max_bytes"] if info["max_bytes"] >= 0 else None}
         del g, g2
     print(json.dumps({"metric": "cg_compile_grammar time per workload (ms)", "unit": "ms", "n_gpus": 1,
                       "higher_is_better": False, "data": "synthetic", "configs": res}))
@@ -893,6 +894,7 @@ def main():
         "compile_ms": round(info["compile_ms"], 2),
         "compile_total_ms": round(info["total_ms"], 2),
         "table_bytes": info["table_bytes"],
+        "max_bytes": info["max_bytes"] if info["max_bytes"] >= 0 else None,
         "roofline": roofline,
     }
     # a plain device-to-device copy of 256 MiB: what the memory system gives

@@ -114,6 +114,12 @@ typedef struct {
     double total_ms;        /* the whole cg_compile_grammar call that built the handle: the
                                automaton, the vocabulary tables, the precomputed masks and
                                the upload (a cached handle keeps its first compile's time) */
+    int64_t max_bytes;      /* longest member of the language in bytes when it is finite
+                               (every string at its cap, every whitespace run at ws_max,
+                               every optional key present), -1 when it is infinite (an
+                               uncapped string, an array without maxItems, any-JSON values,
+                               calc expressions, text): how long a constrained output can
+                               get ("Constrained decoding", "A valid call also has to end") */
 } cg_info;
 
 /*

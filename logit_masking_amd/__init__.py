@@ -45,7 +45,7 @@ class Info(ctypes.Structure):
                 ("max_token_len", ctypes.c_int32), ("n_states", ctypes.c_int32),
                 ("table_entries", ctypes.c_int32), ("table_bytes", ctypes.c_int32),
                 ("compile_ms", ctypes.c_double), ("state_masks", ctypes.c_int32), ("pad", ctypes.c_int32),
-                ("total_ms", ctypes.c_double)]
+                ("total_ms", ctypes.c_double), ("max_bytes", ctypes.c_int64)]
 
 
 _lib = None

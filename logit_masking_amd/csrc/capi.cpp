@@ -727,6 +727,7 @@ int cg_grammar_info(const cg_grammar *g, cg_info *info) {
     info->total_ms = g->total_ms;
     info->state_masks = g->n_smask;
     info->pad = 0;
+    info->max_bytes = g->max_bytes;
     return CG_OK;
 }
 

@@ -288,6 +288,7 @@ struct cg_grammar {
     int32_t q_tiles = 0;     // and of the string-closing list
     double compile_ms = 0;   // spec -> automaton (parse, build, trim, pack)
     double total_ms = 0;     // the whole cg_compile_grammar call that built the handle
+    int64_t max_bytes = -1;  // longest member of the language in bytes; -1: infinite
     uint64_t *host_comb = nullptr;
     std::vector<uint32_t> host_forced;  // bit q: state q is inside an engine-written region
     bool has_forced = false;

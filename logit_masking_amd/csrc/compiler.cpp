@@ -24,9 +24,11 @@
 
 #include <algorithm>
 #include <chrono>
+#include <functional>
 #include <map>
 #include <set>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "cg_internal.hpp"
@@ -1079,6 +1081,158 @@ void trim_and_pack(Builder &B, cg_grammar *g) {
     g->k.q_limit = (uint32_t)max_base + 1;
 }
 
+// ---- the longest member ------------------------------------------------
+// The language's longest member in bytes, or -1 when the language is
+// infinite: the longest path from the start configuration to the accepting
+// state in the configuration graph of the packed automaton (the walker's
+// rules, step_byte).  Outside strings a configuration is (state, whitespace
+// run, container stack); a string, from its opening quote to its closing
+// one, is a single edge of 2 + cap x P bytes, where P is the longest path of
+// the string machine from its body state back to it (one code point: each
+// such path starts with the one OP_CHAR that spends the budget).  A cycle
+// through a configuration that can still reach the accepting state, or a
+// string with no cap, makes the language infinite.
+struct LongestMember {
+    const uint64_t *comb;
+    WalkConsts k;
+    static constexpr int64_t kDead = INT64_MIN / 4;
+    struct Cfg {
+        uint32_t q, ws, depth;
+        uint64_t stk;
+        bool operator==(const Cfg &o) const { return q == o.q && ws == o.ws && depth == o.depth && stk == o.stk; }
+    };
+    struct Hash {
+        size_t operator()(const Cfg &c) const {
+            return std::hash<uint64_t>()(c.stk * 0x9E3779B97F4A7C15ull ^ ((uint64_t)c.q << 24 | c.ws << 16 | c.depth));
+        }
+    };
+    struct Infinite {};
+    std::unordered_map<Cfg, int64_t, Hash> memo;  // kGray while on the search path
+    static constexpr int64_t kGray = INT64_MIN / 2;
+    int64_t code_point = 0;  // P
+
+    // the edges of a configuration outside strings: (next, bytes); false if
+    // the byte is refused there
+    bool step(const Cfg &c, uint32_t b, Cfg &n, int64_t &w) const {
+        const uint64_t e = comb[c.q + b];
+        const uint32_t lo = (uint32_t)e, hi = (uint32_t)(e >> 32);
+        if ((lo & 0x7FFFu) != c.q) return false;  // the engine's bytes belong to the output too
+        const uint32_t op = hi & 0xFu, arg = hi >> 4;
+        n = c;
+        n.q = lo >> 16;
+        n.ws = op == OP_WS ? c.ws + 1 : 0;
+        if (n.ws > k.ws_max) return false;
+        w = 1;
+        switch (op) {
+        case OP_STR_OPEN:
+            if (arg == kUncapped) throw Infinite{};
+            w = 2 + (int64_t)arg * code_point;  // the body from state k.s_body, then the closing quote
+            return true;
+        case OP_PUSH:
+            if (c.depth >= (arg >> 1)) return false;
+            n.stk = (c.stk << 1) | (arg & 1u);
+            n.depth = c.depth + 1;
+            return true;
+        case OP_POP:
+            if (c.depth == 0) return false;
+            n.stk = c.stk >> 1;
+            n.depth = c.depth - 1;
+            n.q = n.depth == 0 ? n.q : ((n.stk & 1u) ? (arg >> 14) : (arg & 0x3FFFu));
+            return true;
+        case OP_NONE:
+        case OP_WS:
+            return true;
+        default:  // code points and closing quotes occur only inside the string machine
+            return false;
+        }
+    }
+
+    // breadth first, so the nearest way out is found first
+    bool reaches_accept(const Cfg &from) const {
+        std::unordered_map<Cfg, char, Hash> seen;
+        std::vector<Cfg> todo{from};
+        seen[from] = 1;
+        for (size_t i = 0; i < todo.size(); i++) {
+            const Cfg c = todo[i];
+            if (c.q == k.accept) return true;
+            if (seen.size() > (1u << 22)) return true;  // (not reached by these grammars)
+            for (uint32_t b = 0; b < 256; b++) {
+                Cfg n;
+                int64_t w;
+                if (step(c, b, n, w) && seen.emplace(n, 1).second) todo.push_back(n);
+            }
+        }
+        return false;
+    }
+
+    int64_t longest(const Cfg &c) {
+        if (c.q == k.accept) return 0;
+        auto it = memo.find(c);
+        if (it != memo.end()) {
+            if (it->second != kGray) return it->second;
+            if (reaches_accept(c)) throw Infinite{};
+            return kDead;  // a cycle that cannot end
+        }
+        memo[c] = kGray;
+        int64_t best = kDead;
+        for (uint32_t b = 0; b < 256; b++) {
+            Cfg n;
+            int64_t w;
+            if (!step(c, b, n, w)) continue;
+            const int64_t v = longest(n);
+            if (v != kDead) best = std::max(best, w + v);
+        }
+        memo[c] = best;
+        return best;
+    }
+
+    // P: the longest code point of the string machine, each path from the
+    // body state back to it holding exactly one OP_CHAR (its first edge)
+    int64_t string_body() const {
+        if (k.s_body >= k.q_limit) return 0;
+        std::unordered_map<uint32_t, int64_t> f;  // longest path from a state inside a code point back to the body
+        std::function<int64_t(uint32_t)> back = [&](uint32_t q) -> int64_t {
+            if (q == k.s_body) return 0;
+            auto it = f.find(q);
+            if (it != f.end()) {
+                if (it->second == kGray) throw Infinite{};
+                return it->second;
+            }
+            f[q] = kGray;
+            int64_t best = kDead;
+            for (uint32_t b = 0; b < 256; b++) {
+                const uint64_t e = comb[q + b];
+                if (((uint32_t)e & 0xFFFFu) != q) continue;
+                // (inside a code point every edge is a plain move)
+                const int64_t v = back(((uint32_t)e >> 16) & 0xFFFFu);
+                if (v != kDead) best = std::max(best, 1 + v);
+            }
+            f[q] = best;
+            return best;
+        };
+        int64_t p = 0;
+        for (uint32_t b = 0; b < 256; b++) {
+            const uint64_t e = comb[k.s_body + b];
+            if (((uint32_t)e & 0xFFFFu) != k.s_body) continue;
+            const uint32_t op = (uint32_t)(e >> 32) & 0xFu;
+            if (op != OP_CHAR) continue;  // the closing quote
+            const int64_t v = back(((uint32_t)e >> 16) & 0xFFFFu);
+            if (v != kDead) p = std::max(p, 1 + v);
+        }
+        return p;
+    }
+
+    int64_t run() {
+        try {
+            code_point = string_body();
+            const int64_t v = longest(Cfg{k.start, 0, 0, 0});
+            return v < 0 ? -1 : v;
+        } catch (const Infinite &) {
+            return -1;
+        }
+    }
+};
+
 }  // namespace
 
 int compile_spec(const char *spec, size_t len, cg_grammar *g) {
@@ -1169,6 +1323,7 @@ int compile_spec(const char *spec, size_t len, cg_grammar *g) {
         }
         if (B.need_strings) B.strings();
         trim_and_pack(B, g);
+        g->max_bytes = LongestMember{g->host_comb, g->k}.run();
     } catch (const CompileError &e) {
         set_error("%s", e.msg.c_str());
         return e.code;

@@ -383,6 +383,7 @@ class Grammar:
             raise Unsupported("$.kind", f"unknown grammar kind {kind!r}")
         og.open_obj = b.add(kind=K_OBJ, open=1)
         og.open_arr = b.add(kind=K_ARR, open=1)
+        self._tree = (b.nodes, b.props, bytes(b.pool))
         self.settings = s
         self.gkind = og.gkind
         n = max(1, len(b.nodes))
@@ -402,6 +403,104 @@ class Grammar:
         if og.gkind == G_TOOL and not any(self._L.og_sat(ctypes.byref(og), b.props[og.tools_first + i]["node"], 0)
                                           for i in range(og.tools_count)):
             raise Unsupported("$", "grammar accepts no string")
+
+    # -- the longest member --------------------------------------------------
+    def longest_member(self):
+        """The language's longest member as (length, witness), or (None, None)
+        when the language is infinite (page "Constrained decoding", section "A
+        valid call also has to end": how long a constrained output can get).
+        A recursion over the schema tree under the recognizer's rules: every
+        optional key present, every whitespace slot filled to ws_max (after
+        '{' '[' ',' and around ':' and after each member), every capped string
+        at its cap with each code point spelled as the longest escape
+        (\\u0041, six bytes), each integer at its longest canonical spelling
+        within its bounds and digit limit, containers only where the depth cap
+        allows them.  Uncapped strings, arrays without maxItems, numbers,
+        any-JSON values and calc expressions are unbounded."""
+        nodes, props, pool = self._tree
+        W = b" " * self.settings["ws_max"]
+        cap = self.settings["depth_cap"]
+
+        class _Inf(Exception):
+            pass
+
+        def lit(p):
+            return pool[p["lit_off"]:p["lit_off"] + p["lit_len"]]
+
+        def kids(n):
+            return [props[n["first"] + j] for j in range(n["count"])]
+
+        def sat(i, d):  # the recognizer's satisfiability under the depth cap
+            n = nodes[i]
+            k = n["kind"]
+            if k == K_OBJ:
+                return d + 1 <= cap and (n["open"] or all(sat(p["node"], d + 1) for p in kids(n) if p["required"]))
+            if k == K_ARR:
+                return d + 1 <= cap
+            if k == K_ANYOF:
+                return any(sat(p["node"], d) for p in kids(n))
+            return True
+
+        def longest(i, d) -> bytes:  # a longest spelling of node i nested in d containers
+            n = nodes[i]
+            k = n["kind"]
+            if k == K_OBJ:
+                if n["open"]:
+                    raise _Inf
+                members = [lit(p) + W + b":" + W + longest(p["node"], d + 1) + W
+                           for p in kids(n) if sat(p["node"], d + 1)]
+                return b"{" + W + (b"," + W).join(members) + b"}"
+            if k == K_ARR:
+                if n["open"]:
+                    raise _Inf
+                if not sat(n["item"], d + 1) or n["cap"] == 0:
+                    return b"[" + W + b"]"
+                if n["cap"] < 0:
+                    raise _Inf
+                item = longest(n["item"], d + 1) + W
+                return b"[" + W + (b"," + W).join([item] * n["cap"]) + b"]"
+            if k == K_STR:
+                if n["cap"] < 0:
+                    raise _Inf
+                return b'"' + b"\\u0041" * n["cap"] + b'"'
+            if k == K_INT:
+                md = n["maxdigits"]
+                if n["has_lo"] and n["has_hi"]:
+                    c = [str(n["lo"]), str(n["hi"])]
+                else:
+                    c = []
+                    if not n["has_hi"]:
+                        c.append("9" * md)
+                    elif n["hi"] >= 0:
+                        c.append(str(n["hi"]))
+                    if not n["has_lo"]:
+                        c.append("-" + "9" * md)
+                    elif n["lo"] < 0:
+                        c.append(str(n["lo"]))
+                return max(c, key=len).encode()
+            if k == K_INTSTR:
+                return b'"-' + b"9" * n["maxdigits"] + b'"'
+            if k == K_BOOL:
+                return b"false"
+            if k == K_NULL:
+                return b"null"
+            if k == K_ENUM:
+                return max((lit(p) for p in kids(n)), key=len)
+            if k == K_ANYOF:
+                return max((longest(p["node"], d) for p in kids(n) if sat(p["node"], d)), key=len)
+            raise _Inf  # numbers, any-JSON values
+
+        try:
+            if self.gkind == G_JSON:
+                w = longest(self._og.root, 0)
+            elif self.gkind == G_TOOL:
+                tools = [props[self._og.tools_first + i] for i in range(self._og.tools_count)]
+                w = max((lit(t) + longest(t["node"], 0) + b")" for t in tools if sat(t["node"], 0)), key=len)
+            else:
+                raise _Inf  # calc expressions and text
+        except _Inf:
+            return None, None
+        return len(w), w
 
     # -- configurations --------------------------------------------------
     def start(self):
