@@ -458,12 +458,12 @@ __device__ __forceinline__ void top2d_merge(Top2d &a, double bv1, int bi1, doubl
         a.v2 = fmax(a.v2, bv1);
     }
 }
-// Per-wave copy of the best chunk seen so far (bf16 rows): the chunk's logits
-// in id order (4 KB) and each lane's four mask bytes, so the pick inside the
-// chosen chunk reads LDS instead of HBM.
-constexpr int kStashWords = kChunk / 2;  // bf16 pairs per chunk
+// Per-wave copy of the best chunk seen so far: the chunk's logits in id
+// order (4 KB of bf16 pairs, 8 KB of float32) and each lane's four mask
+// bytes, so the pick inside the chosen chunk reads LDS instead of HBM.
+template <int DT>
 struct Stash {
-    uint32_t d[kWaves][kStashWords];
+    uint32_t d[kWaves][DT == 1 ? kChunk / 2 : kChunk];
     uint32_t mb[kWaves][64];
     int c[kWaves];
 };
@@ -495,8 +495,8 @@ constexpr int kStageRegs = 3;
 
 // One workgroup per row.  Its 16 waves stream the row's 2048-id chunks (wave
 // w starts with chunk w and then takes the next unclaimed one from a counter
-// in LDS; one bf16 or two float32 chunks' loads in flight per wave, the next
-// load issued as each chunk is reduced) and leave
+// in LDS; one chunk's loads in flight per wave, the next load issued as each
+// chunk is reduced) and leave
 // one summary per chunk in LDS (masked max, sum of exponentials, the
 // chunk's screening noise); each wave also keeps a copy of its best chunk
 // so far in an LDS stash.  After one barrier three waves reduce the chunk
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
                                                  AdvanceArgs adv, FillArgs pa, int plan_next) {
     extern __shared__ uint64_t dyn[];
     ChunkInfo *ci = (ChunkInfo *)dyn;
-    Stash *st = (Stash *)((char *)dyn + stash_offset(K));  // valid when use_stash (bf16 only)
+    Stash<DT> *st = (Stash<DT> *)((char *)dyn + stash_offset(K));  // valid when use_stash
     __shared__ Slots sl[4];
     __shared__ uint4 lut[256];
     __shared__ RowDecision wdec;
@@ -531,13 +531,15 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const size_t rowbase = (size_t)r * (size_t)stride;
     // Each wave streams its chunks through a ring of NB chunk buffers (the
     // first ones wave, wave + 16, ...): the next load into a buffer is
-    // issued as soon as its chunk is reduced.  One bf16 chunk (4 KB) per wave in flight keeps
-    // the memory queues shallow: deeper rings (all of a 128K-id row requested
-    // at once) leave every chunk waiting behind the whole chip's requests and
-    // bunch the arrivals, and the reductions, at the end of the stream.
+    // issued as soon as its chunk is reduced.  One chunk per wave in flight
+    // (4 KB of bf16, 8 KB of float32) keeps the memory queues shallow:
+    // deeper rings (all of a 128K-id row requested at once) leave every
+    // chunk waiting behind the whole chip's requests and bunch the arrivals,
+    // and the reductions, at the end of the stream; a second float32 buffer
+    // would also leave no registers for the stash's bookkeeping.
     // Rows whose storage is not 16-byte aligned are read one chunk at a time
     // with bounds-checked loads instead.
-    constexpr int NB = DT == 1 ? 1 : 2;
+    constexpr int NB = 1;
     const int Kf = VEC ? K : 0;  // chunks read through buffer loads
     RowBufs rb;
     rb.x = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)logits + rowbase * (DT == 1 ? 2 : 4)), (short)0,
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     const float kk = greedy ? kLog2e : kLog2e / Tf;
     const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
     constexpr double kLn2d = 0.6931471805599453, kLog2ed = 1.4426950408889634;
-    const bool stash = DT == 1 && use_stash;
+    const bool stash = use_stash != 0;
     // fused advance: the transition table is fetched into registers at the
     // start, right behind the first chunk, so its round trip is over long
     // before the stream ends; it is stored to LDS after the stream and the
@@ -643,9 +645,18 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             if (score > best) {
                 best = score;
 #pragma unroll
-                for (int g = 0; g < 4; g++)
-                    *(uint4 *)&st->d[wave][g * 256 + lane * 4] =
-                        make_uint4(R.d[g * 4], R.d[g * 4 + 1], R.d[g * 4 + 2], R.d[g * 4 + 3]);
+                for (int g = 0; g < 4; g++) {
+                    if (DT == 1) {
+                        *(uint4 *)&st->d[wave][g * 256 + lane * 4] =
+                            make_uint4(R.d[g * 4], R.d[g * 4 + 1], R.d[g * 4 + 2], R.d[g * 4 + 3]);
+                    } else {
+#pragma unroll
+                        for (int h = 0; h < 2; h++)
+                            *(uint4 *)&st->d[wave][g * 512 + lane * 8 + 4 * h] =
+                                make_uint4(R.d[g * 8 + 4 * h], R.d[g * 8 + 4 * h + 1], R.d[g * 8 + 4 * h + 2],
+                                           R.d[g * 8 + 4 * h + 3]);
+                    }
+                }
                 st->mb[wave][lane] = mb[0] | mb[1] << 8 | mb[2] << 16 | mb[3] << 24;
                 if (lane == 0) st->c[wave] = cc;
             }
@@ -803,11 +814,19 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         from_stash = held != 0ull;
         mb4 = 0;
         if (from_stash) {
-            const uint2 dw = *(const uint2 *)&st->d[ws][2 * t];
-            xq[0] = __uint_as_float(dw.x << 16);
-            xq[1] = __uint_as_float(dw.x & 0xFFFF0000u);
-            xq[2] = __uint_as_float(dw.y << 16);
-            xq[3] = __uint_as_float(dw.y & 0xFFFF0000u);
+            if (DT == 1) {
+                const uint2 dw = *(const uint2 *)&st->d[ws][2 * t];
+                xq[0] = __uint_as_float(dw.x << 16);
+                xq[1] = __uint_as_float(dw.x & 0xFFFF0000u);
+                xq[2] = __uint_as_float(dw.y << 16);
+                xq[3] = __uint_as_float(dw.y & 0xFFFF0000u);
+            } else {
+                const uint4 dw = *(const uint4 *)&st->d[ws][4 * t];
+                xq[0] = __uint_as_float(dw.x);
+                xq[1] = __uint_as_float(dw.y);
+                xq[2] = __uint_as_float(dw.z);
+                xq[3] = __uint_as_float(dw.w);
+            }
             const int li = 4 * t;
             mb4 = (st->mb[ws][(li & 511) >> 3] >> (8 * (li >> 9) + (li & 7))) & 15u;
         } else {
@@ -908,6 +927,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     auto x_of = [&](int id) -> float {  // logit of an id of the chosen chunk (thread 0)
         const int li = id - chosen * kChunk;
         if (from_stash) {
+            if (DT == 0) return __uint_as_float(st->d[ws][li]);
             const uint32_t dw = st->d[ws][li >> 1];
             return __uint_as_float((li & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
         }
@@ -1073,10 +1093,10 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
     const size_t static_lds =
         4 * sizeof(Slots) + 256 * sizeof(uint4) + sizeof(RowDecision) + sizeof(PlanShared) + sizeof(cg_state) + 256;
     const size_t table = g ? (size_t)g->comb_len * 8 : 0;
-    // bf16 rows keep each wave's best chunk in LDS when it fits beside the table
-    const int use_stash =
-        dt == 1 && stash_offset(K) + sizeof(Stash) + table + static_lds <= (size_t)lds_max;
-    const size_t base = use_stash ? stash_offset(K) + sizeof(Stash) : (lds_ci + 15) / 16 * 16;
+    // each wave's best chunk is kept in LDS when it fits beside the table
+    const size_t stash_bytes = dt == 1 ? sizeof(Stash<1>) : sizeof(Stash<0>);
+    const int use_stash = stash_offset(K) + stash_bytes + table + static_lds <= (size_t)lds_max;
+    const size_t base = use_stash ? stash_offset(K) + stash_bytes : (lds_ci + 15) / 16 * 16;
     const size_t lds = base + table;
     if (lds + static_lds > (size_t)lds_max) {
         set_error("sample_advance: %zu bytes of LDS needed, %d available", lds + static_lds, lds_max);
