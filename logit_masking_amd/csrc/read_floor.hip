@@ -15,6 +15,7 @@ namespace {
 constexpr int kChunk = 2048;  // ids per chunk
 constexpr int kWaves = 16;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kStreamPolicy = 2;        // non-temporal loads, as in the sampler's stream
 
 __device__ __forceinline__ uint32_t fold(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
@@ -43,8 +44,8 @@ __global__ __launch_bounds__(1024) void k_read_floor(const char *logits, int V, 
 #pragma unroll
         for (int p = 0; p < kPieces; p++)
             d[b][p] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, c * kChunk * ES + p * 1024 + lane * 16, 0, 0));
-        mw[b] = __builtin_amdgcn_raw_buffer_load_b32(rm, c * 256 + lane * 4, 0, 0);
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, c * kChunk * ES + p * 1024 + lane * 16, 0, kStreamPolicy));
+        mw[b] = __builtin_amdgcn_raw_buffer_load_b32(rm, c * 256 + lane * 4, 0, kStreamPolicy);
         __builtin_amdgcn_sched_barrier(0);
     };
     uint32_t acc = 0;

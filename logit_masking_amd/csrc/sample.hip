@@ -214,6 +214,11 @@ struct RowBufs {
     __amdgpu_buffer_rsrc_t x, m;
 };
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+// Cache policy of the stream's loads: non-temporal.  Every logit and mask
+// word is read once, and with the hint the stream leaves the caches to the
+// small tables that the row's tail reads after it; the read-only floor
+// kernel, with the same hint, also reads faster.
+constexpr int kStreamPolicy = 2;
 
 template <int DT>
 __device__ __forceinline__ void load_buf(ChunkRegs<DT> &R, const RowBufs &rb, int c, int lane) {
@@ -224,12 +229,12 @@ __device__ __forceinline__ void load_buf(ChunkRegs<DT> &R, const RowBufs &rb, in
 #pragma unroll
         for (int h = 0; h < (DT == 1 ? 1 : 2); h++) {
             const uint4 v =
-                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.x, e0 * kEs + 16 * h, 0, 0));
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.x, e0 * kEs + 16 * h, 0, kStreamPolicy));
             uint32_t *d = &R.d[g * (DT == 1 ? 4 : 8) + 4 * h];
             d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
         }
     }
-    R.mw = __builtin_amdgcn_raw_buffer_load_b32(rb.m, c * 256 + lane * 4, 0, 0);
+    R.mw = __builtin_amdgcn_raw_buffer_load_b32(rb.m, c * 256 + lane * 4, 0, kStreamPolicy);
 }
 
 // Group g's mask byte for this lane (chunk byte 64g + lane) from the lane
