@@ -15,14 +15,16 @@ namespace {
 constexpr int kChunk = 2048;  // ids per chunk
 constexpr int kWaves = 16;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int kStreamPolicy = 2;        // non-temporal loads, as in the sampler's stream
+// the sampler's cache policy rule: logits of a launch above 32 MB are read
+// with the non-temporal hint, smaller ones with the default policy
+constexpr size_t kStreamBytes = size_t(32) << 20;
 
 __device__ __forceinline__ uint32_t fold(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
 // Chunk c of a row: 4 KB (bf16) or 8 KB (float32) of logits in 16-byte
 // pieces, lane l taking the pieces l, l + 64, ..., and the chunk's 256 mask
 // bytes as one dword per lane, which is also written to the output row.
-template <int ES>
+template <int ES, bool NT>
 __global__ __launch_bounds__(1024) void k_read_floor(const char *logits, int V, int64_t stride,
                                                      const uint64_t *mask, int wpr, uint64_t *out_mask) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -44,8 +46,8 @@ __global__ __launch_bounds__(1024) void k_read_floor(const char *logits, int V, 
 #pragma unroll
         for (int p = 0; p < kPieces; p++)
             d[b][p] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, c * kChunk * ES + p * 1024 + lane * 16, 0, kStreamPolicy));
-        mw[b] = __builtin_amdgcn_raw_buffer_load_b32(rm, c * 256 + lane * 4, 0, kStreamPolicy);
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, c * kChunk * ES + p * 1024 + lane * 16, 0, NT ? 2 : 0));
+        mw[b] = __builtin_amdgcn_raw_buffer_load_b32(rm, c * 256 + lane * 4, 0, NT ? 2 : 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     uint32_t acc = 0;
@@ -82,11 +84,17 @@ extern "C" int cg_floor_read_rows(const void *logits, int es, int B, int V, int6
         ((stride * es) % 16) != 0)
         return 1;
     hipStream_t st = (hipStream_t)stream;
-    if (es == 2)
-        hipLaunchKernelGGL(k_read_floor<2>, dim3(B), dim3(1024), 0, st, (const char *)logits, V, stride, mask, wpr,
-                           out_mask);
-    else
-        hipLaunchKernelGGL(k_read_floor<4>, dim3(B), dim3(1024), 0, st, (const char *)logits, V, stride, mask, wpr,
-                           out_mask);
+    const bool nt = (size_t)B * (size_t)V * (size_t)es > kStreamBytes;
+#define CG_FLOOR(E, N)                                                                                        \
+    hipLaunchKernelGGL((k_read_floor<E, N>), dim3(B), dim3(1024), 0, st, (const char *)logits, V, stride, mask, \
+                       wpr, out_mask)
+    if (es == 2) {
+        if (nt) CG_FLOOR(2, true);
+        else CG_FLOOR(2, false);
+    } else {
+        if (nt) CG_FLOOR(4, true);
+        else CG_FLOOR(4, false);
+    }
+#undef CG_FLOOR
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -214,13 +214,16 @@ struct RowBufs {
     __amdgpu_buffer_rsrc_t x, m;
 };
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
-// Cache policy of the stream's loads: non-temporal.  Every logit and mask
-// word is read once, and with the hint the stream leaves the caches to the
-// small tables that the row's tail reads after it; the read-only floor
-// kernel, with the same hint, also reads faster.
-constexpr int kStreamPolicy = 2;
+// Cache policy of the stream's loads.  Every logit and mask word is read
+// once.  A launch whose rows are large next to the memory-side cache (256 MB
+// on this chip) reads them with the non-temporal hint: the stream then does
+// not displace the small tables that each row's tail reads after it, and
+// even a plain read of the same rows goes faster.  A smaller launch keeps
+// the default policy, so rows that are read again soon stay cached.
+constexpr int kPolicyCached = 0, kPolicyStream = 2;
+constexpr size_t kStreamBytes = size_t(32) << 20;  // logits of a launch above this: non-temporal
 
-template <int DT>
+template <int DT, int CP>
 __device__ __forceinline__ void load_buf(ChunkRegs<DT> &R, const RowBufs &rb, int c, int lane) {
     constexpr int kEs = DT == 1 ? 2 : 4;
 #pragma unroll
@@ -229,12 +232,12 @@ __device__ __forceinline__ void load_buf(ChunkRegs<DT> &R, const RowBufs &rb, in
 #pragma unroll
         for (int h = 0; h < (DT == 1 ? 1 : 2); h++) {
             const uint4 v =
-                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.x, e0 * kEs + 16 * h, 0, kStreamPolicy));
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.x, e0 * kEs + 16 * h, 0, CP));
             uint32_t *d = &R.d[g * (DT == 1 ? 4 : 8) + 4 * h];
             d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
         }
     }
-    R.mw = __builtin_amdgcn_raw_buffer_load_b32(rb.m, c * 256 + lane * 4, 0, kStreamPolicy);
+    R.mw = __builtin_amdgcn_raw_buffer_load_b32(rb.m, c * 256 + lane * 4, 0, CP);
 }
 
 // Group g's mask byte for this lane (chunk byte 64g + lane) from the lane
@@ -512,7 +515,7 @@ constexpr int kStageRegs = 3;
 // thread commits the token; with plan_next the workgroup then plans its
 // row's next mask from the committed state (fill_plan.hpp), rewriting the
 // row's mask words it has finished reading (mask is not restrict).
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool NT>
 __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
                                                  const uint64_t *mask, int words_per_row,
                                                  const float *__restrict__ temp, const uint64_t *__restrict__ seed,
@@ -554,7 +557,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     // regrouping loads across chunks, which would make the first chunk wait
     // for the others)
     auto load = [&](ChunkRegs<DT> &R, int cc) {
-        load_buf<DT>(R, rb, min(cc, Kf), lane);
+        load_buf<DT, NT ? kPolicyStream : kPolicyCached>(R, rb, min(cc, Kf), lane);
         __builtin_amdgcn_sched_barrier(0);
     };
     ChunkRegs<DT> buf[NB];
@@ -1043,7 +1046,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex dev_mu;
 int dev_lds_max[kMaxDevices];         // 0: not asked yet
-int sample_lds_attr[kMaxDevices][4];  // k_sample<dtype, vec>'s dynamic-LDS limit as raised (0: default)
+int sample_lds_attr[kMaxDevices][8];  // k_sample<dtype, vec, nt>'s dynamic-LDS limit as raised (0: default)
 
 // LDS a workgroup may use on a device, asked once per device
 int lds_max_of(int dev) {
@@ -1128,22 +1131,30 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
     const int plan_next = (plan && g) ? 1 : 0;
     const int es = dt == 0 ? 4 : 2;
     const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * es) % 16 == 0);
-#define CG_LAUNCH_SAMPLE(D, VV)                                                                                  \
+    const bool nt = (size_t)B * (size_t)V * (size_t)es > kStreamBytes;
+#define CG_LAUNCH_SAMPLE(D, VV, NN)                                                                              \
     do {                                                                                                         \
         if (lds > 64 * 1024) {                                                                                   \
-            const int rc = raise_lds_limit((const void *)k_sample<D, VV>, dev, 2 * (D) + ((VV) ? 1 : 0), lds);    \
+            const int rc = raise_lds_limit((const void *)k_sample<D, VV, NN>, dev,                               \
+                                           4 * ((NN) ? 1 : 0) + 2 * (D) + ((VV) ? 1 : 0), lds);                  \
             if (rc != CG_OK) return rc;                                                                          \
         }                                                                                                        \
-        hipLaunchKernelGGL((k_sample<D, VV>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask, wpr, \
-                           temp, seed, step, K, use_stash, out_id, out_lp, adv, pa, plan_next);              \
+        hipLaunchKernelGGL((k_sample<D, VV, NN>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask,  \
+                           wpr, temp, seed, step, K, use_stash, out_id, out_lp, adv, pa, plan_next);             \
+    } while (0)
+#define CG_LAUNCH_SAMPLE_NT(D, VV)              \
+    do {                                        \
+        if (nt) CG_LAUNCH_SAMPLE(D, VV, true);  \
+        else CG_LAUNCH_SAMPLE(D, VV, false);    \
     } while (0)
     if (dt == 0) {
-        if (vec) CG_LAUNCH_SAMPLE(0, true);
-        else CG_LAUNCH_SAMPLE(0, false);
+        if (vec) CG_LAUNCH_SAMPLE_NT(0, true);
+        else CG_LAUNCH_SAMPLE_NT(0, false);
     } else {
-        if (vec) CG_LAUNCH_SAMPLE(1, true);
-        else CG_LAUNCH_SAMPLE(1, false);
+        if (vec) CG_LAUNCH_SAMPLE_NT(1, true);
+        else CG_LAUNCH_SAMPLE_NT(1, false);
     }
+#undef CG_LAUNCH_SAMPLE_NT
 #undef CG_LAUNCH_SAMPLE
     return launch_status(g ? "sample_advance" : "apply_mask_sample");
 }
