@@ -5,7 +5,11 @@ bf16, T = 0.7), the integer answer (vocab 151,936, batch 1024, greedy) and
 recursive JSON (vocab 256,000, batch 512, Student-t logits, T = 1.0).  The
 batch is made of 32 rows at random legal prefixes repeated in a seeded
 order; for 24 rows the mask, the pick, its log-probability and the next
-step's mask are compared with the oracle's."""
+step's mask are compared with the oracle's.  Two more cases of the tool-call
+workload cover both cache policies of the sampler's stream (logits of a
+launch above 32 MB are read with the non-temporal hint): its logits in
+float32 (131 MB, the float32 kernel with the hint) and a batch of 64 rows
+(16 MB, the bf16 kernel without it)."""
 import numpy as np
 import pytest
 
@@ -19,12 +23,14 @@ pytestmark = pytest.mark.gpu
 NEAR_TIE = 1e-6
 
 
-@pytest.mark.parametrize("cfg", [3, 4, 5])
-def test_full_size_step_against_oracle(cfg):
+@pytest.mark.parametrize("cfg,fp32,batch", [(3, False, None), (4, False, None), (5, False, None),
+                                            (3, True, None), (3, False, 64)],
+                         ids=["3", "4", "5", "3-fp32", "3-b64"])
+def test_full_size_step_against_oracle(cfg, fp32, batch):
     import torch
-    say("full size", cfg)
+    say("full size", cfg, "fp32" if fp32 else "", batch or "")
     c = W.CONFIGS[cfg]
-    B, T = c["B"], float(c["T"] or 0.0)
+    B, T = batch or c["B"], float(c["T"] or 0.0)
     blob, off = W.make_vocab(cfg)
     V = len(off) - 1
     toks = [blob[off[i]:off[i + 1]] for i in range(V)]
@@ -47,6 +53,8 @@ def test_full_size_step_against_oracle(cfg):
     ids = torch.empty(B, dtype=torch.int32, device="cuda")
     lp = torch.empty(B, dtype=torch.float32, device="cuda")
     logits = W.make_logits(cfg, 3, B, V, "cuda")
+    if fp32:
+        logits = logits.float()
     g.fill_bitmask(st, mask, fws)
     torch.cuda.synchronize()
     check = np.sort(np.random.default_rng(100 + cfg).choice(B, 24, replace=False))
