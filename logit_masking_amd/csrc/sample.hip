@@ -531,6 +531,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     __shared__ PlanShared psh;
     __shared__ cg_state next_state;
     __shared__ int next_chunk;  // the next chunk to deal to a wave
+    __shared__ uint32_t cur_w[6];  // fused: the row's state, for the wave that commits the pick
     // the wave index through readfirstlane: the compiler then knows it (and
     // every chunk index derived from it) is uniform, and branches on scalars
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -570,8 +571,9 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
 #pragma unroll
         for (int b = 0; b < NB; b++) load(buf[b], wave + b * kWaves);
     }
-    // fused: wave 0's lanes 0..5 fetch the row's 24-byte state now; thread
-    // 0 assembles it after the pick, long after it has arrived
+    // fused: wave 0's lanes 0..5 fetch the row's 24-byte state now, and
+    // leave it in LDS for the committing wave after the stream, long after
+    // it has arrived
     const bool fuse = adv.comb != nullptr;
     uint32_t stw = 0;
     if (fuse && wave == 0 && lane < 6) stw = ((const uint32_t *)(adv.states + r))[lane];
@@ -592,7 +594,8 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     // walk of the chosen token reads it there
     uint64_t *lds_comb = (uint64_t *)((char *)dyn + adv.comb_off);
     const uint32_t tn = fuse ? adv.comb_len : 0u;
-    // the pick (thread 0): every exit path below leaves it here
+    // the pick: every exit path below leaves it here (its log-probability in
+    // the thread that commits it)
     int pick = -1;
     float pick_lp = 0.f;
     Decision dc;
@@ -808,6 +811,15 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     // logit mv; sampled: the top two of x/T + G(0, i) screened in float) in
     // its slot, and the chunk it worked on.
     int e = 0, ws = 0;
+    // Each token wave keeps its candidate and fetches that token's bytes
+    // right after the decision's barrier (lane j < nw: word j, lane
+    // kInfoLane: the summary word), while the candidates are merged into
+    // the pick; the wave that holds the pick then commits it with the bytes
+    // in registers.  (Issued before the barrier, the fetch would be waited
+    // for there.)
+    constexpr int kInfoLane = kMaxTokenLen / 4;
+    int pre_id = -1;
+    uint32_t pre_w = 0u;
     bool from_stash = false;
     float xq[4] = {0.f, 0.f, 0.f, 0.f};
     uint32_t mb4 = 0;  // mask bits of e .. e + 3
@@ -853,6 +865,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             for (int j = 3; j >= 0; j--)
                 if (((mb4 >> j) & 1u) && xq[j] == mv) im = e + j;
             im = wave_min_i_fast(im);
+            pre_id = im;
             if (lane == 0) sl[2].i[wave] = im;
         } else {
             uint4 o = make_uint4(0, 0, 0, 0);
@@ -866,6 +879,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
             for (int j = 0; j < 4; j++)
                 if ((mb4 >> j) & 1u) top2_merge(ts, xq[j] * it + gumbel32(wq[j]), e + j, -INFINITY);
             ts = top2_wave_fast(ts);
+            pre_id = ts.i1;
             if (lane == 0) {
                 sl[2].f[wave] = ts.v1;
                 sl[2].h[wave] = ts.v2;
@@ -887,6 +901,7 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         else if (lane == 0) sl[2].j[wave] = -1;
     }
     if (tn > treg) stage_table(lds_comb, adv.comb, tn, treg);
+    if (fuse && wave == 0 && lane < 6) cur_w[lane] = stw;  // fetched at the start
     __syncthreads();  // the decision, the table and the token waves' slots
     dc.lse_all = wdec.lse_all;
     dc.mv = wdec.mv;
@@ -894,14 +909,9 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     dc.chosen = greedy ? wdec.mc : wdec.c1;
     dc.exact_chunk = !greedy && wdec.c1 >= 0 && !(wdec.cs1 - wdec.cs2 > kContendChunk);
     dc.cs1 = wdec.cs1;
-    // fused: the row's state, fetched at the start
-    cg_state row_state{};
-    if (fuse && threadIdx.x == 0) {
-        uint32_t w6[6];
-#pragma unroll
-        for (int j = 0; j < 6; j++) w6[j] = (uint32_t)__builtin_amdgcn_readlane((int)stw, j);
-        __builtin_memcpy(&row_state, w6, sizeof(w6));
-    }
+    // the wave that holds the pick (its 256-id part of the chosen chunk)
+    // publishes and commits it; wave 0 when nothing is picked
+    int cw = 0;
     do {
     if (dc.mc < 0) break;  // nothing allowed: a finished row
     if (dc.exact_chunk) {
@@ -932,7 +942,11 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         if (tok) tok_phase(chosen, dc.mv);
         __syncthreads();
     }
-    auto x_of = [&](int id) -> float {  // logit of an id of the chosen chunk (thread 0)
+    if (fuse && tok && pre_id >= 0 && pre_id < adv.V) {  // the candidate's token (pre_id: the same in every lane)
+        if (lane < adv.nw) pre_w = adv.tokw[(size_t)lane * adv.V + pre_id];
+        else if (lane == kInfoLane) pre_w = adv.tokinfo[pre_id];
+    }
+    auto x_of = [&](int id) -> float {  // logit of an id of the chosen chunk (a token-wave thread)
         const int li = id - chosen * kChunk;
         if (from_stash) {
             if (DT == 0) return __uint_as_float(st->d[ws][li]);
@@ -941,14 +955,17 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         }
         return load_logit<DT>(logits, rowbase + id);
     };
+    auto holder = [&](int id) {
+        const int li = id - chosen * kChunk;
+        return (li >= 0 && li < kChunk) ? li >> 8 : 0;
+    };
     if (greedy) {
-        if (threadIdx.x == 0) {
-            int best = sl[2].i[0];
+        int best = sl[2].i[0];
 #pragma unroll
-            for (int w = 1; w < kTokWaves; w++) best = min(best, sl[2].i[w]);
-            pick = best;
-            pick_lp = (float)((double)dc.mv - dc.lse_all);
-        }
+        for (int w = 1; w < kTokWaves; w++) best = min(best, sl[2].i[w]);
+        pick = best;
+        pick_lp = (float)((double)dc.mv - dc.lse_all);
+        cw = holder(best);
         break;
     }
     // sampled: argmax_i x_i / T + G(0, i) screened in float; the winner is
@@ -969,10 +986,9 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     for (int k = 1; k < kTokWaves; k++) top2_merge(tt, sv1[k], si1[k], sv2[k]);
     const double win = 1e-4 + 2e-6 * fabs((double)tt.v1);
     if ((double)tt.v1 - (double)tt.v2 > win) {
-        if (threadIdx.x == 0) {
-            pick = tt.i1;
-            pick_lp = (float)((double)x_of(tt.i1) * invT - dc.lse_all);
-        }
+        pick = tt.i1;
+        cw = holder(pick);
+        if ((int)threadIdx.x == cw * 64) pick_lp = (float)((double)x_of(pick) * invT - dc.lse_all);
         break;
     }
     // contenders recomputed in double (rare)
@@ -992,28 +1008,43 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    {
         double v = sl[3].b[0];
         int i = sl[3].j[0];
         for (int k = 1; k < kTokWaves; k++) arg_better(v, i, sl[3].b[k], sl[3].j[k]);
         pick = i;
-        pick_lp = (float)((double)x_of(i) * invT - dc.lse_all);
+        cw = holder(pick);
+        if ((int)threadIdx.x == cw * 64) pick_lp = (float)((double)x_of(pick) * invT - dc.lse_all);
     }
     } while (0);
-    // ---- epilogue: thread 0 publishes the pick and, fused, commits it ---------
-    if (threadIdx.x == 0) {
+    // ---- epilogue: lane 0 of wave cw publishes the pick and, fused, commits it
+    uint32_t pw[kInfoLane + 1];  // the wave's fetched token (whole waves read their lanes)
+#pragma unroll
+    for (int j = 0; j <= kInfoLane; j++) pw[j] = (uint32_t)__builtin_amdgcn_readlane((int)pre_w, j);
+    if ((int)threadIdx.x == cw * 64) {
         out_id[r] = pick;
         out_lp[r] = pick_lp;
         if (fuse) {
+            cg_state row_state;
+            uint32_t w6[6];
+#pragma unroll
+            for (int j = 0; j < 6; j++) w6[j] = cur_w[j];
+            __builtin_memcpy(&row_state, w6, sizeof(w6));
             uint32_t words[kMaxTokenLen / 4];
             uint32_t n = 0;
 #pragma unroll
             for (int j = 0; j < kMaxTokenLen / 4; j++) words[j] = 0;
             if (pick >= 0 && pick < adv.V) {
-                n = tok_len(adv.tokinfo[pick]);
+                if (pick == pre_id) {  // fetched with the candidate
+                    n = tok_len(pw[kInfoLane]);
 #pragma unroll
-                for (int j = 0; j < kMaxTokenLen / 4; j++)
-                    if (j < adv.nw) words[j] = adv.tokw[(size_t)j * adv.V + pick];
+                    for (int j = 0; j < kMaxTokenLen / 4; j++) words[j] = pw[j];
+                } else {
+                    n = tok_len(adv.tokinfo[pick]);
+#pragma unroll
+                    for (int j = 0; j < kMaxTokenLen / 4; j++)
+                        if (j < adv.nw) words[j] = adv.tokw[(size_t)j * adv.V + pick];
+                }
             }
             int stp1 = (int)stp;
             const int res =
