@@ -158,13 +158,15 @@ __device__ inline void plan_row(const FillArgs &a, int r, const cg_state &s, con
     const int ridx = (plain && in_str && a.rq_idx) ? a.rq_idx[s.ret] : -1;
     const size_t c_off = (size_t)min(s.cnt, (uint32_t)kStrBitsets - 1u) * a.Wv;
     const uint64_t *base = in_str ? a.strbits + c_off : sidx >= 0 ? a.state_mask + (size_t)sidx * a.Wv : nullptr;
+    // (non-temporal stores: this workgroup never reads the words back; the
+    // walk ORs into them, on any XCD, and the next sampler reads them once)
     if (ridx >= 0 || ridx2 >= 0) {
         const uint64_t *cb = a.closebits + c_off;
         const uint64_t *rm = ridx >= 0 ? a.retmask + (size_t)ridx * a.Wv
                                        : a.retmask2 + ((size_t)ridx2 * 2 + (s.stk & 1u)) * a.Wv;
-        for (int i = tid; i < a.Wv; i += kPlanThreads) out[i] = base[i] | (cb[i] & rm[i]);
+        for (int i = tid; i < a.Wv; i += kPlanThreads) __builtin_nontemporal_store(base[i] | (cb[i] & rm[i]), &out[i]);
     } else {
-        for (int i = tid; i < a.Wv; i += kPlanThreads) out[i] = base ? base[i] : 0ull;
+        for (int i = tid; i < a.Wv; i += kPlanThreads) __builtin_nontemporal_store(base ? base[i] : 0ull, &out[i]);
     }
     if (!live || (sidx >= 0 && ctx == 0) || ridx >= 0) {
         if (tid == 0) plan[0] = 0;
