@@ -240,6 +240,33 @@ __device__ __forceinline__ void load_buf(ChunkRegs<DT> &R, const RowBufs &rb, in
     R.mw = __builtin_amdgcn_raw_buffer_load_b32(rb.m, c * 256 + lane * 4, 0, CP);
 }
 
+// The same logit loads for a row whose mask is staged in LDS: a lane reads
+// its 16 bytes of group g only when their 8 mask bits (byte g of mt, the
+// lane's transposed mask dword of the chunk) hold an allowed id.  A masked
+// logit never reaches a result (the reduction replaces it by -inf before
+// any arithmetic, the pick skips it), so the registers of a piece not read
+// may hold anything.
+template <int DT, int CP>
+__device__ __forceinline__ void load_buf_masked(ChunkRegs<DT> &R, const RowBufs &rb, int c, int lane, uint32_t mt) {
+    constexpr int kEs = DT == 1 ? 2 : 4;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+        if (((mt >> (8 * g)) & 0xFFu) == 0u) continue;
+        const int e0 = c * kChunk + g * 512 + lane * 8;
+#pragma unroll
+        for (int h = 0; h < (DT == 1 ? 1 : 2); h++) {
+            const uint4 v =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.x, e0 * kEs + 16 * h, 0, CP));
+            uint32_t *d = &R.d[g * (DT == 1 ? 4 : 8) + 4 * h];
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        }
+    }
+}
+
+// Pieces of 16 mask bytes each thread stages for a row whose mask goes to
+// LDS: K <= 64 * kMaskPieces chunks.
+constexpr int kMaskPieces = 4;
+
 // Group g's mask byte for this lane (chunk byte 64g + lane) from the lane
 // that loaded it: one cross-lane read per group, no LDS memory.
 __device__ __forceinline__ void mask_bytes(uint32_t mw, int lane, uint32_t (&mb)[4]) {
@@ -515,15 +542,23 @@ constexpr int kStageRegs = 3;
 // thread commits the token; with plan_next the workgroup then plans its
 // row's next mask from the committed state (fill_plan.hpp), rewriting the
 // row's mask words it has finished reading (mask is not restrict).
-template <int DT, bool VEC, bool NT>
+template <int DT, bool VEC, bool NT, bool SP>
 __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits, int V, int64_t stride,
                                                  const uint64_t *mask, int words_per_row,
                                                  const float *__restrict__ temp, const uint64_t *__restrict__ seed,
-                                                 const int32_t *step, int K, int use_stash,
+                                                 const int32_t *step, int K, int use_stash, int moff,
                                                  int32_t *__restrict__ out_id, float *__restrict__ out_lp,
                                                  AdvanceArgs adv, FillArgs pa, int plan_next) {
     extern __shared__ uint64_t dyn[];
     ChunkInfo *ci = (ChunkInfo *)dyn;
+    // Sparse stream (aligned rows whose mask fits in LDS): the row's mask is
+    // staged in LDS at the start, transposed (dword 64 c + l of lmask holds
+    // bytes l, 64 + l, 128 + l, 192 + l of chunk c: lane l's four group
+    // bytes), and after its first chunk a wave reads only the 16-byte pieces
+    // of logits that hold an allowed id.  Rows of a constrained step are
+    // mostly sparse: their logits are mostly never read.
+    constexpr bool kSparse = SP && VEC;
+    uint32_t *lmask = (uint32_t *)((char *)dyn + moff);
     Stash<DT> *st = (Stash<DT> *)((char *)dyn + stash_offset(K));  // valid when use_stash
     __shared__ Slots sl[4];
     __shared__ uint4 lut[256];
@@ -557,8 +592,17 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     // (a scheduling barrier after each chunk's loads keeps the compiler from
     // regrouping loads across chunks, which would make the first chunk wait
     // for the others)
+    constexpr int CP = NT ? kPolicyStream : kPolicyCached;
+    auto load_all = [&](ChunkRegs<DT> &R, int cc) {
+        load_buf<DT, CP>(R, rb, min(cc, Kf), lane);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     auto load = [&](ChunkRegs<DT> &R, int cc) {
-        load_buf<DT, NT ? kPolicyStream : kPolicyCached>(R, rb, min(cc, Kf), lane);
+        if (kSparse) {
+            if (cc < Kf) load_buf_masked<DT, CP>(R, rb, cc, lane, lmask[cc * 64 + lane]);
+        } else {
+            load_buf<DT, CP>(R, rb, min(cc, Kf), lane);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
     ChunkRegs<DT> buf[NB];
@@ -569,7 +613,17 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     // whenever the row has pipelined chunks at all.
     if (Kf > 0) {
 #pragma unroll
-        for (int b = 0; b < NB; b++) load(buf[b], wave + b * kWaves);
+        for (int b = 0; b < NB; b++) load_all(buf[b], wave + b * kWaves);
+    }
+    // sparse: the row's mask, 16 bytes per piece, right behind the first chunk
+    uint4 mp[kMaskPieces];
+    if (kSparse) {
+#pragma unroll
+        for (int j = 0; j < kMaskPieces; j++) {
+            const int p = threadIdx.x + j * 1024;
+            mp[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (p < K * 16) mp[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb.m, p * 16, 0, CP));
+        }
     }
     // fused: wave 0's lanes 0..5 fetch the row's 24-byte state now, and
     // leave it in LDS for the committing wave after the stream, long after
@@ -628,9 +682,24 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
                 const uint4 o = philox4x32_10(make_uint4((uint32_t)cg >> 2, stp, 1u, 0u), k0, k1);
                 ci[cg].g = gumbel32(pick_word(o, cg & 3));
             }
+        // sparse: the mask pieces transposed into LDS (byte k of chunk c to
+        // byte k / 64 of dword 64 c + k % 64)
+        if (kSparse) {
+#pragma unroll
+            for (int j = 0; j < kMaskPieces; j++) {
+                const int p = threadIdx.x + j * 1024;
+                if (p < K * 16) {
+                    const int k0 = (p & 15) * 16;
+                    uint8_t *dst = (uint8_t *)lmask + (size_t)((p >> 4) * 64 + (k0 & 63)) * 4 + (k0 >> 6);
+                    const uint32_t w4[4] = {mp[j].x, mp[j].y, mp[j].z, mp[j].w};
+#pragma unroll
+                    for (int i = 0; i < 16; i++) dst[4 * i] = (uint8_t)(w4[i >> 2] >> (8 * (i & 3)));
+                }
+            }
+        }
         // (the loads stay in flight across the barrier: a workgroup barrier
         // waits for LDS operations, not for loads from memory)
-        __syncthreads();  // the pair table, the noise and the chunk counter
+        __syncthreads();  // the pair table, the noise, the chunk counter and (sparse) the mask
         // reduce chunk cc into its summary; the wave's best chunk so far (by
         // the chunk score in float: m for greedy rows, m/T + ln s + G(1, c)
         // for sampled ones) is copied to the stash.  A near-tie that the
@@ -640,7 +709,13 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         const float invTf = (float)invT;
         auto process = [&](ChunkRegs<DT> &R, int cc) {
             uint32_t mb[4];
-            mask_bytes(R.mw, lane, mb);
+            if (kSparse) {
+                const uint32_t mt = lmask[cc * 64 + lane];
+#pragma unroll
+                for (int g = 0; g < 4; g++) mb[g] = (mt >> (8 * g)) & 0xFFu;
+            } else {
+                mask_bytes(R.mw, lane, mb);
+            }
             if (VEC && cc == K - 1) clear_tail(mb);
             float m, s;
             bool any;
@@ -1077,7 +1152,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex dev_mu;
 int dev_lds_max[kMaxDevices];         // 0: not asked yet
-int sample_lds_attr[kMaxDevices][8];  // k_sample<dtype, vec, nt>'s dynamic-LDS limit as raised (0: default)
+int sample_lds_attr[kMaxDevices][16];  // k_sample<dtype, vec, nt, sparse>'s dynamic-LDS limit as raised (0: default)
 
 // LDS a workgroup may use on a device, asked once per device
 int lds_max_of(int dev) {
@@ -1163,27 +1238,38 @@ int launch_sample(const void *logits, int dt, int B, int V, int64_t stride, cons
     const int es = dt == 0 ? 4 : 2;
     const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * es) % 16 == 0);
     const bool nt = (size_t)B * (size_t)V * (size_t)es > kStreamBytes;
-#define CG_LAUNCH_SAMPLE(D, VV, NN)                                                                              \
+    // the row's mask staged in LDS for the sparse stream: aligned rows with
+    // more chunks than waves (a wave's first chunk is read whole, so with
+    // fewer the staging saves nothing), when it fits after the table
+    const size_t moff = (lds + 15) / 16 * 16;
+    const bool sp = vec && K > kWaves && K <= 64 * kMaskPieces &&
+                    moff + (size_t)K * 256 + static_lds <= (size_t)lds_max;
+    const size_t lds_all = sp ? moff + (size_t)K * 256 : lds;
+#define CG_LAUNCH_SAMPLE(D, VV, NN, SS)                                                                          \
     do {                                                                                                         \
-        if (lds > 64 * 1024) {                                                                                   \
-            const int rc = raise_lds_limit((const void *)k_sample<D, VV, NN>, dev,                               \
-                                           4 * ((NN) ? 1 : 0) + 2 * (D) + ((VV) ? 1 : 0), lds);                  \
+        if (lds_all > 64 * 1024) {                                                                               \
+            const int rc = raise_lds_limit((const void *)k_sample<D, VV, NN, SS>, dev,                           \
+                                           8 * ((SS) ? 1 : 0) + 4 * ((NN) ? 1 : 0) + 2 * (D) + ((VV) ? 1 : 0),    \
+                                           lds_all);                                                             \
             if (rc != CG_OK) return rc;                                                                          \
         }                                                                                                        \
-        hipLaunchKernelGGL((k_sample<D, VV, NN>), dim3(B), dim3(kWaves * 64), lds, st, logits, V, stride, mask,  \
-                           wpr, temp, seed, step, K, use_stash, out_id, out_lp, adv, pa, plan_next);             \
+        hipLaunchKernelGGL((k_sample<D, VV, NN, SS>), dim3(B), dim3(kWaves * 64), lds_all, st, logits, V,       \
+                           stride, mask, wpr, temp, seed, step, K, use_stash, (int)moff, out_id, out_lp, adv, pa, \
+                           plan_next);                                                                           \
     } while (0)
-#define CG_LAUNCH_SAMPLE_NT(D, VV)              \
-    do {                                        \
-        if (nt) CG_LAUNCH_SAMPLE(D, VV, true);  \
-        else CG_LAUNCH_SAMPLE(D, VV, false);    \
+#define CG_LAUNCH_SAMPLE_NT(D, VV, SS)              \
+    do {                                            \
+        if (nt) CG_LAUNCH_SAMPLE(D, VV, true, SS);  \
+        else CG_LAUNCH_SAMPLE(D, VV, false, SS);    \
     } while (0)
     if (dt == 0) {
-        if (vec) CG_LAUNCH_SAMPLE_NT(0, true);
-        else CG_LAUNCH_SAMPLE_NT(0, false);
+        if (sp) CG_LAUNCH_SAMPLE_NT(0, true, true);
+        else if (vec) CG_LAUNCH_SAMPLE_NT(0, true, false);
+        else CG_LAUNCH_SAMPLE_NT(0, false, false);
     } else {
-        if (vec) CG_LAUNCH_SAMPLE_NT(1, true);
-        else CG_LAUNCH_SAMPLE_NT(1, false);
+        if (sp) CG_LAUNCH_SAMPLE_NT(1, true, true);
+        else if (vec) CG_LAUNCH_SAMPLE_NT(1, true, false);
+        else CG_LAUNCH_SAMPLE_NT(1, false, false);
     }
 #undef CG_LAUNCH_SAMPLE_NT
 #undef CG_LAUNCH_SAMPLE

@@ -15,14 +15,18 @@ V_MAX = 4_194_304  # 2048 chunk summaries of 24 bytes fill the 48 KiB the sample
 NEAR_TIE = 1e-6
 
 
-def _run_sample(x, bits, T, seeds, step, dtype):
-    """x: float64 [B, V] (values representable in dtype), bits: bool [B, V]."""
+def _run_sample(x, bits, T, seeds, step, dtype, stray_rows=()):
+    """x: float64 [B, V] (values representable in dtype), bits: bool [B, V];
+    stray_rows: rows whose mask words also set every bit past V (a caller's
+    mask may carry such bits; they allow nothing)."""
     import torch
     B, V = x.shape
     logits = torch.from_numpy(x).to(dtype).cuda()
     W_ = (V + 63) // 64
     pad = np.zeros((B, W_ * 64), dtype=bool)
     pad[:, :V] = bits
+    for r in stray_rows:
+        pad[r, V:] = True
     words = np.packbits(pad.reshape(B, W_, 64)[:, :, ::-1], axis=2, bitorder="big").view(">u8").astype(np.uint64)
     mask = torch.from_numpy(words.reshape(B, W_).view(np.int64)).cuda()
     temp = torch.full((B,), float(T), dtype=torch.float32, device="cuda")
@@ -64,6 +68,33 @@ def test_sample_max_vocab(dtype_name, T):
     dt = getattr(torch, dtype_name)
     xs, ids, lp = _run_sample(x, bits, T, [12345, 67890], 4, dt)
     assert _check(xs, bits, T, [12345, 67890], 4, ids, lp) <= 1
+
+
+@pytest.mark.parametrize("dtype_name,T", [("bfloat16", 0.7), ("bfloat16", 0.0), ("float32", 0.7), ("float32", 0.0)])
+def test_sample_sparse_rows(dtype_name, T):
+    """Aligned rows of more than 16 chunks take the sparse stream: the mask is
+    staged in LDS and, after each wave's first chunk, a lane reads a 16-byte
+    piece of logits only when one of its ids is allowed.  Vocabulary 100,000
+    (49 chunks, the last one ragged): a single allowed id in a middle chunk;
+    a single one at the last id, with every mask bit past V set; one allowed
+    id per 4096; ids allowed only in the first 16 chunks (the ones read
+    whole); every id; none."""
+    import torch
+    say("sparse rows", dtype_name, T)
+    rng = np.random.default_rng(21)
+    B, V = 6, 100_000
+    x = rng.normal(scale=3.0, size=(B, V))
+    bits = np.zeros((B, V), dtype=bool)
+    bits[0, 40_000] = True
+    bits[1, V - 1] = True
+    bits[2, rng.choice(V, V // 4096, replace=False)] = True
+    bits[3, :16 * 2048] = rng.random(16 * 2048) < 0.5
+    bits[4, :] = True
+    seeds = [int(s) for s in rng.integers(0, 2**63, size=B)]
+    dt = getattr(torch, dtype_name)
+    xs, ids, lp = _run_sample(x, bits, T, seeds, 3, dt, stray_rows=(1,))
+    assert ids[0] == 40_000 and ids[1] == V - 1 and ids[5] == -1
+    assert _check(xs, bits, T, seeds, 3, ids, lp) <= 1
 
 
 def test_sample_vocab_over_limit():
