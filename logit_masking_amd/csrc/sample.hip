@@ -977,6 +977,12 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
     }
     if (tn > treg) stage_table(lds_comb, adv.comb, tn, treg);
     if (fuse && wave == 0 && lane < 6) cur_w[lane] = stw;  // fetched at the start
+    // each lane's address of its part of the candidate's token, worked out
+    // here, so that no kernel argument is read between the barrier and the
+    // merge (a scalar read would share the merge's LDS wait)
+    const uint32_t *pre_p = nullptr;
+    if (fuse && tok && pre_id >= 0 && pre_id < adv.V)
+        pre_p = lane < adv.nw ? adv.tokw + (size_t)lane * adv.V + pre_id : lane == kInfoLane ? adv.tokinfo + pre_id : nullptr;
     __syncthreads();  // the decision, the table and the token waves' slots
     dc.lse_all = wdec.lse_all;
     dc.mv = wdec.mv;
@@ -1017,10 +1023,12 @@ __global__ __launch_bounds__(1024) void k_sample(const void *__restrict__ logits
         if (tok) tok_phase(chosen, dc.mv);
         __syncthreads();
     }
-    if (fuse && tok && pre_id >= 0 && pre_id < adv.V) {  // the candidate's token (pre_id: the same in every lane)
-        if (lane < adv.nw) pre_w = adv.tokw[(size_t)lane * adv.V + pre_id];
-        else if (lane == kInfoLane) pre_w = adv.tokinfo[pre_id];
-    }
+    if (again)  // the candidates were picked again
+        pre_p = !(fuse && tok && pre_id >= 0 && pre_id < adv.V) ? nullptr
+                : lane < adv.nw                                  ? adv.tokw + (size_t)lane * adv.V + pre_id
+                : lane == kInfoLane                              ? adv.tokinfo + pre_id
+                                                                 : nullptr;
+    if (pre_p) pre_w = *pre_p;  // the candidate's token
     auto x_of = [&](int id) -> float {  // logit of an id of the chosen chunk (a token-wave thread)
         const int li = id - chosen * kChunk;
         if (from_stash) {
